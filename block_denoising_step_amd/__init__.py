@@ -1,0 +1,290 @@
+"""Python binding of libdg, the HIP (gfx950) hot path of one block-diffusion
+denoising step: mixed-mode attention, the DiffusionSampler step and the
+self-conditioning embedding average.
+
+The binding only marshals arguments: torch tensors give device pointers and the
+current HIP stream, and every step of the computation runs in libdg's kernels.
+There is no fallback: if libdg.so is missing or cannot be loaded, every call
+raises. Build it with `python -m block_denoising_step_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = 0, 1, 2, 3, 4
+DG_F32, DG_BF16 = 0, 1
+DG_CAUSAL, DG_BIDIR = 0, 1
+DG_CONF_NEG_ENTROPY, DG_CONF_MAX_PROB = 0, 1
+DG_CONV_AND, DG_CONV_OR = 0, 1
+DG_ENTROPY_IN, DG_INIT_CANVAS = 1, 2
+DG_MAX_SEQS = DG_MAX_REQS = 64
+DG_MAX_CANVAS = 1024
+
+_c_int32, _c_int64, _c_uint32, _c_uint64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
+_vp, _fp = ctypes.c_void_p, ctypes.c_void_p
+
+
+class DgSeq(ctypes.Structure):
+    _fields_ = [("q_start", _c_int32), ("num_q", _c_int32), ("kv_start", _c_int32),
+                ("prefix_len", _c_int32), ("mode", _c_int32)]
+
+
+class DgAttnArgs(ctypes.Structure):
+    _fields_ = [("num_seqs", _c_int32), ("seqs", ctypes.POINTER(DgSeq)), ("window", _c_int32),
+                ("num_q_heads", _c_int32), ("num_kv_heads", _c_int32), ("head_dim", _c_int32),
+                ("scale", ctypes.c_float), ("dtype", _c_int32), ("total_q", _c_int64), ("total_kv", _c_int64),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp), ("lse", _vp), ("kv_chunk", _c_int32),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DgSreq(ctypes.Structure):
+    _fields_ = [("row_start", _c_int32), ("num_rows", _c_int32), ("seed", _c_uint64), ("step", _c_int32),
+                ("reserved", _c_int32)]
+
+
+class DgSamplerArgs(ctypes.Structure):
+    _fields_ = [("num_reqs", _c_int32), ("reqs", ctypes.POINTER(DgSreq)), ("num_rows", _c_int32),
+                ("vocab", _c_int32), ("dtype", _c_int32), ("logits", _vp), ("ld", _c_int64),
+                ("budget", ctypes.c_float), ("min_accept", _c_int32), ("conf_mode", _c_int32),
+                ("renoise", _c_int32), ("stable_k", _c_int32), ("tau", ctypes.c_float), ("step_limit", _c_int32),
+                ("combine", _c_int32), ("flags", _c_uint32),
+                ("entropy", _vp), ("conf", _vp), ("row_max", _vp), ("row_sum", _vp), ("argmax", _vp),
+                ("cand", _vp), ("accept", _vp), ("canvas", _vp), ("prev_argmax", _vp),
+                ("stable_count", _vp), ("num_accepted", _vp), ("converged", _vp), ("mean_entropy", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DgSelfcondArgs(ctypes.Structure):
+    _fields_ = [("M", _c_int32), ("V", _c_int32), ("d", _c_int32), ("dtype", _c_int32),
+                ("p", _vp), ("ldp", _c_int64), ("row_max", _vp), ("row_sum", _vp),
+                ("embed", _vp), ("lde", _c_int64), ("out", _vp), ("ldo", _c_int64),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
+EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sampler_workspace_size",
+           "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_status_string", "dg_last_error",
+           "dg_abi_version"]
+
+_lib = None
+
+
+class DgError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_string(status)}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libdg.so (once). Raises if it is not built: there is no other path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_denoising_step_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.dg_attn_mixed.argtypes = [ctypes.POINTER(DgAttnArgs), _vp]
+    lib.dg_attn_mixed.restype = ctypes.c_int
+    lib.dg_attn_workspace_size.argtypes = [ctypes.POINTER(DgAttnArgs)]
+    lib.dg_attn_workspace_size.restype = ctypes.c_size_t
+    lib.dg_sampler_step.argtypes = [ctypes.POINTER(DgSamplerArgs), _vp]
+    lib.dg_sampler_step.restype = ctypes.c_int
+    lib.dg_sampler_workspace_size.argtypes = [ctypes.POINTER(DgSamplerArgs)]
+    lib.dg_sampler_workspace_size.restype = ctypes.c_size_t
+    lib.dg_selfcond_embed.argtypes = [ctypes.POINTER(DgSelfcondArgs), _vp]
+    lib.dg_selfcond_embed.restype = ctypes.c_int
+    lib.dg_selfcond_workspace_size.argtypes = [ctypes.POINTER(DgSelfcondArgs)]
+    lib.dg_selfcond_workspace_size.restype = ctypes.c_size_t
+    lib.dg_status_string.argtypes = [ctypes.c_int]
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_last_error.argtypes = []
+    lib.dg_last_error.restype = ctypes.c_char_p
+    lib.dg_abi_version.argtypes = []
+    lib.dg_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().dg_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().dg_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != DG_OK:
+        raise DgError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DG_BF16
+    if t.dtype == torch.float32:
+        return DG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == ctypes.c_size_t(-1).value:
+        return workspace  # invalid args: the call itself reports the error
+    if nbytes == 0:
+        return workspace
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+# ---- dg_attn_mixed ---------------------------------------------------------------
+
+def make_attn_args(q, k, v, out, seqs: Sequence, window: int, num_q_heads: int, num_kv_heads: int,
+                   lse=None, scale: float = 0.0, kv_chunk: int = 0, workspace=None):
+    seq_arr = (DgSeq * max(1, len(seqs)))()
+    for i, s in enumerate(seqs):
+        f = (s.q_start, s.num_q, s.kv_start, s.prefix_len, s.mode) if hasattr(s, "q_start") else tuple(s)
+        seq_arr[i] = DgSeq(*f)
+    a = DgAttnArgs()
+    a.num_seqs = len(seqs)
+    a.seqs = ctypes.cast(seq_arr, ctypes.POINTER(DgSeq))
+    a.window = window
+    a.num_q_heads, a.num_kv_heads = num_q_heads, num_kv_heads
+    a.head_dim = q.shape[-1]
+    a.scale = scale
+    a.dtype = _dtype(q)
+    a.total_q, a.total_kv = q.shape[0], k.shape[0]
+    a.q, a.k, a.v, a.out, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.kv_chunk = kv_chunk
+    a._keep = seq_arr  # keep the host array alive with the struct
+    return a
+
+
+def attn_workspace_size(args: DgAttnArgs) -> int:
+    return load().dg_attn_workspace_size(ctypes.byref(args))
+
+
+def dg_attn_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, seqs: Sequence,
+                  window: int, num_q_heads: int, num_kv_heads: int, lse: Optional[torch.Tensor] = None,
+                  scale: float = 0.0, kv_chunk: int = 0, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Optional[torch.Tensor]:
+    """Mixed-mode attention (see include/dg.h). q [T, Hq, D], k/v [S, Hkv, D], out like q,
+    lse [T, Hq] fp32 or None. Returns the workspace tensor used (reusable)."""
+    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk)
+    ws = _workspace(attn_workspace_size(a), q, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().dg_attn_mixed(ctypes.byref(a), _stream(stream)))
+    return ws
+
+
+# ---- dg_sampler_step -------------------------------------------------------------
+
+class SamplerBuffers:
+    """Device buffers of one sampler call: per-row outputs and per-request state."""
+
+    def __init__(self, num_rows: int, num_reqs: int, device):
+        f = dict(dtype=torch.float32, device=device)
+        i = dict(dtype=torch.int32, device=device)
+        self.entropy = torch.zeros(num_rows, **f)
+        self.conf = torch.zeros(num_rows, **f)
+        self.row_max = torch.zeros(num_rows, **f)
+        self.row_sum = torch.zeros(num_rows, **f)
+        self.argmax = torch.zeros(num_rows, **i)
+        self.cand = torch.zeros(num_rows, **i)
+        self.accept = torch.zeros(num_rows, dtype=torch.uint8, device=device)
+        self.canvas = torch.zeros(num_rows, **i)
+        self.prev_argmax = torch.full((num_rows,), -1, **i)
+        self.stable_count = torch.zeros(num_reqs, **i)
+        self.num_accepted = torch.zeros(num_reqs, **i)
+        self.converged = torch.zeros(num_reqs, **i)
+        self.mean_entropy = torch.zeros(num_reqs, **f)
+        self.workspace: Optional[torch.Tensor] = None
+
+
+def make_sampler_args(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, int, int, int]], vocab: int,
+                      bufs: SamplerBuffers, budget: float, min_accept: int = 1,
+                      conf_mode: int = DG_CONF_NEG_ENTROPY, renoise: int = 1, stable_k: int = 3, tau: float = 0.05,
+                      step_limit: int = 48, combine: int = DG_CONV_AND, flags: int = 0, num_rows: Optional[int] = None):
+    req_arr = (DgSreq * max(1, len(reqs)))()
+    for i, (row_start, n, seed, step) in enumerate(reqs):
+        req_arr[i] = DgSreq(row_start, n, seed, step, 0)
+    a = DgSamplerArgs()
+    a.num_reqs = len(reqs)
+    a.reqs = ctypes.cast(req_arr, ctypes.POINTER(DgSreq))
+    a.num_rows = num_rows if num_rows is not None else (logits.shape[0] if logits is not None else bufs.canvas.shape[0])
+    a.vocab = vocab
+    a.dtype = _dtype(logits) if logits is not None else DG_BF16
+    a.logits = _ptr(logits)
+    a.ld = logits.stride(0) if logits is not None else vocab
+    a.budget, a.min_accept, a.conf_mode, a.renoise = budget, min_accept, conf_mode, renoise
+    a.stable_k, a.tau, a.step_limit, a.combine, a.flags = stable_k, tau, step_limit, combine, flags
+    for name in ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
+                 "stable_count", "num_accepted", "converged", "mean_entropy"):
+        setattr(a, name, _ptr(getattr(bufs, name)))
+    a._keep = req_arr
+    return a
+
+
+def sampler_workspace_size(args: DgSamplerArgs) -> int:
+    return load().dg_sampler_workspace_size(ctypes.byref(args))
+
+
+def dg_sampler_step(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, int, int, int]], vocab: int,
+                    bufs: SamplerBuffers, budget: float, stream=None, **kw) -> None:
+    """One DiffusionSampler denoise step (see include/dg.h). reqs: (row_start, num_rows,
+    seed, step) per request. Outputs and state live in `bufs`."""
+    a = make_sampler_args(logits, reqs, vocab, bufs, budget, **kw)
+    like = logits if logits is not None else bufs.canvas
+    bufs.workspace = _workspace(sampler_workspace_size(a), like, bufs.workspace)
+    a.workspace = _ptr(bufs.workspace)
+    a.workspace_bytes = 0 if bufs.workspace is None else bufs.workspace.numel()
+    _check(load().dg_sampler_step(ctypes.byref(a), _stream(stream)))
+
+
+# ---- dg_selfcond_embed -----------------------------------------------------------
+
+def make_selfcond_args(p: torch.Tensor, embed: torch.Tensor, out: torch.Tensor, row_max=None, row_sum=None,
+                       num_cols: Optional[int] = None):
+    a = DgSelfcondArgs()
+    a.M = p.shape[0]
+    a.V = num_cols if num_cols is not None else p.shape[1]
+    a.d = embed.shape[1]
+    a.dtype = _dtype(p)
+    a.p, a.ldp = _ptr(p), p.stride(0)
+    a.row_max, a.row_sum = _ptr(row_max), _ptr(row_sum)
+    a.embed, a.lde = _ptr(embed), embed.stride(0)
+    a.out, a.ldo = _ptr(out), out.stride(0)
+    return a
+
+
+def selfcond_workspace_size(args: DgSelfcondArgs) -> int:
+    return load().dg_selfcond_workspace_size(ctypes.byref(args))
+
+
+def dg_selfcond_embed(p: torch.Tensor, embed: torch.Tensor, out: torch.Tensor,
+                      row_max: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """out = P . E with P given, or P = softmax rebuilt from logits and row stats
+    (see include/dg.h). Returns the workspace tensor used (reusable)."""
+    a = make_selfcond_args(p, embed, out, row_max, row_sum)
+    ws = _workspace(selfcond_workspace_size(a), p, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().dg_selfcond_embed(ctypes.byref(a), _stream(stream)))
+    return ws

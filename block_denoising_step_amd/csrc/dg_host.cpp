@@ -1,0 +1,307 @@
+// Host half of libdg: argument validation, work planning, workspace sizing and the
+// extern "C" entry points declared in include/dg.h. Nothing here touches HIP: a
+// call either fails validation here (nothing launched, nothing written) or is
+// handed to the launchers in the .hip files.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dg_status fail(dg_status s, const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Request-local key range [lo, hi] of new token i ([P1] section
+// "대칭 슬라이딩 윈도우 어텐션": one-sided window for causal requests, symmetric for
+// bidirectional ones; global layers use window < 0).
+void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int* hi) {
+  const int p = prefix + i;
+  const int last = prefix + num_q - 1;
+  *lo = window < 0 ? 0 : std::max(0, p - window);
+  if (mode == DG_CAUSAL) *hi = p;
+  else *hi = window < 0 ? last : std::min(last, p + window);
+}
+
+}  // namespace
+
+// ---- attention plan ----------------------------------------------------------
+//
+// A request with a single chunk per q tile writes its output directly; one with
+// several writes fp32 partials that the merge kernel combines in chunk order.
+// A request's chunk length gives it about kTargetGroups work groups, but never
+// under kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write
+// and read.
+
+static constexpr int kKeyTile = kAttnKeyTile;
+static constexpr int kTileRows = kAttnTileRows;
+static constexpr int kTargetGroups = 512;
+static constexpr int kMinChunkTiles = 8;
+
+dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
+  auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
+  if (!a) return bad(DG_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 1 || a->num_seqs > DG_MAX_SEQS) return bad(DG_ERR_INVALID_ARG, "num_seqs must be in [1, DG_MAX_SEQS]");
+  if (!a->seqs) return bad(DG_ERR_INVALID_ARG, "seqs is NULL");
+  if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1) return bad(DG_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (a->num_q_heads % a->num_kv_heads) return bad(DG_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = a->num_q_heads / a->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16 && G != 32)
+    return bad(DG_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads must be a power of two <= 32");
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return bad(DG_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (a->dtype == DG_F32 && a->head_dim > 128) return bad(DG_ERR_UNSUPPORTED, "fp32 attention supports head_dim 64 and 128");
+  if (a->window < -1) return bad(DG_ERR_INVALID_ARG, "window must be -1 (global) or >= 0");
+  if (!std::isfinite(a->scale) || a->scale < 0.f) return bad(DG_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (a->total_q < 0 || a->total_kv < 0) return bad(DG_ERR_INVALID_ARG, "total_q and total_kv must be >= 0");
+  if (a->kv_chunk < 0 || a->kv_chunk % kKeyTile) return bad(DG_ERR_INVALID_ARG, "kv_chunk must be 0 or a positive multiple of 64");
+  if (!a->q || !a->k || !a->v || !a->out) return bad(DG_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+    return bad(DG_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (a->lse && !aligned4(a->lse)) return bad(DG_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+
+  // request geometry
+  std::vector<std::pair<int64_t, int64_t>> qranges;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const dg_seq& q = a->seqs[s];
+    if (q.mode != DG_CAUSAL && q.mode != DG_BIDIR) return bad(DG_ERR_INVALID_ARG, "seq mode must be DG_CAUSAL or DG_BIDIR");
+    if (q.q_start < 0 || q.num_q < 0 || q.kv_start < 0 || q.prefix_len < 0)
+      return bad(DG_ERR_INVALID_ARG, "seq offsets and lengths must be >= 0");
+    if ((int64_t)q.q_start + q.num_q > a->total_q) return bad(DG_ERR_INVALID_ARG, "seq query rows exceed total_q");
+    if ((int64_t)q.kv_start + q.prefix_len + q.num_q > a->total_kv) return bad(DG_ERR_INVALID_ARG, "seq key rows exceed total_kv");
+    if ((int64_t)q.prefix_len + q.num_q > INT32_MAX - kKeyTile) return bad(DG_ERR_INVALID_ARG, "seq too long");
+    if (q.num_q > 0) qranges.push_back({q.q_start, (int64_t)q.q_start + q.num_q});
+  }
+  std::sort(qranges.begin(), qranges.end());
+  for (size_t i = 1; i < qranges.size(); ++i)
+    if (qranges[i].first < qranges[i - 1].second) return bad(DG_ERR_INVALID_ARG, "seq query ranges overlap");
+
+  // tiles and chunks; the split of a request depends on that request alone, so its
+  // result is the same whatever else is in the batch
+  const int tok_per_tile = kTileRows / G;
+  int64_t num_work = 0, num_merge = 0, num_parts = 0;
+  plan->num_seqs = a->num_seqs;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const dg_seq& q = a->seqs[s];
+    const int64_t ntiles_q = ceil_div(q.num_q, tok_per_tile);
+    int64_t max_tiles = 0, units = 0;
+    for (int t = 0; t < ntiles_q; ++t) {
+      const int i0 = t * tok_per_tile, i1 = std::min<int>(q.num_q, i0 + tok_per_tile) - 1;
+      int lo0, hi0, lo1, hi1;
+      key_range(q.mode, q.prefix_len, q.num_q, a->window, i0, &lo0, &hi0);
+      key_range(q.mode, q.prefix_len, q.num_q, a->window, i1, &lo1, &hi1);
+      const int64_t nt = hi1 / kKeyTile - lo0 / kKeyTile + 1;
+      max_tiles = std::max(max_tiles, nt);
+      units += nt * a->num_kv_heads;
+    }
+    int64_t chunk_tiles;
+    if (a->kv_chunk > 0) chunk_tiles = a->kv_chunk / kKeyTile;
+    else chunk_tiles = std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
+    const int64_t nch = max_tiles > 0 ? ceil_div(max_tiles, chunk_tiles) : 0;
+    AttnSeqPlan& sp = plan->seqs[s];
+    sp.q_start = q.q_start;
+    sp.num_q = q.num_q;
+    sp.kv_start = q.kv_start;
+    sp.prefix_len = q.prefix_len;
+    sp.mode = q.mode;
+    sp.num_chunks = (int32_t)nch;
+    sp.chunk_tiles = (int32_t)std::min<int64_t>(chunk_tiles, INT32_MAX);
+    sp.work_begin = (int32_t)num_work;
+    sp.merge_begin = (int32_t)num_merge;
+    sp.part_begin = (int32_t)num_parts;
+    num_work += a->num_kv_heads * ntiles_q * nch;
+    if (nch > 1) {
+      num_merge += a->num_kv_heads * ntiles_q;
+      num_parts += a->num_kv_heads * ntiles_q * nch;
+    }
+    if (num_work > INT32_MAX / 2 || num_parts > INT32_MAX / 2) return bad(DG_ERR_UNSUPPORTED, "too much work for one call");
+  }
+  plan->group = G;
+  plan->tokens_per_tile = tok_per_tile;
+  plan->num_work = (int)num_work;
+  plan->num_merge = (int)num_merge;
+  plan->num_parts = (int)num_parts;
+  plan->part_o_offset = 0;
+  const size_t o_bytes = (size_t)num_parts * kTileRows * a->head_dim * sizeof(float);
+  plan->part_ml_offset = align_up(o_bytes, 256);
+  const size_t ml_bytes = (size_t)num_parts * kTileRows * 2 * sizeof(float);
+  plan->bytes = num_parts ? align_up(plan->part_ml_offset + ml_bytes, 256) : 0;
+  return DG_OK;
+}
+
+// ---- sampler plan ------------------------------------------------------------
+
+dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char** msg) {
+  auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
+  if (!a) return bad(DG_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_reqs < 1 || a->num_reqs > DG_MAX_REQS) return bad(DG_ERR_INVALID_ARG, "num_reqs must be in [1, DG_MAX_REQS]");
+  if (!a->reqs) return bad(DG_ERR_INVALID_ARG, "reqs is NULL");
+  if (a->num_rows < 1) return bad(DG_ERR_INVALID_ARG, "num_rows must be >= 1");
+  if (a->vocab < 1) return bad(DG_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (a->ld < a->vocab || a->ld % 8) return bad(DG_ERR_INVALID_ARG, "ld must be >= vocab and a multiple of 8");
+  if (!std::isfinite(a->budget) || a->budget < 0.f) return bad(DG_ERR_INVALID_ARG, "budget must be finite and >= 0");
+  if (!std::isfinite(a->tau) || a->tau < 0.f) return bad(DG_ERR_INVALID_ARG, "tau must be finite and >= 0");
+  if (a->min_accept < 0) return bad(DG_ERR_INVALID_ARG, "min_accept must be >= 0");
+  if (a->conf_mode != DG_CONF_NEG_ENTROPY && a->conf_mode != DG_CONF_MAX_PROB) return bad(DG_ERR_INVALID_ARG, "bad conf_mode");
+  if (a->combine != DG_CONV_AND && a->combine != DG_CONV_OR) return bad(DG_ERR_INVALID_ARG, "bad combine");
+  if (a->renoise != 0 && a->renoise != 1) return bad(DG_ERR_INVALID_ARG, "renoise must be 0 or 1");
+  if (a->stable_k < 1 || a->step_limit < 1) return bad(DG_ERR_INVALID_ARG, "stable_k and step_limit must be >= 1");
+  if (a->flags & ~(DG_ENTROPY_IN | DG_INIT_CANVAS)) return bad(DG_ERR_INVALID_ARG, "unknown flag bits");
+  const bool init = a->flags & DG_INIT_CANVAS;
+  if (!init && !a->logits) return bad(DG_ERR_INVALID_ARG, "logits is NULL");
+  if (a->logits && !aligned16(a->logits)) return bad(DG_ERR_INVALID_ARG, "logits must be 16-byte aligned");
+  const void* ptrs[] = {a->entropy, a->conf, a->row_max, a->row_sum, a->argmax, a->cand, a->canvas,
+                        a->prev_argmax, a->stable_count, a->num_accepted, a->converged, a->mean_entropy};
+  for (const void* p : ptrs)
+    if (!p || !aligned4(p)) return bad(DG_ERR_INVALID_ARG, "every output/state pointer must be non-NULL and 4-byte aligned");
+  if (!a->accept) return bad(DG_ERR_INVALID_ARG, "accept is NULL");
+  std::vector<std::pair<int64_t, int64_t>> r;
+  for (int i = 0; i < a->num_reqs; ++i) {
+    const dg_sreq& q = a->reqs[i];
+    if (q.num_rows < 1 || q.num_rows > DG_MAX_CANVAS) return bad(DG_ERR_INVALID_ARG, "request num_rows must be in [1, DG_MAX_CANVAS]");
+    if (q.row_start < 0 || (int64_t)q.row_start + q.num_rows > a->num_rows) return bad(DG_ERR_INVALID_ARG, "request rows exceed num_rows");
+    if (q.step < 0) return bad(DG_ERR_INVALID_ARG, "request step must be >= 0");
+    if (q.reserved != 0) return bad(DG_ERR_INVALID_ARG, "request reserved field must be 0");
+    r.push_back({q.row_start, (int64_t)q.row_start + q.num_rows});
+  }
+  std::sort(r.begin(), r.end());
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].first < r[i - 1].second) return bad(DG_ERR_INVALID_ARG, "request row ranges overlap");
+  plan->chunk = a->dtype == DG_BF16 ? 16384 : 8192;
+  plan->num_chunks = (int)ceil_div(a->vocab, plan->chunk);
+  if (plan->num_chunks > 1024) return bad(DG_ERR_UNSUPPORTED, "vocab too large (more than 1024 row-pass chunks)");
+  plan->bytes = init ? 0 : align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
+  return DG_OK;
+}
+
+// ---- self-conditioning plan --------------------------------------------------
+
+dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const char** msg) {
+  auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
+  if (!a) return bad(DG_ERR_INVALID_ARG, "args is NULL");
+  if (a->M < 1 || a->V < 1 || a->d < 1) return bad(DG_ERR_INVALID_ARG, "M, V and d must be >= 1");
+  if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (a->d % 128) return bad(DG_ERR_UNSUPPORTED, "d must be a multiple of 128");
+  if (a->ldp < a->V || a->ldp % 8) return bad(DG_ERR_INVALID_ARG, "ldp must be >= V and a multiple of 8");
+  if (a->lde < a->d || a->lde % 8) return bad(DG_ERR_INVALID_ARG, "lde must be >= d and a multiple of 8");
+  if (a->ldo < a->d || a->ldo % 8) return bad(DG_ERR_INVALID_ARG, "ldo must be >= d and a multiple of 8");
+  if (!a->p || !a->embed || !a->out) return bad(DG_ERR_INVALID_ARG, "p, embed and out must be non-NULL");
+  if (!aligned16(a->p) || !aligned16(a->embed) || !aligned16(a->out)) return bad(DG_ERR_INVALID_ARG, "p, embed and out must be 16-byte aligned");
+  if ((a->row_max == nullptr) != (a->row_sum == nullptr)) return bad(DG_ERR_INVALID_ARG, "set both row_max and row_sum, or neither");
+  plan->tile_m = 128;
+  plan->tile_n = 128;
+  plan->tile_k = a->dtype == DG_BF16 ? 64 : 32;  // 128 bytes of each A row per K step
+  plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
+  plan->n_tiles = a->d / plan->tile_n;
+  // split-K so that the grid is about two work groups per CU, in slices of whole K steps
+  const int64_t base = (int64_t)plan->m_tiles * plan->n_tiles;
+  const int64_t ksteps = ceil_div(a->V, plan->tile_k);
+  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(ksteps, ceil_div(512, base)));
+  const int64_t steps_per_split = ceil_div(ksteps, splits);
+  splits = ceil_div(ksteps, steps_per_split);
+  plan->splits = (int)splits;
+  plan->k_per_split = (int)(steps_per_split * plan->tile_k);
+  plan->bytes = splits > 1 ? align_up((size_t)splits * a->M * a->d * sizeof(float), 256) : 0;
+  return DG_OK;
+}
+
+}  // namespace dg
+
+// ---- C ABI -------------------------------------------------------------------
+
+using namespace dg;
+
+extern "C" {
+
+const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_INVALID_ARG: return "DG_ERR_INVALID_ARG";
+    case DG_ERR_UNSUPPORTED: return "DG_ERR_UNSUPPORTED";
+    case DG_ERR_WORKSPACE: return "DG_ERR_WORKSPACE";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+  }
+  return "unknown dg_status";
+}
+
+const char* dg_last_error(void) { return g_last_error; }
+int dg_abi_version(void) { return DG_ABI_VERSION; }
+
+size_t dg_attn_workspace_size(const dg_attn_args* a) {
+  AttnPlan plan;
+  const char* msg = "";
+  if (attn_plan(a, &plan, &msg) != DG_OK) return (size_t)-1;
+  return plan.bytes;
+}
+
+dg_status dg_attn_mixed(const dg_attn_args* a, void* stream) {
+  AttnPlan plan;
+  const char* msg = "";
+  dg_status s = attn_plan(a, &plan, &msg);
+  if (s != DG_OK) return fail(s, msg);
+  if (plan.bytes && (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace)))
+    return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_attn_workspace_size");
+  if (plan.num_work == 0) { g_last_error[0] = 0; return DG_OK; }
+  int e = launch_attn(a, plan, stream);
+  if (e) return fail(DG_ERR_HIP, hip_error_name(e));
+  g_last_error[0] = 0;
+  return DG_OK;
+}
+
+size_t dg_sampler_workspace_size(const dg_sampler_args* a) {
+  SamplerPlan plan;
+  const char* msg = "";
+  if (sampler_plan(a, &plan, &msg) != DG_OK) return (size_t)-1;
+  return plan.bytes;
+}
+
+dg_status dg_sampler_step(const dg_sampler_args* a, void* stream) {
+  SamplerPlan plan;
+  const char* msg = "";
+  dg_status s = sampler_plan(a, &plan, &msg);
+  if (s != DG_OK) return fail(s, msg);
+  if (plan.bytes && (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace)))
+    return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_sampler_workspace_size");
+  int e = launch_sampler(a, plan, stream);
+  if (e) return fail(DG_ERR_HIP, hip_error_name(e));
+  g_last_error[0] = 0;
+  return DG_OK;
+}
+
+size_t dg_selfcond_workspace_size(const dg_selfcond_args* a) {
+  SelfcondPlan plan;
+  const char* msg = "";
+  if (selfcond_plan(a, &plan, &msg) != DG_OK) return (size_t)-1;
+  return plan.bytes;
+}
+
+dg_status dg_selfcond_embed(const dg_selfcond_args* a, void* stream) {
+  SelfcondPlan plan;
+  const char* msg = "";
+  dg_status s = selfcond_plan(a, &plan, &msg);
+  if (s != DG_OK) return fail(s, msg);
+  if (plan.bytes && (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace)))
+    return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_selfcond_workspace_size");
+  int e = launch_selfcond(a, plan, stream);
+  if (e) return fail(DG_ERR_HIP, hip_error_name(e));
+  g_last_error[0] = 0;
+  return DG_OK;
+}
+
+}  // extern "C"

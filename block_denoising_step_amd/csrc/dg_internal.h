@@ -1,0 +1,76 @@
+// Internal interface between the host half of libdg (validation, planning,
+// workspace layout) and the HIP launchers. No HIP types appear here, so the host
+// half compiles and is testable without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+// ---- attention ---------------------------------------------------------------
+//
+// Work is laid out per request as [kv head][q tile][key chunk]. A q tile holds
+// kTileRows query rows (tokens x grouped heads); a key chunk is a run of 64-key
+// tiles. Every q tile of a request gets the same number of chunks (a chunk past a
+// tile's keys is empty and exits at once). The kernel finds its (request, head,
+// tile, chunk) from this table, so no work list has to be copied to the device.
+
+constexpr int kAttnKeyTile = 64;
+constexpr int kAttnTileRows = 128;
+
+struct AttnSeqPlan {
+  int32_t q_start, num_q, kv_start, prefix_len, mode;
+  int32_t num_chunks;   // key chunks per q tile
+  int32_t chunk_tiles;  // 64-key tiles per chunk (depends on this request only)
+  int32_t work_begin;   // first work-group index of this request
+  int32_t merge_begin;  // first merge index (requests with num_chunks > 1)
+  int32_t part_begin;   // first partial slot (requests with num_chunks > 1)
+};
+
+struct AttnPlan {
+  int num_seqs;
+  int group;            // G = Hq / Hkv
+  int tokens_per_tile;  // kAttnTileRows / G
+  int num_work;         // work groups of the attention kernel
+  int num_merge;        // work groups of the merge kernel
+  int num_parts;        // partial slots
+  size_t part_o_offset;   // workspace: [num_parts][kAttnTileRows][D] fp32 partial outputs
+  size_t part_ml_offset;  // workspace: [num_parts][kAttnTileRows][2] fp32 (max, sum) in log2 units
+  size_t bytes;
+  AttnSeqPlan seqs[DG_MAX_SEQS];
+};
+
+// Validates args (everything but the workspace) and fills the plan.
+dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg);
+
+// ---- sampler -----------------------------------------------------------------
+
+struct SamplerPlan {
+  int chunk;        // vocabulary entries per row-pass work group
+  int num_chunks;   // chunks per row
+  size_t bytes;     // workspace bytes (per-chunk statistics)
+};
+dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char** msg);
+
+// ---- self-conditioning -------------------------------------------------------
+
+struct SelfcondPlan {
+  int tile_m, tile_n, tile_k;  // output tile per work group, K step
+  int m_tiles, n_tiles;
+  int splits;                  // split-K slices over V
+  int k_per_split;             // vocabulary rows per slice (multiple of tile_k)
+  size_t bytes;                // workspace: fp32 partials [splits][M][d]
+};
+dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const char** msg);
+
+// ---- launchers (HIP side); return 0 on success or a hipError_t value ---------
+
+int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream);
+int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stream);
+int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream);
+const char* hip_error_name(int err);
+
+}  // namespace dg

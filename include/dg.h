@@ -1,0 +1,236 @@
+/*
+ * dg.h - C ABI of libdg: the hot path of one block-diffusion denoising step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [P1] "DiffusionGemma: vLLM에서 네이티브로 처음 지원되는 첫 번째 Diffusion LLM"
+ *        (agentlenshq.com summary of the vLLM integration)
+ *   [P2] "DiffusionGemma 개발자 가이드" (molayo1419.me retelling of the developer guide)
+ *   [P3] "DiffusionGemma u vLLM: prvi diskretni difuzijski model od 26 milijardi
+ *        parametara integriran u produkcijsko okruženje" (24-ai.news)
+ *
+ * The three calls follow the split of the per-model hooks in [P1] section
+ * "ModelState 인터페이스" and [P3] section "Integracija u vLLM infrastrukturu":
+ *   dg_attn_mixed      - attention with a causal/bidirectional switch per request
+ *                        (the prepare_attn hook and the attention backend);
+ *   dg_sampler_step    - the DiffusionSampler's denoise step (the custom_sampler hook);
+ *   dg_selfcond_embed  - the self-conditioning average (the self-conditioning part
+ *                        of the prepare_inputs hook).
+ * Per-request state (canvas, previous argmax, stable count) lives in caller
+ * buffers, standing in for the add_request/remove_request lifecycle.
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked "device" are device (HBM) addresses; "host" ones are read on
+ *     the host during the call and may be freed when it returns.
+ *   - The caller owns every buffer, the workspace included (size it with the
+ *     matching dg_*_workspace_size). The library never allocates, frees or
+ *     synchronises; every call is asynchronous on `stream` (a hipStream_t, NULL for
+ *     the default stream) and performs no host<->device copy.
+ *   - Every argument is validated before anything is launched. On any error the
+ *     call launches nothing, writes no output, returns a non-zero dg_status and
+ *     leaves a message for dg_last_error() (thread-local). Launch failures return
+ *     DG_ERR_HIP; faults inside a kernel surface at the caller's next synchronisation.
+ *   - Results are deterministic: the same inputs, seeds and steps give bit-identical
+ *     outputs (no floating-point atomics; every split is merged in a fixed order).
+ *   - Row-major layouts; the last dimension is contiguous. Device buffers must be
+ *     16-byte aligned.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_ABI_VERSION 1
+#define DG_MAX_SEQS 64      /* requests per dg_attn_mixed call */
+#define DG_MAX_REQS 64      /* requests per dg_sampler_step call */
+#define DG_MAX_CANVAS 1024  /* positions per sampler request */
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1, /* an argument breaks a documented rule */
+  DG_ERR_UNSUPPORTED = 2, /* valid in principle but not built (e.g. head_dim) */
+  DG_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dg_*_workspace_size */
+  DG_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Per-request attention mode ([P1] sections "듀얼 모드 운영" and
+ * "동적 퍼-시퀀스 인과적 어텐션"): prefill and commit are causal ("encoder mode"),
+ * denoising is bidirectional ("decoder mode"). */
+typedef enum { DG_CAUSAL = 0, DG_BIDIR = 1 } dg_mode;
+
+/* ------------------------------------------------------------------------------
+ * dg_attn_mixed: masked softmax attention for a batch of requests in mixed modes.
+ *
+ * Request r owns query rows [q_start, q_start + num_q) of q/out/lse and key rows
+ * [kv_start, kv_start + prefix_len + num_q) of k/v: the first prefix_len rows are
+ * its committed KV cache, the last num_q rows are this call's tokens (the canvas,
+ * a commit or a prefill), whose K/V the caller has already written. New token i
+ * sits at position p = prefix_len + i and attends to keys j of its own request with
+ *     lo <= j <= hi,  lo = (window < 0) ? 0 : max(0, p - window),
+ *     hi = CAUSAL ? p : (window < 0 ? prefix_len + num_q - 1
+ *                                   : min(prefix_len + num_q - 1, p + window)).
+ * So a causal request in a sliding-window layer sees the `window` tokens before
+ * it plus itself, and a bidirectional one up to `window` on each side, 2W+1 keys
+ * ([P1] section "대칭 슬라이딩 윈도우 어텐션"; [P3] decoder mode with +-W windows).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped heads).
+ *   out[t, h, :] = sum_j softmax_j(scale * <q[t,h], k[j,g]>) * v[j, g, :]
+ *   lse[t, h]    = log sum_j exp(scale * <q[t,h], k[j,g]>)      (natural log)
+ * ------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t q_start, num_q, kv_start, prefix_len, mode; /* mode: dg_mode */
+} dg_seq;
+
+typedef struct {
+  int32_t num_seqs;             /* 1..DG_MAX_SEQS */
+  const dg_seq* seqs;           /* host array [num_seqs]; query ranges must not overlap */
+  int32_t window;               /* -1: global layer; W >= 0: sliding window */
+  int32_t num_q_heads;          /* Hq >= 1 */
+  int32_t num_kv_heads;         /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1,2,4,8,16} */
+  int32_t head_dim;             /* D in {64, 128, 256} */
+  float scale;                  /* 0 => 1/sqrt(head_dim) */
+  int32_t dtype;                /* dg_dtype of q, k, v and out */
+  int64_t total_q;              /* rows of q/out/lse: every q range must fit */
+  int64_t total_kv;             /* rows of k/v: every kv range must fit */
+  const void* q;                /* device [total_q, Hq, D] */
+  const void* k;                /* device [total_kv, Hkv, D] */
+  const void* v;                /* device [total_kv, Hkv, D] */
+  void* out;                    /* device [total_q, Hq, D], dtype; rows outside every request untouched */
+  float* lse;                   /* device [total_q, Hq] fp32, or NULL */
+  int32_t kv_chunk;             /* keys per split-KV chunk: 0 = library's choice, else a multiple of 64 */
+  void* workspace;              /* device, >= dg_attn_workspace_size(args) bytes (may be NULL if that is 0) */
+  size_t workspace_bytes;
+} dg_attn_args;
+
+dg_status dg_attn_mixed(const dg_attn_args* args, void* stream);
+/* Workspace the call needs for these arguments (split-KV partials and the work
+ * list). Pure host; 0 means none. Returns (size_t)-1 if the arguments are invalid. */
+size_t dg_attn_workspace_size(const dg_attn_args* args);
+
+/* ------------------------------------------------------------------------------
+ * dg_sampler_step: one denoise step of the DiffusionSampler over canvas rows
+ * ([P1] section "샘플링 루프와 엔트로피 경계 디노이징"; [P3] section
+ * "Mehanizam odlučivanja o gotovim tokenima"; re-noising of unaccepted positions,
+ * [P2] sections "아키텍처 (The Architecture)" and "Diffusion에 스도쿠가 흥미로운 이유").
+ *
+ * Row statistics, for each row i of logits (every row 0..num_rows-1):
+ *   row_max[i] = max_v l[i,v];  argmax[i] = lowest v with l[i,v] = row_max[i];
+ *   row_sum[i] = sum_v exp(l[i,v] - row_max[i]);  p = exp(l - row_max) / row_sum;
+ *   entropy[i] = -sum_v p_v ln p_v (nats, >= 0);
+ *   conf[i]    = -entropy[i] (DG_CONF_NEG_ENTROPY) or 1/row_sum, the largest
+ *                probability (DG_CONF_MAX_PROB).
+ * Per request r (rows [row_start, row_start + num_rows), position j = row - row_start):
+ *   cand    = first token whose cumulative probability exceeds u, u = Philox4x64-10
+ *             24-bit uniform for key (seed, 0), counter (step, j, 0, 0);
+ *   accept  = the longest run of positions, most confident first (ties: lower j
+ *             first), whose entropy total stays <= budget, and at least min_accept
+ *             positions; totals are exact integer sums of floor(entropy * 2^40);
+ *   canvas  = accept ? cand : converged ? argmax : renoise ? token : canvas, where the
+ *             token is floor(hi32(x0) * vocab / 2^32) of Philox counter (step, j, 1, 0);
+ *   stable_count = (step > 0 and argmax == prev_argmax at every position)
+ *                  ? stable_count + 1 : 0;
+ *   mean_entropy = sum floor(entropy * 2^40) / 2^40 / num_rows;
+ *   converged    = DG_CONV_AND: (stable_count >= stable_k and mean < tau) or step + 1 >= step_limit
+ *                  DG_CONV_OR:  stable_count >= stable_k or mean < tau or step + 1 >= step_limit
+ *                  (mean < tau is tested exactly in the 2^-40 fixed point);
+ *   prev_argmax  = argmax.
+ * With DG_ENTROPY_IN the call reads `entropy` (and, for DG_CONF_MAX_PROB, `conf`)
+ * instead of writing them, so a selection can be replayed on given entropies.
+ * With DG_INIT_CANVAS the call only starts a block: canvas = Philox token from
+ * counter (step, j, 2, 0), prev_argmax = -1, stable_count = 0, converged = 0,
+ * num_accepted = 0; logits are not read.
+ * Precondition: every logits row has at least one finite value (-inf means p = 0).
+ * ------------------------------------------------------------------------------ */
+#define DG_CONF_NEG_ENTROPY 0
+#define DG_CONF_MAX_PROB 1
+#define DG_CONV_AND 0
+#define DG_CONV_OR 1
+#define DG_ENTROPY_IN 1u
+#define DG_INIT_CANVAS 2u
+
+typedef struct {
+  int32_t row_start, num_rows; /* rows of this request's canvas; 1..DG_MAX_CANVAS rows */
+  uint64_t seed;               /* Philox key word 0 */
+  int32_t step;                /* denoise step index within the block, >= 0 */
+  int32_t reserved;            /* must be 0 */
+} dg_sreq;
+
+typedef struct {
+  int32_t num_reqs;            /* 1..DG_MAX_REQS */
+  const dg_sreq* reqs;         /* host array; request row ranges must not overlap */
+  int32_t num_rows;            /* M: rows of logits and of every [M] buffer */
+  int32_t vocab;               /* V >= 1 */
+  int32_t dtype;               /* dg_dtype of logits */
+  const void* logits;          /* device [M, ld] */
+  int64_t ld;                  /* row stride of logits in elements, >= V, multiple of 8 */
+  float budget;                /* entropy budget in nats, finite, >= 0 */
+  int32_t min_accept;          /* >= 0 */
+  int32_t conf_mode;           /* DG_CONF_* */
+  int32_t renoise;             /* 1: re-noise unaccepted positions; 0: keep their token */
+  int32_t stable_k;            /* >= 1 */
+  float tau;                   /* mean-entropy threshold, finite, >= 0 */
+  int32_t step_limit;          /* >= 1 */
+  int32_t combine;             /* DG_CONV_* */
+  uint32_t flags;              /* DG_ENTROPY_IN | DG_INIT_CANVAS */
+  float* entropy;              /* device [M] (input with DG_ENTROPY_IN) */
+  float* conf;                 /* device [M] (input with DG_ENTROPY_IN and DG_CONF_MAX_PROB) */
+  float* row_max;              /* device [M] */
+  float* row_sum;              /* device [M] */
+  int32_t* argmax;             /* device [M] */
+  int32_t* cand;               /* device [M]; -1 for rows outside every request */
+  uint8_t* accept;             /* device [M] (0/1) */
+  int32_t* canvas;             /* device [M], in/out */
+  int32_t* prev_argmax;        /* device [M], in/out */
+  int32_t* stable_count;       /* device [num_reqs], in/out */
+  int32_t* num_accepted;       /* device [num_reqs] */
+  int32_t* converged;          /* device [num_reqs] (0/1) */
+  float* mean_entropy;         /* device [num_reqs] */
+  void* workspace;             /* device, >= dg_sampler_workspace_size(args) bytes */
+  size_t workspace_bytes;
+} dg_sampler_args;
+
+dg_status dg_sampler_step(const dg_sampler_args* args, void* stream);
+size_t dg_sampler_workspace_size(const dg_sampler_args* args);
+
+/* ------------------------------------------------------------------------------
+ * dg_selfcond_embed: the probability-weighted average of the token embeddings
+ * ([P1] section "안정성을 위한 셀프 컨디셔닝"; [P3] section
+ * "Mehanizam odlučivanja o gotovim tokenima"):
+ *   out[i, :] = sum_v p[i, v] * embed[v, :]
+ * p is either given (row_max == NULL) or rebuilt from logits and the sampler's row
+ * statistics, p = exp(l - row_max[i]) / row_sum[i] (both non-NULL). Products are
+ * accumulated in fp32; out has the input dtype.
+ * ------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t M, V, d;             /* M >= 1; V >= 1; d a multiple of 128 */
+  int32_t dtype;               /* dg_dtype of p/logits, embed and out */
+  const void* p;               /* device [M, ldp]: probabilities, or logits with row stats */
+  int64_t ldp;                 /* >= V, multiple of 8 */
+  const float* row_max;        /* device [M] or NULL */
+  const float* row_sum;        /* device [M] or NULL (set both or neither) */
+  const void* embed;           /* device [V, lde] */
+  int64_t lde;                 /* >= d, multiple of 8 */
+  void* out;                   /* device [M, ldo], dtype */
+  int64_t ldo;                 /* >= d */
+  void* workspace;             /* device, >= dg_selfcond_workspace_size(args) bytes */
+  size_t workspace_bytes;
+} dg_selfcond_args;
+
+dg_status dg_selfcond_embed(const dg_selfcond_args* args, void* stream);
+size_t dg_selfcond_workspace_size(const dg_selfcond_args* args);
+
+/* ------------------------------------------------------------------------------ */
+const char* dg_status_string(dg_status s); /* static string for a status */
+const char* dg_last_error(void);           /* message of this thread's last failed call */
+int dg_abi_version(void);                  /* DG_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

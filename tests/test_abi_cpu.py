@@ -1,0 +1,181 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel launched): libdg.so loads,
+exports every function include/dg.h declares, sizes workspaces, and maps every
+invalid argument to its dg_status with a message, before anything is launched.
+Device pointers here are fake aligned addresses: every call below fails
+validation, which happens before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_denoising_step_amd as dg
+from workloads import pack_seqs, BIDIR, CAUSAL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "dg.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dg_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = dg.load()
+    names = _declared()
+    assert set(names) == set(dg.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dg_abi_version() == 1
+    for s in range(5):
+        assert lib.dg_status_string(s).decode().startswith("DG_")
+
+
+class _T:
+    """Stand-in for a tensor: only what the binding reads."""
+
+    def __init__(self, shape, ptr=FAKE, dtype="bf16"):
+        self.shape = shape
+        self._ptr = ptr
+        import torch
+        self.dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i):
+        s = 1
+        for x in self.shape[i + 1:]:
+            s *= x
+        return s
+
+
+def _attn(**over):
+    seqs = over.pop("seqs", pack_seqs([(64, 32, BIDIR)]))
+    q = over.pop("q", _T((32, 4, 64)))
+    k = over.pop("k", _T((96, 2, 64)))
+    a = dg.make_attn_args(q, k, _T(k.shape), _T(q.shape), seqs, over.pop("window", -1),
+                          over.pop("hq", 4), over.pop("hkv", 2))
+    for key, val in over.items():
+        setattr(a, key[6:] if key.startswith("field_") else key, val)
+    return a
+
+
+def _status(a):
+    lib = dg.load()
+    return lib.dg_attn_mixed(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(num_seqs=0), dg.DG_ERR_INVALID_ARG),
+    (dict(num_seqs=65), dg.DG_ERR_INVALID_ARG),
+    (dict(hq=6, hkv=4), dg.DG_ERR_INVALID_ARG),
+    (dict(hq=12, hkv=4), dg.DG_ERR_UNSUPPORTED),  # G = 3
+    (dict(head_dim=96), dg.DG_ERR_UNSUPPORTED),
+    (dict(window=-2), dg.DG_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), dg.DG_ERR_INVALID_ARG),
+    (dict(scale=-1.0), dg.DG_ERR_INVALID_ARG),
+    (dict(dtype=7), dg.DG_ERR_INVALID_ARG),
+    (dict(field_q=None), dg.DG_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), dg.DG_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), dg.DG_ERR_INVALID_ARG),
+    (dict(kv_chunk=100), dg.DG_ERR_INVALID_ARG),
+    (dict(total_q=31), dg.DG_ERR_INVALID_ARG),
+    (dict(total_kv=95), dg.DG_ERR_INVALID_ARG),
+    (dict(seqs=pack_seqs([(64, 32, 5)])), dg.DG_ERR_INVALID_ARG),
+    (dict(seqs=[(0, 16, 0, 8, BIDIR), (8, 16, 24, 8, BIDIR)], q=_T((24, 4, 64)), k=_T((96, 2, 64))),
+     dg.DG_ERR_INVALID_ARG),  # overlapping query ranges
+])
+def test_attn_validation(change, status):
+    a = _attn(**change)
+    if "head_dim" in change:
+        a.head_dim = change["head_dim"]
+    assert _status(a) == status
+    assert dg.last_error()
+
+
+def test_attn_fp32_head_dim_256_unsupported_and_workspace():
+    a = _attn(q=_T((32, 4, 256), dtype="f32"), k=_T((96, 2, 256), dtype="f32"))
+    assert _status(a) == dg.DG_ERR_UNSUPPORTED
+    # a long prefix splits keys into chunks, which need a workspace; too small is an error
+    seqs = pack_seqs([(8192, 256, BIDIR)])
+    a = _attn(seqs=seqs, q=_T((256, 16, 256)), k=_T((8448, 8, 256)), hq=16, hkv=8)
+    need = dg.attn_workspace_size(a)
+    assert 0 < need < 2**40
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert _status(a) == dg.DG_ERR_WORKSPACE
+    bad = _attn(num_seqs=0)
+    assert dg.attn_workspace_size(bad) == ctypes.c_size_t(-1).value
+
+
+def test_attn_workspace_single_chunk_is_zero():
+    a = _attn()
+    assert dg.attn_workspace_size(a) == 0
+
+
+def _sampler(**over):
+    bufs = dg.SamplerBuffers.__new__(dg.SamplerBuffers)
+    for n in ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
+              "stable_count", "num_accepted", "converged", "mean_entropy"):
+        setattr(bufs, n, _T((256,)))
+    logits = over.pop("logits", _T((256, 4096)))
+    reqs = over.pop("reqs", [(0, 256, 1, 0)])
+    a = dg.make_sampler_args(logits, reqs, 4096, bufs, 64.0)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change", [
+    dict(num_reqs=0), dict(reqs=[(0, 1025, 1, 0)]), dict(reqs=[(200, 100, 1, 0)]),
+    dict(reqs=[(0, 128, 1, 0), (100, 100, 2, 0)]), dict(reqs=[(0, 256, 1, -1)]), dict(vocab=0), dict(ld=4095),
+    dict(ld=4100), dict(budget=float("inf")), dict(budget=-1.0), dict(tau=float("nan")), dict(min_accept=-1),
+    dict(conf_mode=2), dict(combine=3), dict(renoise=2), dict(stable_k=0), dict(step_limit=0), dict(flags=4),
+    dict(logits=None), dict(entropy=None), dict(accept=None), dict(canvas=FAKE + 2), dict(dtype=3),
+])
+def test_sampler_validation(change):
+    a = _sampler(**change)
+    assert dg.load().dg_sampler_step(ctypes.byref(a), None) == dg.DG_ERR_INVALID_ARG
+    assert dg.last_error()
+
+
+def test_sampler_workspace():
+    a = _sampler()
+    need = dg.sampler_workspace_size(a)
+    assert need >= 256 * 1 * 16  # one 16-byte statistics record per row and chunk
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert dg.load().dg_sampler_step(ctypes.byref(a), None) == dg.DG_ERR_WORKSPACE
+    init = _sampler(flags=dg.DG_INIT_CANVAS, logits=None)
+    assert dg.sampler_workspace_size(init) == 0
+
+
+def _selfcond(**over):
+    p = over.pop("p", _T((256, 4096)))
+    e = over.pop("e", _T((4096, 256)))
+    a = dg.make_selfcond_args(p, e, _T((256, 256)))
+    for key, val in over.items():
+        setattr(a, key[6:] if key.startswith("field_") else key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(M=0), dg.DG_ERR_INVALID_ARG), (dict(V=0), dg.DG_ERR_INVALID_ARG), (dict(d=200), dg.DG_ERR_UNSUPPORTED),
+    (dict(ldp=4000), dg.DG_ERR_INVALID_ARG), (dict(lde=100), dg.DG_ERR_INVALID_ARG),
+    (dict(ldo=100), dg.DG_ERR_INVALID_ARG), (dict(field_p=None), dg.DG_ERR_INVALID_ARG),
+    (dict(embed=FAKE + 8), dg.DG_ERR_INVALID_ARG), (dict(row_max=FAKE), dg.DG_ERR_INVALID_ARG),
+    (dict(dtype=2), dg.DG_ERR_INVALID_ARG),
+])
+def test_selfcond_validation(change, status):
+    a = _selfcond(**change)
+    assert dg.load().dg_selfcond_embed(ctypes.byref(a), None) == status
+    assert dg.last_error()
+
+
+def test_selfcond_workspace_is_split_k_partials():
+    a = _selfcond(p=_T((256, 262144)), e=_T((262144, 2048)))
+    a.d = 2048
+    a.ldo = 2048
+    need = dg.selfcond_workspace_size(a)
+    assert need > 0 and need % (256 * 2048 * 4) == 0

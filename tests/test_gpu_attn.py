@@ -1,0 +1,125 @@
+"""GPU parity of dg_attn_mixed against the CPU oracle, through the C ABI.
+
+Bar: max-relative error per (token, head) output row <= 2e-2 (bf16 inputs, fp32
+accumulation; fp32 inputs are checked against the same bar and expected far
+inside it), lse within 1e-3 absolute. Full-size configurations are checked on
+sampled query rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_denoising_step_amd as dg
+from oracle.attn import attn_mixed as ref_attn
+from workloads import attn_case, pack_seqs, Seq, CAUSAL, BIDIR, normal, round_to_bf16
+from tests.gpu_util import DEV, dev, host, max_rel_rows, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _gpu(case_seqs, window, q, k, v, hq, hkv, bf16, kv_chunk=0, out_fill=np.nan):
+    qt, kt, vt = dev(q, bf16), dev(k, bf16), dev(v, bf16)
+    out = torch.full(qt.shape, out_fill, device=DEV, dtype=qt.dtype)
+    lse = torch.full(qt.shape[:2], np.nan, device=DEV, dtype=torch.float32)
+    dg.dg_attn_mixed(qt, kt, vt, out, case_seqs, window, hq, hkv, lse=lse, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+def _compare(seqs, window, q, k, v, hq, hkv, bf16, rows=None, kv_chunk=0, label=""):
+    say(f"[attn] {label}: W={window} rows={'all' if rows is None else len(rows)} chunk={kv_chunk}")
+    out, lse = _gpu(seqs, window, q, k, v, hq, hkv, bf16, kv_chunk)
+    want, wlse = ref_attn(seqs, window, q, k, v, hq, hkv, rows=rows)
+    sel = np.arange(q.shape[0]) if rows is None else np.array(rows)
+    err = max_rel_rows(out[sel], want[sel])
+    lerr = float(np.abs(lse[sel] - wlse[sel]).max())
+    say(f"  max-rel {err:.3e}  lse abs {lerr:.3e}")
+    assert err <= TOL and lerr <= 1e-3, (label, err, lerr)
+    # rows of no request are untouched (still NaN)
+    covered = np.zeros(q.shape[0], bool)
+    for s in seqs:
+        covered[s.q_start:s.q_start + s.num_q] = True
+    assert np.isnan(out[~covered]).all()
+    return err, out
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("window", [32, -1])
+def test_config1_fp32(mode, window):
+    c = attn_case(1).with_mode(mode).with_window(window)
+    q, k, v = c.tensors()
+    err, _ = _compare(c.seqs, window, q, k, v, c.num_q_heads, c.num_kv_heads, False, label=f"config 1 mode={mode}")
+    assert err < 1e-4
+
+
+def test_config2_bf16_all_rows():
+    c = attn_case(2)
+    q, k, v = c.tensors()
+    _compare(c.seqs, -1, q, k, v, 16, 8, True, label="config 2 bidir global P=4096")
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_config3_window_512_sampled(mode):
+    c = attn_case(3).with_mode(mode)
+    q, k, v = c.tensors()
+    rows = [0, 1, 63, 64, 100, 191, 192, 200, 254, 255]
+    _compare(c.seqs, 512, q, k, v, 16, 8, True, rows=rows, label=f"config 3 W=512 mode={mode}")
+
+
+@pytest.mark.parametrize("window", [-1, 512])
+def test_config4_mixed_batch_sampled(window):
+    c = attn_case(4)
+    q, k, v = c.tensors()
+    rows = []
+    for s in c.seqs:
+        rows += [s.q_start, s.q_start + 1, s.q_start + s.num_q // 2, s.q_start + s.num_q - 1]
+    rows += [700, 1500, 2047]
+    _compare(c.seqs, window, q, k, v, 16, 8, True, rows=sorted(set(rows)), label=f"config 4 mixed W={window}")
+
+
+def test_config5_long_context_sampled():
+    c = attn_case(5)
+    q, k, v = c.tensors()
+    rows = []
+    for s in c.seqs:
+        rows += [s.q_start, s.q_start + 129, s.q_start + s.num_q - 1]
+    _compare(c.seqs, -1, q, k, v, 16, 8, True, rows=rows, label="config 5 long context")
+
+
+@pytest.mark.parametrize("D,bf16", [(64, True), (128, True), (256, True), (64, False), (128, False)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (16, 2)])
+def test_shapes_ragged_and_split(D, bf16, hq, hkv):
+    """Ragged token counts, empty prefix, empty request, forced key splits, every
+    supported head_dim and group size, both modes, windows."""
+    spec = [(0, 37, CAUSAL), (70, 0, BIDIR), (130, 45, BIDIR), (5, 200, CAUSAL)]
+    seqs = pack_seqs(spec)
+    tq = sum(n for _, n, _ in spec)
+    tk = sum(p + n for p, n, _ in spec)
+    seed = 1000 + D + hq
+    q = normal(seed, (tq, hq, D), bf16=bf16)
+    k = normal(seed + 1, (tk, hkv, D), bf16=bf16)
+    v = normal(seed + 2, (tk, hkv, D), bf16=bf16)
+    for window, chunk in ((-1, 0), (-1, 64), (17, 0), (0, 0), (40, 128)):
+        _compare(seqs, window, q, k, v, hq, hkv, bf16, kv_chunk=chunk,
+                 label=f"D={D} bf16={bf16} G={hq // hkv}")
+
+
+def test_batch_independence_bit_exact():
+    """A request's output does not depend on the rest of the batch (work split per request)."""
+    c = attn_case(4)
+    q, k, v = c.tensors()
+    _, full = _compare(c.seqs, 512, q, k, v, 16, 8, True, rows=[c.seqs[2].q_start], label="batch")
+    for s in c.seqs[1:3]:
+        qs = slice(s.q_start, s.q_start + s.num_q)
+        ks = slice(s.kv_start, s.kv_start + s.prefix_len + s.num_q)
+        alone, _ = _gpu([Seq(0, s.num_q, 0, s.prefix_len, s.mode)], 512, q[qs], k[ks], v[ks], 16, 8, True)
+        assert np.array_equal(alone, full[qs])
+
+
+def test_repeat_is_bit_identical():
+    c = attn_case(2)
+    q, k, v = c.tensors()
+    a, la = _gpu(c.seqs, -1, q, k, v, 16, 8, True)
+    b, lb = _gpu(c.seqs, -1, q, k, v, 16, 8, True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
