@@ -205,12 +205,15 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(
     // entropy in nats: ln Z - (sum p*y) * ln 2, with y the log2-scaled logit offsets
     const double h = (double)kLn2 * (log2((double)Z) - (double)T / (double)Z);
     const float H = fmaxf(0.f, (float)h);
+    // Z sums 2^y with y offset by the rounding of -m*log2e; fma recovers that offset
+    // exactly, so the row sum is sum exp(l - m) (the entropy is offset-invariant).
+    const float zsum = Z * fast_exp2(-fmaf(m, kLog2e, nm2));
     const bool ent_in = flags & DG_ENTROPY_IN;
     if (!ent_in) entropy[row] = H;
     if (conf_mode == DG_CONF_NEG_ENTROPY) conf[row] = -(ent_in ? entropy[row] : H);
-    else if (!ent_in) conf[row] = 1.f / Z;
+    else if (!ent_in) conf[row] = 1.f / zsum;
     row_max[row] = m;
-    row_sum[row] = Z;
+    row_sum[row] = zsum;
     argmax[row] = amax;
   }
 
