@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Denoise steps/s of one block-diffusion denoising step on one MI355X.
+
+A step is the whole hot path: mixed-mode attention for the canvas (dg_attn_mixed),
+the DiffusionSampler step (dg_sampler_step) and the self-conditioning average
+(dg_selfcond_embed). Workload: batch-1 global-attention layer, 256-token
+bidirectional canvas on a 4096-token committed prefix, 16 query / 8 KV heads x
+head_dim 256, sampler over bf16 logits [256 x 262144] with a 128-nat budget,
+self-conditioning against a bf16 embedding table [262144 x 2048]. The denoise loop
+runs blocks to the convergence rule (argmax stable 3 steps or mean entropy < 0.05
+nats, limit 48): every block starts with a random canvas and its logits follow the
+synthetic driver sequence (positions settle over 8 steps), so a block converges
+after 12 steps and a new block starts. All inputs are synthetic and seeded, and
+resident in HBM before the timed region.
+
+Prints one JSON line: whole-job steps/s, per-kernel times with HIP events on the
+launch stream, the roofline of the dominant kernel and the CPU oracle's rate on a
+bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/s (256-tok canvas) + attn MFMA util, sampler HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+# workload sizes
+CANVAS, PREFIX, HQ, HKV, D = 256, 4096, 16, 8, 256
+VOCAB, EMBED = 262144, 2048
+BUDGET, STABLE_K, TAU, STEP_LIMIT = 128.0, 3, 0.05, 48
+
+
+def algorithmic():
+    """Work the method must do per step (allowed query-key pairs, each byte once)."""
+    pairs = CANVAS * (PREFIX + CANVAS)  # every canvas query sees the whole prefix and canvas
+    attn_flop = 4 * D * HQ * pairs
+    attn_bytes = 2 * (2 * CANVAS * HQ * D + 2 * (PREFIX + CANVAS) * HKV * D)  # Q, O, K, V in bf16
+    samp_bytes = 2 * CANVAS * VOCAB + 32 * CANVAS  # logits once + per-row outputs
+    sc_flop = 2 * CANVAS * VOCAB * EMBED
+    sc_bytes = 2 * (VOCAB * EMBED + CANVAS * VOCAB + CANVAS * EMBED)
+    return dict(attn_flop=attn_flop, attn_bytes=attn_bytes, samp_bytes=samp_bytes, sc_flop=sc_flop,
+                sc_bytes=sc_bytes)
+
+
+def cpu_baseline(q, k, v, logits0, E, seqs, seed, rows=32):
+    """The oracle, as it stands, on `rows` of the 256 canvas rows of one step; the
+    time is scaled to a whole step (every part is per canvas row)."""
+    from oracle.attn import attn_mixed
+    from oracle.sampler import sampler_step, CONV_OR
+    from oracle.selfcond import selfcond_embed
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    t0 = time.perf_counter()
+    attn_mixed(seqs, -1, q, k, v, HQ, HKV, rows=range(rows))
+    sampler_step(logits0[:rows], [(0, rows, seed, 0)], VOCAB, BUDGET, 1, np.zeros(rows, np.int64),
+                 np.full(rows, -1), [0], stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=CONV_OR)
+    selfcond_embed(E, logits=logits0[:rows])
+    dt = time.perf_counter() - t0
+    per_step = dt * CANVAS / rows
+    return {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of {CANVAS} canvas rows of one step (attention, sampler, self-conditioning), "
+                      f"{dt:.1f} s measured, scaled x{CANVAS // rows} to a whole step",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_denoising_step_amd as dg
+    from workloads import attn_case, embed_table, driver_pool, driver_rows, request_seeds
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dg.load()
+
+    # ---- inputs, resident in HBM before timing ---------------------------------------
+    case = attn_case(2)
+    q_np, k_np, v_np = case.tensors()
+    q = torch.from_numpy(q_np).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(k_np).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(v_np).to(dev).to(torch.bfloat16)
+    E_np = embed_table(2, VOCAB, EMBED, bf16=True)
+    E = torch.from_numpy(E_np).to(dev).to(torch.bfloat16)
+    pool_np = driver_pool(VOCAB, bf16=True)
+    pool = torch.from_numpy(pool_np).to(dev).to(torch.bfloat16)
+    settle = 9  # steps >= 8 read the settled rows: 9 distinct logits tensors cover every step
+    step_logits = [pool[torch.from_numpy(driver_rows(t)).to(dev)].contiguous() for t in range(settle)]
+    seed = request_seeds(2, 1)[0]
+
+    attn_out = torch.empty_like(q)
+    lse = torch.empty(CANVAS, HQ, device=dev, dtype=torch.float32)
+    # the sampler also writes block-scaled probabilities for self-conditioning
+    bufs = dg.SamplerBuffers(CANVAS, 1, dev, vocab=VOCAB, probs_dtype=torch.bfloat16)
+    sc_out = torch.empty(CANVAS, EMBED, device=dev, dtype=torch.bfloat16)
+
+    attn_call = dg.prepare_attn(q, k, v, attn_out, case.seqs, -1, HQ, HKV, lse=lse)
+    samp_calls = [dg.prepare_sampler(step_logits[t], [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET,
+                                     stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR)
+                  for t in range(settle)]
+    init_call = dg.prepare_sampler(None, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
+                                   num_rows=CANVAS)
+    sc_call = dg.prepare_selfcond(bufs.probs, E, sc_out, p_scale=bufs.probs_scale)
+
+    stream = torch.cuda.current_stream()
+    flags = torch.zeros(2, dtype=torch.int32, pin_memory=True)  # converged flag of the last two steps
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    state = {"t": 0, "block": 0, "issued": 0, "pending": None}
+
+    def start_block():
+        seed_b = (seed + state["block"]) & ((1 << 64) - 1)
+        init_call.args._keep[0].step = 0
+        init_call.args._keep[0].seed = seed_b
+        init_call(stream)
+        state["t"] = 0
+        state["pending"] = None
+
+    def one_step(ev=None):
+        """Enqueue one step and its 4-byte flag read-back; return the previous step's flag."""
+        t = state["t"]
+        i = min(t, settle - 1)
+        samp = samp_calls[i]
+        samp.args._keep[0].step = t
+        samp.args._keep[0].seed = (seed + state["block"]) & ((1 << 64) - 1)
+        if ev is not None:
+            ev[0].record(stream)
+        attn_call(stream)
+        if ev is not None:
+            ev[1].record(stream)
+        samp(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        sc_call(stream)
+        if ev is not None:
+            ev[3].record(stream)
+        slot = state["issued"] % 2
+        flags[slot:slot + 1].copy_(bufs.converged, non_blocking=True)
+        fe = torch.cuda.Event()
+        fe.record(stream)
+        state["issued"] += 1
+        state["t"] = t + 1
+        # the host reads the previous step's flag while this step runs on the GPU
+        prev_done = False
+        if state["pending"] is not None:
+            pev, pslot = state["pending"]
+            pev.synchronize()
+            prev_done = bool(flags[pslot].item())
+        state["pending"] = (fe, slot)
+        return prev_done
+
+    def run(n, events=None):
+        for s_ in range(n):
+            if one_step(events[s_] if events is not None else None) or state["t"] >= STEP_LIMIT:
+                state["block"] += 1  # converged: the step just issued was speculative; start a new block
+                start_block()
+
+    start_block()
+    run(args.warmup)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    blocks0 = state["block"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps, events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    blocks = state["block"] - blocks0
+
+    ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in events])
+    attn_ms, samp_ms, sc_ms = (float(x) for x in ms.mean(axis=0))
+    alg = algorithmic()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = args.steps / elapsed
+
+    attn_tflops = alg["attn_flop"] / (attn_ms * 1e-3) / 1e12
+    samp_gbs = alg["samp_bytes"] / (samp_ms * 1e-3) / 1e9
+    sc_gbs = alg["sc_bytes"] / (sc_ms * 1e-3) / 1e9
+    sc_tflops = alg["sc_flop"] / (sc_ms * 1e-3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "batch-1 global-attention denoise step: canvas 256 (bidirectional) on prefix 4096, "
+                        "16 q / 8 kv heads x 256; sampler on bf16 logits [256 x 262144], budget 128 nats; "
+                        "self-conditioning with bf16 E [262144 x 2048]; blocks run to argmax-stable-3 or "
+                        "mean entropy < 0.05 (limit 48)",
+            "canvas": CANVAS, "prefix": PREFIX, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+            "vocab": VOCAB, "embed_dim": EMBED, "blocks_in_timed_region": blocks,
+        },
+        "roofline": {
+            "kernel": "dg_selfcond_embed (selfcond_gemm_dma + selfcond_reduce)",
+            "bound": "hbm",
+            "achieved": round(sc_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(sc_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "kernels": {
+            "attn_mixed": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 1),
+                           "frac_bf16_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
+            "sampler_step": {"ms": round(samp_ms, 4), "gbs": round(samp_gbs, 1),
+                             "frac_hbm_peak": round(samp_gbs / PEAK_HBM_GBS, 4)},
+            "selfcond_embed": {"ms": round(sc_ms, 4), "gbs": round(sc_gbs, 1), "tflops": round(sc_tflops, 1),
+                               "frac_hbm_peak": round(sc_gbs / PEAK_HBM_GBS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        logits0 = pool_np[driver_rows(0)]
+        line["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, logits0, E_np, case.seqs, seed)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

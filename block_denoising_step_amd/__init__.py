@@ -26,6 +26,7 @@ DG_CONV_AND, DG_CONV_OR = 0, 1
 DG_ENTROPY_IN, DG_INIT_CANVAS = 1, 2
 DG_MAX_SEQS = DG_MAX_REQS = 64
 DG_MAX_CANVAS = 1024
+DG_PROB_BLOCK = 8192
 
 _c_int32, _c_int64, _c_uint32, _c_uint64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
 _vp, _fp = ctypes.c_void_p, ctypes.c_void_p
@@ -58,12 +59,13 @@ class DgSamplerArgs(ctypes.Structure):
                 ("entropy", _vp), ("conf", _vp), ("row_max", _vp), ("row_sum", _vp), ("argmax", _vp),
                 ("cand", _vp), ("accept", _vp), ("canvas", _vp), ("prev_argmax", _vp),
                 ("stable_count", _vp), ("num_accepted", _vp), ("converged", _vp), ("mean_entropy", _vp),
+                ("probs", _vp), ("ldq", _c_int64), ("probs_scale", _vp),
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DgSelfcondArgs(ctypes.Structure):
     _fields_ = [("M", _c_int32), ("V", _c_int32), ("d", _c_int32), ("dtype", _c_int32),
-                ("p", _vp), ("ldp", _c_int64), ("row_max", _vp), ("row_sum", _vp),
+                ("p", _vp), ("ldp", _c_int64), ("row_max", _vp), ("row_sum", _vp), ("p_scale", _vp),
                 ("embed", _vp), ("lde", _c_int64), ("out", _vp), ("ldo", _c_int64),
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
 
@@ -198,7 +200,7 @@ def dg_attn_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
 class SamplerBuffers:
     """Device buffers of one sampler call: per-row outputs and per-request state."""
 
-    def __init__(self, num_rows: int, num_reqs: int, device):
+    def __init__(self, num_rows: int, num_reqs: int, device, vocab: int = 0, probs_dtype=None):
         f = dict(dtype=torch.float32, device=device)
         i = dict(dtype=torch.int32, device=device)
         self.entropy = torch.zeros(num_rows, **f)
@@ -215,12 +217,19 @@ class SamplerBuffers:
         self.converged = torch.zeros(num_reqs, **i)
         self.mean_entropy = torch.zeros(num_reqs, **f)
         self.workspace: Optional[torch.Tensor] = None
+        # block-scaled probabilities (optional): w [num_rows, vocab] and scales
+        self.probs = self.probs_scale = None
+        if vocab and probs_dtype is not None:
+            ld = (vocab + 7) // 8 * 8
+            self.probs = torch.empty(num_rows, ld, dtype=probs_dtype, device=device)[:, :vocab]
+            self.probs_scale = torch.empty(num_rows, (vocab + DG_PROB_BLOCK - 1) // DG_PROB_BLOCK, **f)
 
 
 def make_sampler_args(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, int, int, int]], vocab: int,
                       bufs: SamplerBuffers, budget: float, min_accept: int = 1,
                       conf_mode: int = DG_CONF_NEG_ENTROPY, renoise: int = 1, stable_k: int = 3, tau: float = 0.05,
-                      step_limit: int = 48, combine: int = DG_CONV_AND, flags: int = 0, num_rows: Optional[int] = None):
+                      step_limit: int = 48, combine: int = DG_CONV_AND, flags: int = 0, num_rows: Optional[int] = None,
+                      probs: Optional[torch.Tensor] = None, probs_scale: Optional[torch.Tensor] = None):
     req_arr = (DgSreq * max(1, len(reqs)))()
     for i, (row_start, n, seed, step) in enumerate(reqs):
         req_arr[i] = DgSreq(row_start, n, seed, step, 0)
@@ -237,6 +246,8 @@ def make_sampler_args(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, 
     for name in ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
                  "stable_count", "num_accepted", "converged", "mean_entropy"):
         setattr(a, name, _ptr(getattr(bufs, name)))
+    a.probs, a.probs_scale = _ptr(probs), _ptr(probs_scale)
+    a.ldq = probs.stride(0) if probs is not None else 0
     a._keep = req_arr
     return a
 
@@ -248,7 +259,10 @@ def sampler_workspace_size(args: DgSamplerArgs) -> int:
 def dg_sampler_step(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, int, int, int]], vocab: int,
                     bufs: SamplerBuffers, budget: float, stream=None, **kw) -> None:
     """One DiffusionSampler denoise step (see include/dg.h). reqs: (row_start, num_rows,
-    seed, step) per request. Outputs and state live in `bufs`."""
+    seed, step) per request. Outputs and state live in `bufs` (block-scaled
+    probabilities too, when bufs holds them)."""
+    kw.setdefault("probs", bufs.probs)
+    kw.setdefault("probs_scale", bufs.probs_scale)
     a = make_sampler_args(logits, reqs, vocab, bufs, budget, **kw)
     like = logits if logits is not None else bufs.canvas
     bufs.workspace = _workspace(sampler_workspace_size(a), like, bufs.workspace)
@@ -260,7 +274,7 @@ def dg_sampler_step(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, in
 # ---- dg_selfcond_embed -----------------------------------------------------------
 
 def make_selfcond_args(p: torch.Tensor, embed: torch.Tensor, out: torch.Tensor, row_max=None, row_sum=None,
-                       num_cols: Optional[int] = None):
+                       num_cols: Optional[int] = None, p_scale=None):
     a = DgSelfcondArgs()
     a.M = p.shape[0]
     a.V = num_cols if num_cols is not None else p.shape[1]
@@ -268,6 +282,7 @@ def make_selfcond_args(p: torch.Tensor, embed: torch.Tensor, out: torch.Tensor, 
     a.dtype = _dtype(p)
     a.p, a.ldp = _ptr(p), p.stride(0)
     a.row_max, a.row_sum = _ptr(row_max), _ptr(row_sum)
+    a.p_scale = _ptr(p_scale)
     a.embed, a.lde = _ptr(embed), embed.stride(0)
     a.out, a.ldo = _ptr(out), out.stride(0)
     return a
@@ -279,12 +294,57 @@ def selfcond_workspace_size(args: DgSelfcondArgs) -> int:
 
 def dg_selfcond_embed(p: torch.Tensor, embed: torch.Tensor, out: torch.Tensor,
                       row_max: Optional[torch.Tensor] = None, row_sum: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
-    """out = P . E with P given, or P = softmax rebuilt from logits and row stats
-    (see include/dg.h). Returns the workspace tensor used (reusable)."""
-    a = make_selfcond_args(p, embed, out, row_max, row_sum)
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      p_scale: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """out = P . E with P given, rebuilt from logits and row stats, or block-scaled
+    (p holds w, p_scale the per-block scales; see include/dg.h). Returns the
+    workspace tensor used (reusable)."""
+    a = make_selfcond_args(p, embed, out, row_max, row_sum, p_scale=p_scale)
     ws = _workspace(selfcond_workspace_size(a), p, workspace)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().dg_selfcond_embed(ctypes.byref(a), _stream(stream)))
     return ws
+
+
+# ---- prepared calls (argument structs built once, reused every step) ----------------
+
+class Prepared:
+    """A libdg call with its argument struct and workspace fixed; calling it only
+    passes the struct and the stream. `args` stays editable (e.g. a request's step)."""
+
+    def __init__(self, fn, args, keep=()):
+        self._fn = fn
+        self.args = args
+        self._keep = keep
+
+    def __call__(self, stream=None) -> None:
+        _check(self._fn(ctypes.byref(self.args), _stream(stream)))
+
+
+def prepare_attn(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse=None, scale=0.0, kv_chunk=0):
+    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk)
+    ws = _workspace(attn_workspace_size(a), q, None)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel()
+    return Prepared(load().dg_attn_mixed, a, (ws,))
+
+
+def prepare_sampler(logits, reqs, vocab, bufs, budget, **kw):
+    if logits is not None:
+        kw.setdefault("probs", bufs.probs)
+        kw.setdefault("probs_scale", bufs.probs_scale)
+    a = make_sampler_args(logits, reqs, vocab, bufs, budget, **kw)
+    like = logits if logits is not None else bufs.canvas
+    bufs.workspace = _workspace(sampler_workspace_size(a), like, bufs.workspace)
+    a.workspace = _ptr(bufs.workspace)
+    a.workspace_bytes = 0 if bufs.workspace is None else bufs.workspace.numel()
+    return Prepared(load().dg_sampler_step, a, (bufs,))
+
+
+def prepare_selfcond(p, embed, out, row_max=None, row_sum=None, p_scale=None):
+    a = make_selfcond_args(p, embed, out, row_max, row_sum, p_scale=p_scale)
+    ws = _workspace(selfcond_workspace_size(a), p, None)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel()
+    return Prepared(load().dg_selfcond_embed, a, (ws,))

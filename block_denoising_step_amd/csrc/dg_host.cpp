@@ -171,6 +171,9 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   for (const void* p : ptrs)
     if (!p || !aligned4(p)) return bad(DG_ERR_INVALID_ARG, "every output/state pointer must be non-NULL and 4-byte aligned");
   if (!a->accept) return bad(DG_ERR_INVALID_ARG, "accept is NULL");
+  if ((a->probs == nullptr) != (a->probs_scale == nullptr)) return bad(DG_ERR_INVALID_ARG, "set both probs and probs_scale, or neither");
+  if (a->probs && (!aligned16(a->probs) || !aligned4(a->probs_scale))) return bad(DG_ERR_INVALID_ARG, "probs must be 16-byte aligned");
+  if (a->probs && (a->ldq < a->vocab || a->ldq % 8)) return bad(DG_ERR_INVALID_ARG, "ldq must be >= vocab and a multiple of 8");
   std::vector<std::pair<int64_t, int64_t>> r;
   for (int i = 0; i < a->num_reqs; ++i) {
     const dg_sreq& q = a->reqs[i];
@@ -186,7 +189,8 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   plan->chunk = a->dtype == DG_BF16 ? 16384 : 8192;
   plan->num_chunks = (int)ceil_div(a->vocab, plan->chunk);
   if (plan->num_chunks > 1024) return bad(DG_ERR_UNSUPPORTED, "vocab too large (more than 1024 row-pass chunks)");
-  plan->bytes = init ? 0 : align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
+  plan->counter_offset = align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
+  plan->bytes = init ? 0 : plan->counter_offset + align_up(DG_MAX_REQS * sizeof(int32_t), 256);
   return DG_OK;
 }
 
@@ -204,20 +208,38 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   if (!a->p || !a->embed || !a->out) return bad(DG_ERR_INVALID_ARG, "p, embed and out must be non-NULL");
   if (!aligned16(a->p) || !aligned16(a->embed) || !aligned16(a->out)) return bad(DG_ERR_INVALID_ARG, "p, embed and out must be 16-byte aligned");
   if ((a->row_max == nullptr) != (a->row_sum == nullptr)) return bad(DG_ERR_INVALID_ARG, "set both row_max and row_sum, or neither");
-  plan->tile_m = 128;
-  plan->tile_n = 128;
-  plan->tile_k = a->dtype == DG_BF16 ? 64 : 32;  // 128 bytes of each A row per K step
+  if (a->p_scale && a->row_max) return bad(DG_ERR_INVALID_ARG, "p_scale and row_max/row_sum are exclusive");
+  const bool scaled = a->p_scale != nullptr;
+  const bool fused = a->row_max != nullptr;
+  plan->dma = a->dtype == DG_BF16 && a->V % 32 == 0;
+  plan->tile_m = 256;
+  plan->tile_n = 256;
+  plan->tile_k = plan->dma ? 32 : (a->dtype == DG_BF16 ? 64 : 32);
   plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
-  plan->n_tiles = a->d / plan->tile_n;
-  // split-K so that the grid is about two work groups per CU, in slices of whole K steps
+  plan->n_tiles = (int)ceil_div(a->d, plan->tile_n);
+  // split-K: about one work group per CU, in slices of at least kMinSteps K steps
+  constexpr int64_t kCUs = 256, kMinSteps = 8;
   const int64_t base = (int64_t)plan->m_tiles * plan->n_tiles;
-  const int64_t ksteps = ceil_div(a->V, plan->tile_k);
-  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(ksteps, ceil_div(512, base)));
-  const int64_t steps_per_split = ceil_div(ksteps, splits);
-  splits = ceil_div(ksteps, steps_per_split);
-  plan->splits = (int)splits;
-  plan->k_per_split = (int)(steps_per_split * plan->tile_k);
-  plan->bytes = splits > 1 ? align_up((size_t)splits * a->M * a->d * sizeof(float), 256) : 0;
+  const int64_t target = std::max<int64_t>(1, ceil_div(kCUs, base));
+  int64_t k_per_split;
+  if (scaled) {
+    // every slice inside one scale block: a power-of-two fraction of DG_PROB_BLOCK
+    k_per_split = DG_PROB_BLOCK;
+    while (k_per_split > plan->tile_k * kMinSteps && ceil_div(a->V, k_per_split) < target) k_per_split /= 2;
+  } else {
+    const int64_t ksteps = ceil_div(a->V, plan->tile_k);
+    const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(target, ksteps / kMinSteps));
+    k_per_split = ceil_div(ksteps, splits) * plan->tile_k;
+  }
+  plan->splits = (int)ceil_div(a->V, k_per_split);
+  plan->k_per_split = (int)k_per_split;
+  plan->part_offset = 0;
+  // partials in whole 256 x 256 tiles (MFMA register layout)
+  size_t bytes = plan->splits > 1 ? align_up((size_t)plan->splits * plan->m_tiles * plan->n_tiles *
+                                             plan->tile_m * plan->tile_n * sizeof(float), 256) : 0;
+  plan->p_offset = bytes;
+  if (plan->dma && fused) bytes += align_up((size_t)a->M * a->V * 2, 256);
+  plan->bytes = bytes;
   return DG_OK;
 }
 

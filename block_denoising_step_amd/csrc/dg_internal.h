@@ -49,20 +49,24 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg);
 // ---- sampler -----------------------------------------------------------------
 
 struct SamplerPlan {
-  int chunk;        // vocabulary entries per row-pass work group
-  int num_chunks;   // chunks per row
-  size_t bytes;     // workspace bytes (per-chunk statistics)
+  int chunk;              // vocabulary entries per row-pass work group
+  int num_chunks;         // chunks per row
+  size_t counter_offset;  // workspace: per-request completion counters (int32)
+  size_t bytes;           // workspace bytes (per-chunk statistics, counters)
 };
 dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char** msg);
 
 // ---- self-conditioning -------------------------------------------------------
 
 struct SelfcondPlan {
+  int dma;                     // 1: LDS-DMA kernel (bf16, V % 32 == 0); 0: register-staged kernel
   int tile_m, tile_n, tile_k;  // output tile per work group, K step
   int m_tiles, n_tiles;
   int splits;                  // split-K slices over V
   int k_per_split;             // vocabulary rows per slice (multiple of tile_k)
-  size_t bytes;                // workspace: fp32 partials [splits][M][d]
+  size_t part_offset;          // workspace: fp32 partials [splits][M][d] (splits > 1)
+  size_t p_offset;             // workspace: rebuilt bf16 probabilities [M][V] (logits mode, DMA kernel)
+  size_t bytes;
 };
 dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const char** msg);
 

@@ -8,10 +8,12 @@
 //   sampler_finalize  one work group per row: merges the chunk statistics in chunk
 //                     order, writes max, sum, entropy, confidence and argmax, then
 //                     draws the candidate by inverse CDF - walk the chunk masses to
-//                     the chunk holding u*Z, re-read that one chunk.
-//   sampler_select    one work group per request: rank sort by confidence, exact
-//                     integer prefix sum of entropies, budget cut, canvas update and
-//                     convergence bookkeeping.
+//                     the chunk holding u*Z, re-read that one chunk (vector loads, a
+//                     block prefix scan). The last row of a request to finish (an
+//                     atomic count per request) then runs the request's selection:
+//                     rank sort by confidence, exact integer prefix sum of entropies,
+//                     budget cut, canvas update and convergence bookkeeping.
+//   sampler_init      start of a block: random canvas, state reset.
 //
 // What these compute is stated in [P1] ("DiffusionGemma: vLLM에서 네이티브로 처음
 // 지원되는 첫 번째 Diffusion LLM") section "샘플링 루프와 엔트로피 경계 디노이징",
@@ -28,8 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLoads = 8;  // 16-byte loads per thread per chunk
-constexpr int kSelectThreads = DG_MAX_CANVAS;
-constexpr int kFixedShift = 40;
+constexpr int kPerThread = DG_MAX_CANVAS / kThreads;  // canvas positions per thread in the selection
 
 struct ReqTable {
   int32_t n;
@@ -100,6 +101,46 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int i = 1; i < kThreads / 64; ++i) r += red[i];
   return r;
 }
+__device__ __forceinline__ int block_max_int(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+  return r;
+}
+// Exclusive prefix sum over the block in thread order (fixed association).
+__device__ __forceinline__ float block_exclusive_scan(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  float off = 0.f;
+  for (int i = 0; i < w; ++i) off += red[i];
+  return off + x - v;
+}
+__device__ __forceinline__ long long block_sum_ll(long long v, long long* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  long long r = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) r += red[i];
+  return r;
+}
 __device__ __forceinline__ int block_min_int(int v, int* red) {
   v = wave_min_int(v);
   const int w = threadIdx.x >> 6;
@@ -113,17 +154,25 @@ __device__ __forceinline__ int block_min_int(int v, int* red) {
 }
 
 // ---- row pass ---------------------------------------------------------------------
-template <bool kBf16>
+// kTail: the launch covers only the last, partial chunk of every row (elements past V
+// read as -inf); otherwise it covers the first `nfull` whole chunks of every row and
+// needs no bounds checks, which keeps its register use low.
+template <bool kBf16, bool kStore, bool kTail>
 __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restrict__ logits, int64_t ld, int V,
-                                                            int chunk, int num_chunks, float4* __restrict__ stats) {
+                                                            int chunk, int num_chunks, int nfull,
+                                                            float4* __restrict__ stats, void* __restrict__ probs,
+                                                            int64_t ldq, int* __restrict__ counters, int num_reqs) {
   using VT = Vec<kBf16>;
   __shared__ float redf[kThreads / 64];
   __shared__ int redi[kThreads / 64];
-  const int c = blockIdx.x % num_chunks, row = blockIdx.x / num_chunks, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid < num_reqs) counters[tid] = 0;  // finalize counts finished rows per request
+  const int c = kTail ? num_chunks - 1 : blockIdx.x % nfull;
+  const int row = kTail ? blockIdx.x : blockIdx.x / nfull;
   const char* rowp = reinterpret_cast<const char*>(logits) + (int64_t)row * ld * (kBf16 ? 2 : 4);
   const int c0 = c * chunk;
   uint4 buf[kLoads];
-  if (c0 + chunk <= V) {
+  if (!kTail) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       buf[i] = *reinterpret_cast<const uint4*>(rowp + ((int64_t)c0 + (i * kThreads + tid) * VT::n) * (kBf16 ? 2 : 4));
@@ -139,21 +188,54 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
   const float m = block_max(mx, redf);
   if (m == kNegInf) {  // chunk without a finite logit carries no mass
     if (tid == 0) stats[(int64_t)row * num_chunks + c] = make_float4(kNegInf, 0.f, 0.f, __int_as_float(INT_MAX));
+    if (kStore) {
+      char* qrow = reinterpret_cast<char*>(probs) + (int64_t)row * ldq * (kBf16 ? 2 : 4);
+      for (int i = 0; i < kLoads; ++i)
+        for (int e = 0; e < VT::n; ++e) {
+          const int v = c0 + (i * kThreads + tid) * VT::n + e;
+          if (v < V) {
+            if (kBf16) reinterpret_cast<uint16_t*>(qrow)[v] = 0;
+            else reinterpret_cast<float*>(qrow)[v] = 0.f;
+          }
+        }
+    }
     return;
   }
   const float nm2 = -m * kLog2e;
   float z = 0.f, t = 0.f;
   int first = INT_MAX;
+  // With kStore the pass also writes w = 2^y of the chunk (block-scaled probabilities).
+  char* qrow = kStore ? reinterpret_cast<char*>(probs) + (int64_t)row * ldq * (kBf16 ? 2 : 4) : nullptr;
 #pragma unroll
   for (int i = kLoads - 1; i >= 0; --i) {
+    float wl[VT::n];
 #pragma unroll
     for (int e = VT::n - 1; e >= 0; --e) {
       const float v = VT::get(buf[i], e);
       const float y = fmaxf(fmaf(v, kLog2e, nm2), -200.f);  // clamp keeps 0 * y finite for -inf logits
       const float w = fast_exp2(y);
+      wl[e] = w;
       z += w;
       t = fmaf(w, y, t);
       if (v == m) first = c0 + (i * kThreads + tid) * VT::n + e;  // ends at the lowest index
+    }
+    if (kStore) {
+      const int v0 = c0 + (i * kThreads + tid) * VT::n;
+      if (!kTail) {
+        const uint4 wv = kBf16 ? make_uint4(pack_bf16(wl[0], wl[1]), pack_bf16(wl[2], wl[3]),
+                                            pack_bf16(wl[4], wl[5]), pack_bf16(wl[6], wl[7]))
+                               : make_uint4(__float_as_uint(wl[0]), __float_as_uint(wl[1]), __float_as_uint(wl[2]),
+                                            __float_as_uint(wl[3]));
+        *reinterpret_cast<uint4*>(qrow + (int64_t)v0 * (kBf16 ? 2 : 4)) = wv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < VT::n; ++e)
+          if (v0 + e < V) {
+            if (kBf16) reinterpret_cast<__bf16*>(qrow)[v0 + e] = (__bf16)wl[e];
+            else reinterpret_cast<float*>(qrow)[v0 + e] = wl[e];
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep one 16-byte group's values live at a time
     }
   }
   const float zs = block_sum(z, redf);
@@ -162,22 +244,153 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
   if (tid == 0) stats[(int64_t)row * num_chunks + c] = make_float4(m, zs, ts, __int_as_float(am));
 }
 
-// ---- finalize: per-row statistics and candidate draw ---------------------------
+// ---- finalize: per-row statistics, candidate draw, and (last row of a request) the selection
+
+struct SelectParams {
+  int vocab, min_accept, conf_mode, renoise, stable_k, step_limit, combine;
+  float budget, tau;
+  uint32_t flags;
+};
+
+struct RowOut {
+  float *entropy, *conf, *row_max, *row_sum;
+  int *argmax, *cand;
+  float* probs_scale;
+  uint8_t* accept;
+  int *canvas, *prev_argmax, *stable_count, *num_accepted, *converged;
+  float* mean_entropy;
+  int* counters;
+};
+
+__device__ __forceinline__ int renoise_token(uint64_t seed, int step, int j, int stream, int vocab) {
+  const uint64_t x = philox_word0(seed, (uint64_t)step, (uint64_t)j, (uint64_t)stream);
+  return (int)(((x >> 32) * (uint64_t)vocab) >> 32);
+}
+
+// Selection for request r by one work group of kThreads: rank sort by (confidence
+// desc, position asc), exact integer prefix sum of floor(H * 2^40), budget cut, canvas
+// update and convergence bookkeeping. Positions j = tid + kThreads * q.
+__device__ void select_request(int r, const ReqTable& reqs, const SelectParams& sp, const RowOut& o) {
+  __shared__ float key[DG_MAX_CANVAS];
+  __shared__ long long sorted[DG_MAX_CANVAS];
+  __shared__ long long wred[kThreads / 64];
+  __shared__ int ired[kThreads / 64];
+  __shared__ long long chunk_tot[kThreads];
+  const int tid = threadIdx.x;
+  const int n = reqs.num_rows[r], step = reqs.step[r], row0 = reqs.row_start[r];
+  const uint64_t seed = reqs.seed[r];
+  float c[kPerThread];
+  long long fx[kPerThread];
+  long long sum = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int j = tid + kThreads * q;
+    c[q] = kNegInf;
+    fx[q] = 0;
+    if (j < n) {
+      const float h = o.entropy[row0 + j];
+      c[q] = sp.conf_mode == DG_CONF_NEG_ENTROPY ? -h : o.conf[row0 + j];
+      fx[q] = (long long)floor((double)h * 0x1p40);  // exact: h * 2^40 is exact in double
+      sum += fx[q];
+      key[j] = c[q];
+    }
+  }
+  __syncthreads();
+  int rank[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int j = tid + kThreads * q;
+    rank[q] = 0;
+    if (j < n) {
+      int rk = 0;
+      for (int i = 0; i < n; ++i) {
+        const float ki = key[i];
+        rk += (ki > c[q]) || (ki == c[q] && i < j);
+      }
+      rank[q] = rk;
+      sorted[rk] = fx[q];
+    }
+  }
+  __syncthreads();
+  // inclusive scan of sorted[0, n): each thread owns 4 consecutive ranks
+  long long part[kPerThread];
+  long long run = 0;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = tid * kPerThread + q;
+    run += i < n ? sorted[i] : 0;
+    part[q] = run;
+  }
+  chunk_tot[tid] = run;
+  __syncthreads();
+  long long off = 0;
+  for (int t = 0; t < tid; ++t) off += chunk_tot[t];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = tid * kPerThread + q;
+    if (i < n) sorted[i] = off + part[q];
+  }
+  __syncthreads();
+  const long long limit = (long long)floor((double)sp.budget * 0x1p40);
+  bool acc[kPerThread];
+  int cnt = 0, same = 1;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int j = tid + kThreads * q;
+    acc[q] = j < n && (sorted[rank[q]] <= limit || rank[q] < sp.min_accept);
+    cnt += acc[q];
+    if (j < n) same &= o.argmax[row0 + j] == o.prev_argmax[row0 + j];
+  }
+  const long long total = block_sum_ll(sum, wred);
+  const int count = (int)block_sum_ll(cnt, wred);
+  const int all_same = -block_max_int(-same, ired) ;  // min over threads
+  __shared__ int conv_flag;
+  if (tid == 0) {
+    const int stable = (step > 0 && all_same) ? o.stable_count[r] + 1 : 0;
+    const long long thr = (long long)ceil((double)sp.tau * (double)n * 0x1p40);
+    const bool low = total < thr;
+    const bool done = step + 1 >= sp.step_limit;
+    const bool conv = sp.combine == DG_CONV_AND ? ((stable >= sp.stable_k && low) || done)
+                                                : (stable >= sp.stable_k || low || done);
+    o.stable_count[r] = stable;
+    o.converged[r] = conv;
+    o.num_accepted[r] = count;
+    o.mean_entropy[r] = (float)((double)total * 0x1p-40 / (double)n);
+    conv_flag = conv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int j = tid + kThreads * q;
+    if (j >= n) continue;
+    const int row = row0 + j;
+    const int am = o.argmax[row];
+    int tok;
+    if (acc[q]) tok = o.cand[row];
+    else if (conv_flag) tok = am;
+    else if (sp.renoise) tok = renoise_token(seed, step, j, 1, sp.vocab);
+    else tok = o.canvas[row];
+    o.canvas[row] = tok;
+    o.accept[row] = acc[q];
+    o.prev_argmax[row] = am;
+  }
+}
+
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void sampler_finalize(
-    const void* __restrict__ logits, int64_t ld, int V, int chunk, int num_chunks, const float4* __restrict__ stats,
-    ReqTable reqs, uint32_t flags, int conf_mode, float* __restrict__ entropy, float* __restrict__ conf,
-    float* __restrict__ row_max, float* __restrict__ row_sum, int* __restrict__ argmax, int* __restrict__ cand) {
+__global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restrict__ logits, int64_t ld, int V,
+                                                             int chunk, int num_chunks,
+                                                             const float4* __restrict__ stats, ReqTable reqs,
+                                                             SelectParams sp, RowOut o) {
   using VT = Vec<kBf16>;
   __shared__ float redf[kThreads / 64];
   __shared__ int redi[kThreads / 64];
   __shared__ float mass[1024];
-  __shared__ float seg[kThreads];
-  __shared__ int pick_chunk, pick_seg, fallback;
-  __shared__ float before, seg_before;
+  __shared__ int pick_chunk, fallback, is_last;
+  __shared__ float before;
   const int row = blockIdx.x, tid = threadIdx.x;
   const float4* st = stats + (int64_t)row * num_chunks;
 
+  // merge the chunk statistics in chunk order
   float mx = kNegInf;
   for (int c = tid; c < num_chunks; c += kThreads) mx = fmaxf(mx, st[c].x);
   const float m = block_max(mx, redf);
@@ -200,7 +413,17 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(
   const float Z = block_sum(z, redf);
   const float T = block_sum(t, redf);
   const int amax = block_min_int(am, redi);
-
+  if (o.probs_scale) {
+    // p = w * 2^(chunk offset) / Z: one scale per DG_PROB_BLOCK entries (a chunk spans
+    // chunk / DG_PROB_BLOCK blocks, all with the chunk's scale)
+    const int per = chunk / DG_PROB_BLOCK;
+    const int nblocks = (V + DG_PROB_BLOCK - 1) / DG_PROB_BLOCK;
+    const float invz = 1.f / Z;
+    for (int c = tid; c < num_chunks; c += kThreads) {
+      const float sc = mass[c] > 0.f ? mass[c] / st[c].y * invz : 0.f;
+      for (int b = c * per; b < min(nblocks, (c + 1) * per); ++b) o.probs_scale[(int64_t)row * nblocks + b] = sc;
+    }
+  }
   if (tid == 0) {
     // entropy in nats: ln Z - (sum p*y) * ln 2, with y the log2-scaled logit offsets
     const double h = (double)kLn2 * (log2((double)Z) - (double)T / (double)Z);
@@ -208,13 +431,13 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(
     // Z sums 2^y with y offset by the rounding of -m*log2e; fma recovers that offset
     // exactly, so the row sum is sum exp(l - m) (the entropy is offset-invariant).
     const float zsum = Z * fast_exp2(-fmaf(m, kLog2e, nm2));
-    const bool ent_in = flags & DG_ENTROPY_IN;
-    if (!ent_in) entropy[row] = H;
-    if (conf_mode == DG_CONF_NEG_ENTROPY) conf[row] = -(ent_in ? entropy[row] : H);
-    else if (!ent_in) conf[row] = 1.f / zsum;
-    row_max[row] = m;
-    row_sum[row] = zsum;
-    argmax[row] = amax;
+    const bool ent_in = sp.flags & DG_ENTROPY_IN;
+    if (!ent_in) o.entropy[row] = H;
+    if (sp.conf_mode == DG_CONF_NEG_ENTROPY) o.conf[row] = -(ent_in ? o.entropy[row] : H);
+    else if (!ent_in) o.conf[row] = 1.f / zsum;
+    o.row_max[row] = m;
+    o.row_sum[row] = zsum;
+    o.argmax[row] = amax;
   }
 
   // which request (if any) owns this row
@@ -222,9 +445,10 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(
   for (int i = 0; i < reqs.n; ++i)
     if (row >= reqs.row_start[i] && row < reqs.row_start[i] + reqs.num_rows[i]) r = i;
   if (r < 0) {
-    if (tid == 0) cand[row] = -1;
+    if (tid == 0) o.cand[row] = -1;
     return;
   }
+  // candidate: inverse CDF at u*Z; walk the chunk masses, then re-read one chunk
   const int j = row - reqs.row_start[r];
   const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)reqs.step[r], (uint64_t)j, 0);
   const float u = (float)(x0 >> 40) * 0x1p-24f;
@@ -243,152 +467,66 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(
     before = cum;
   }
   __syncthreads();
-  // re-read the chosen chunk: thread tid owns a contiguous run of chunk/256 elements
-  const int per = chunk / kThreads;
+  // thread tid owns the contiguous run [e0, e0 + per) of the chosen chunk: 8 x 16 bytes
+  constexpr int per = kLoads * VT::n;
   const int e0 = pick_chunk * chunk + tid * per;
   const char* rowp = reinterpret_cast<const char*>(logits) + (int64_t)row * ld * (kBf16 ? 2 : 4);
-  float w[64];
-  float s = 0.f;
+  float w[per];
+  float seg = 0.f;
   int last_pos = -1;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    if (i < per) {
-      const int v = e0 + i;
-      const float l = v < V ? VT::scalar(rowp, v) : kNegInf;
-      w[i] = fast_exp2(fmaf(l, kLog2e, nm2));
-      s += w[i];
-      if (w[i] > 0.f) last_pos = v;
+  for (int i = 0; i < kLoads; ++i) {
+    const uint4 v = load_vec<kBf16>(rowp, e0 + i * VT::n, V);
+#pragma unroll
+    for (int e = 0; e < VT::n; ++e) {
+      const float x = fast_exp2(fmaf(VT::get(v, e), kLog2e, nm2));
+      w[i * VT::n + e] = x;
+      seg += x;
+      if (x > 0.f) last_pos = e0 + i * VT::n + e;
     }
   }
-  seg[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    const float rem = target - before;
-    float pre = 0.f;
-    int ps = -1;
-    if (!fallback)
-      for (int i = 0; i < kThreads; ++i) {
-        if (pre + seg[i] > rem) { ps = i; break; }
-        pre += seg[i];
-      }
-    pick_seg = ps;
-    seg_before = pre;
-  }
-  __syncthreads();
-  if (pick_seg < 0) {  // rounding left u*Z past the re-read mass: last token with mass
-    const int lp = -block_min_int(-last_pos, redi);
-    if (tid == 0) cand[row] = lp;
-    return;
-  }
-  if (tid == pick_seg) {
-    const float rem = target - before;
-    float acc = 0.f;
+  const float pre = block_exclusive_scan(seg, redf);
+  const float rem = target - before;
+  const bool hit = !fallback && pre + seg > rem;
+  const int first_hit = block_min_int(hit ? tid : INT_MAX, redi);
+  if (first_hit == INT_MAX) {  // rounding left u*Z past the re-read mass: last token with mass
+    const int lp = block_max_int(last_pos, redi);
+    if (tid == 0) o.cand[row] = lp;
+  } else if (tid == first_hit) {
+    float acc = pre;
     int got = last_pos;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if (i < per) {
-        acc += w[i];
-        if (seg_before + acc > rem) { got = e0 + i; break; }
-      }
+    for (int e = 0; e < per; ++e) {
+      acc += w[e];
+      if (acc > rem) { got = e0 + e; break; }
     }
-    cand[row] = got;
+    o.cand[row] = got;
   }
+
+  // the last finished row of the request runs its selection
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(&o.counters[r], 1) == reqs.num_rows[r] - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  select_request(r, reqs, sp, o);
 }
 
-// ---- selection, canvas update, convergence -------------------------------------
-__global__ __launch_bounds__(kSelectThreads) void sampler_select(
-    ReqTable reqs, int vocab, float budget, int min_accept, int conf_mode, int renoise, int stable_k, float tau,
-    int step_limit, int combine, uint32_t flags, const float* __restrict__ entropy, const float* __restrict__ conf,
-    const int* __restrict__ argmax, const int* __restrict__ cand, uint8_t* __restrict__ accept,
-    int* __restrict__ canvas, int* __restrict__ prev_argmax, int* __restrict__ stable_count,
-    int* __restrict__ num_accepted, int* __restrict__ converged, float* __restrict__ mean_entropy) {
-  __shared__ float key[kSelectThreads];
-  __shared__ long long scan[2][kSelectThreads];
-  __shared__ long long wsum[kSelectThreads / 64];
-  __shared__ int conv_flag;
-  const int r = blockIdx.x, j = threadIdx.x;
-  const int n = reqs.num_rows[r], step = reqs.step[r];
-  const uint64_t seed = reqs.seed[r];
-  const bool active = j < n;
-  const int row = reqs.row_start[r] + j;
-
-  if (flags & DG_INIT_CANVAS) {
-    if (active) {
-      const uint64_t x = philox_word0(seed, (uint64_t)step, (uint64_t)j, 2);
-      canvas[row] = (int)(((x >> 32) * (uint64_t)vocab) >> 32);
-      prev_argmax[row] = -1;
-      accept[row] = 0;
-    }
-    if (j == 0) {
-      stable_count[r] = 0;
-      converged[r] = 0;
-      num_accepted[r] = 0;
-      mean_entropy[r] = 0.f;
-    }
-    return;
+// Start of a block: a uniform random canvas (Philox stream 2), state reset.
+__global__ __launch_bounds__(kThreads) void sampler_init(ReqTable reqs, int vocab, RowOut o) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int n = reqs.num_rows[r], row0 = reqs.row_start[r];
+  for (int j = tid; j < n; j += kThreads) {
+    o.canvas[row0 + j] = renoise_token(reqs.seed[r], reqs.step[r], j, 2, vocab);
+    o.prev_argmax[row0 + j] = -1;
+    o.accept[row0 + j] = 0;
   }
-
-  const float h = active ? entropy[row] : 0.f;
-  const float c = active ? (conf_mode == DG_CONF_NEG_ENTROPY ? -h : conf[row]) : kNegInf;
-  key[j] = c;
-  __syncthreads();
-  int rank = 0;
-  if (active)
-    for (int i = 0; i < n; ++i) {
-      const float ki = key[i];
-      rank += (ki > c) || (ki == c && i < j);
-    }
-  // exact fixed point: floor(h * 2^40); h * 2^40 is exact in double
-  const long long fx = active ? (long long)floor((double)h * 0x1p40) : 0;
-  scan[0][j] = 0;
-  __syncthreads();
-  if (active) scan[0][rank] = fx;
-  __syncthreads();
-  int cur = 0;
-  for (int off = 1; off < n; off <<= 1) {
-    const long long v = scan[cur][j] + (j >= off ? scan[cur][j - off] : 0);
-    scan[cur ^ 1][j] = v;
-    cur ^= 1;
-    __syncthreads();
-  }
-  const long long limit = (long long)floor((double)budget * 0x1p40);
-  const bool acc = active && (scan[cur][rank] <= limit || rank < min_accept);
-  const int count = __syncthreads_count(acc);
-  const int same = __syncthreads_and(!active || argmax[row] == prev_argmax[row]);
-  // exact total entropy of the request
-  long long tot = fx;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
-  if ((j & 63) == 0) wsum[j >> 6] = tot;
-  __syncthreads();
-  if (j == 0) {
-    long long total = 0;
-    for (int i = 0; i < kSelectThreads / 64; ++i) total += wsum[i];
-    const int stable = (step > 0 && same) ? stable_count[r] + 1 : 0;
-    const long long thr = (long long)ceil((double)tau * (double)n * 0x1p40);
-    const bool low = total < thr;
-    const bool done = step + 1 >= step_limit;
-    const bool conv = combine == DG_CONV_AND ? ((stable >= stable_k && low) || done)
-                                             : (stable >= stable_k || low || done);
-    stable_count[r] = stable;
-    converged[r] = conv;
-    num_accepted[r] = count;
-    mean_entropy[r] = (float)((double)total * 0x1p-40 / (double)n);
-    conv_flag = conv;
-  }
-  __syncthreads();
-  if (active) {
-    const int am = argmax[row];
-    int tok;
-    if (acc) tok = cand[row];
-    else if (conv_flag) tok = am;
-    else if (renoise) {
-      const uint64_t x = philox_word0(seed, (uint64_t)step, (uint64_t)j, 1);
-      tok = (int)(((x >> 32) * (uint64_t)vocab) >> 32);
-    } else tok = canvas[row];
-    canvas[row] = tok;
-    accept[row] = acc;
-    prev_argmax[row] = am;
+  if (tid == 0) {
+    o.stable_count[r] = 0;
+    o.converged[r] = 0;
+    o.num_accepted[r] = 0;
+    o.mean_entropy[r] = 0.f;
   }
 }
 
@@ -404,27 +542,40 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
     t.step[i] = a->reqs[i].step;
     t.seed[i] = a->reqs[i].seed;
   }
-  if (!(a->flags & DG_INIT_CANVAS)) {
-    float4* stats = reinterpret_cast<float4*>(a->workspace);
-    const dim3 grid(plan.num_chunks * a->num_rows);
-    if (a->dtype == DG_BF16) {
-      hipLaunchKernelGGL(sampler_rowpass<true>, grid, dim3(kThreads), 0, s, a->logits, a->ld, a->vocab, plan.chunk,
-                         plan.num_chunks, stats);
-      hipLaunchKernelGGL(sampler_finalize<true>, dim3(a->num_rows), dim3(kThreads), 0, s, a->logits, a->ld, a->vocab,
-                         plan.chunk, plan.num_chunks, stats, t, a->flags, a->conf_mode, a->entropy, a->conf,
-                         a->row_max, a->row_sum, a->argmax, a->cand);
-    } else {
-      hipLaunchKernelGGL(sampler_rowpass<false>, grid, dim3(kThreads), 0, s, a->logits, a->ld, a->vocab, plan.chunk,
-                         plan.num_chunks, stats);
-      hipLaunchKernelGGL(sampler_finalize<false>, dim3(a->num_rows), dim3(kThreads), 0, s, a->logits, a->ld, a->vocab,
-                         plan.chunk, plan.num_chunks, stats, t, a->flags, a->conf_mode, a->entropy, a->conf,
-                         a->row_max, a->row_sum, a->argmax, a->cand);
-    }
+  float4* stats = reinterpret_cast<float4*>(a->workspace);
+  RowOut o{a->entropy, a->conf, a->row_max, a->row_sum, a->argmax, a->cand, a->probs_scale, a->accept, a->canvas,
+           a->prev_argmax, a->stable_count, a->num_accepted, a->converged, a->mean_entropy,
+           reinterpret_cast<int*>(reinterpret_cast<char*>(a->workspace) + plan.counter_offset)};
+  if (a->flags & DG_INIT_CANVAS) {
+    hipLaunchKernelGGL(sampler_init, dim3(a->num_reqs), dim3(kThreads), 0, s, t, a->vocab, o);
+    return (int)hipGetLastError();
   }
-  hipLaunchKernelGGL(sampler_select, dim3(a->num_reqs), dim3(kSelectThreads), 0, s, t, a->vocab, a->budget,
-                     a->min_accept, a->conf_mode, a->renoise, a->stable_k, a->tau, a->step_limit, a->combine, a->flags,
-                     a->entropy, a->conf, a->argmax, a->cand, a->accept, a->canvas, a->prev_argmax, a->stable_count,
-                     a->num_accepted, a->converged, a->mean_entropy);
+  SelectParams sp{a->vocab, a->min_accept, a->conf_mode, a->renoise, a->stable_k, a->step_limit, a->combine,
+                  a->budget, a->tau, a->flags};
+  const int nfull = a->vocab / plan.chunk;
+  const bool tail = nfull < plan.num_chunks;
+  const dim3 gfull((unsigned)nfull * a->num_rows), gtail(a->num_rows), blk(kThreads);
+#define DG_ROWPASS(BF, ST)                                                                                     \
+  do {                                                                                                         \
+    if (nfull)                                                                                                 \
+      hipLaunchKernelGGL((sampler_rowpass<BF, ST, false>), gfull, blk, 0, s, a->logits, a->ld, a->vocab,      \
+                         plan.chunk, plan.num_chunks, nfull, stats, a->probs, a->ldq, o.counters, a->num_reqs); \
+    if (tail)                                                                                                  \
+      hipLaunchKernelGGL((sampler_rowpass<BF, ST, true>), gtail, blk, 0, s, a->logits, a->ld, a->vocab,       \
+                         plan.chunk, plan.num_chunks, nfull, stats, a->probs, a->ldq, o.counters, a->num_reqs); \
+  } while (0)
+  if (a->dtype == DG_BF16) {
+    if (a->probs) DG_ROWPASS(true, true);
+    else DG_ROWPASS(true, false);
+    hipLaunchKernelGGL(sampler_finalize<true>, dim3(a->num_rows), blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk,
+                       plan.num_chunks, stats, t, sp, o);
+  } else {
+    if (a->probs) DG_ROWPASS(false, true);
+    else DG_ROWPASS(false, false);
+    hipLaunchKernelGGL(sampler_finalize<false>, dim3(a->num_rows), blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk,
+                       plan.num_chunks, stats, t, sp, o);
+  }
+#undef DG_ROWPASS
   return (int)hipGetLastError();
 }
 

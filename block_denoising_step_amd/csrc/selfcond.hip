@@ -3,26 +3,37 @@
 // 첫 번째 Diffusion LLM", section "안정성을 위한 셀프 컨디셔닝"; [P3] "DiffusionGemma u vLLM:
 // ...", section "Mehanizam odlučivanja o gotovim tokenima").
 //
-//   selfcond_gemm    128 x 128 output tile per work group (4 waves, 64 x 64 each, 2 x 2
-//                    MFMA 32x32 blocks), K step of 128 bytes per row (64 bf16 / 32 fp32).
-//                    The A tile (P, or logits turned into P on load from the sampler's
-//                    row max and row sum) is staged row-major in LDS; the E tile is
-//                    transposed on its way into LDS so both MFMA operands are single
-//                    16-byte LDS reads. Global loads for step k+1 are in flight while
-//                    step k runs on the matrix cores (double-buffered LDS, one barrier
-//                    per step). Split-K over V; work groups that share an A slice and
-//                    a B slice are placed on the same XCD so the re-reads hit its L2.
-//   selfcond_reduce  sums the split-K partials in slice order (deterministic) and
-//                    rounds to the output dtype.
+// Both GEMM kernels compute a 256 x 256 output tile per work group with 4 waves,
+// each 128 x 128 as 4 x 4 MFMA 32x32 blocks (256 accumulator registers per lane),
+// split-K over V with the work groups that share a K slice placed on one XCD so
+// their re-reads of it hit that XCD's L2. LDS rows are XOR-swizzled in 16-byte
+// chunks so staging writes and operand reads are free of bank conflicts.
+//
+//   selfcond_gemm_dma  bf16, V a multiple of 32: the P and E tiles go straight from
+//                      HBM to LDS (global_load_lds_dwordx4) through a 4-stage ring,
+//                      so three K steps are in flight with no register staging. E
+//                      stays row-major in LDS; its MFMA operand (8 consecutive k of one
+//                      column per lane) comes from two ds_read_b64_tr_b16 transposing
+//                      reads. One fence-free barrier per K step.
+//   selfcond_gemm_reg  general case (fp32, any V): tiles staged through registers
+//                      one K step ahead, E transposed in registers on its way to LDS;
+//                      in the logits mode P is rebuilt at LDS-store time.
+//   selfcond_normalize bf16 logits + row statistics -> probabilities, so the logits
+//                      mode can use the DMA kernel (the rebuild would otherwise be
+//                      repeated once per 256-column tile).
+//   selfcond_reduce    sums the split-K partials in slice order (deterministic) and
+//                      rounds to the output dtype.
+// With block-scaled P (w and per-row scales per DG_PROB_BLOCK vocabulary entries),
+// every split lies inside one scale block and its rows are scaled in the epilogue.
 #include "dg_common.cuh"
 #include "dg_internal.h"
 
 namespace dg {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kThreads = 256;
-constexpr int kRowBytes = 128;             // bytes of one A row (or one E column) per K step
-constexpr int kPitch = kRowBytes + 16;     // LDS row pitch: 16-byte pad keeps ds_read_b128 conflict-free
+constexpr int kBM = 256, kBN = 256, kThreads = 256;
+constexpr int kRow = 128;   // bytes per LDS row (one A row or one E column per K step)
+constexpr int kStages = 1;  // K steps of global loads in flight in registers
 
 template <bool kBf16> struct Tr;
 template <> struct Tr<true> {
@@ -32,34 +43,9 @@ template <> struct Tr<false> {
   static constexpr int esz = 4, epv = 4, bk = 32;
 };
 
-// One 32x32x16 MFMA step from 16 bytes (bf16) or 32 bytes (fp32) of A and B per lane.
-// Lane half h = lane/32 supplies k = 8h..8h+7 of the step for both operands.
-template <bool kBf16> struct Mfma;
-template <> struct Mfma<true> {
-  struct Frag { uint4 v; };
-  __device__ static Frag load(const char* p) { return Frag{*reinterpret_cast<const uint4*>(p)}; }
-  __device__ static void step(f32x16_t& acc, const Frag& a, const Frag& b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
-                                                  acc, 0, 0, 0);
-  }
-};
-template <> struct Mfma<false> {
-  struct Frag { float4 lo, hi; };
-  __device__ static Frag load(const char* p) {
-    return Frag{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 16)};
-  }
-  __device__ static void step(f32x16_t& acc, const Frag& a, const Frag& b) {
-    // k-element j of each half goes through one 32x32x2 MFMA: the pair {j, 8+j}
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
-  }
-};
+// swizzled 16-byte chunk position inside a 128-byte LDS row
+__device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz_b(int n, int chunk) { return chunk ^ ((n & 7) ^ ((n >> 3) & 7)); }
 
 struct GemmArgs {
   const void* p;
@@ -71,12 +57,13 @@ struct GemmArgs {
   void* out;
   int64_t ldo;
   float* part;  // [splits][M][d] fp32, or null when splits == 1
+  const float* p_scale;  // [M][nblocks] block scales, or null
+  int nblocks;
   int M, V, d;
   int m_tiles, n_tiles, splits, k_per_split;
 };
 
-// Turn 16 bytes of logits into probabilities p = 2^(l*log2e + c) with
-// c = -row_max*log2e - log2(row_sum).
+// Logits -> probabilities p = 2^(l*log2e + c), c = -row_max*log2e - log2(row_sum).
 template <bool kBf16> __device__ __forceinline__ uint4 to_prob(uint4 v, float c);
 template <> __device__ __forceinline__ uint4 to_prob<true>(uint4 v, float c) {
   uint4 r;
@@ -96,175 +83,495 @@ template <> __device__ __forceinline__ uint4 to_prob<false>(uint4 v, float c) {
   return r;
 }
 
-template <bool kBf16, bool kFused>
-__global__ __launch_bounds__(kThreads) void selfcond_gemm(GemmArgs g) {
-  using T = Tr<kBf16>;
-  using MF = Mfma<kBf16>;
-  constexpr int BK = T::bk, ESZ = T::esz, EPV = T::epv;
-  __shared__ __attribute__((aligned(16))) char lds_a[2][kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) char lds_b[2][kBN * kPitch];
+// Epilogue shared by both kernels: acc[i][j][e] = C[wm + 32i + 8(e/4) + 4h + e%4][wn + 32j + l32].
+// Split-K partials keep the MFMA register layout: per 256 x 256 tile, float4 q =
+// [wave][i][j][e/4][lane] holds acc[i][j][e/4*4 .. +3], so every store is a coalesced
+// 1 KB wave write; selfcond_reduce maps them back to rows and columns.
+__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[4][4], int split, int k_lo, int mt,
+                                           int nt, int wave, int lane, bool bf16) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const int m0 = mt * kBM, n0 = nt * kBN, wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int blk = k_lo / DG_PROB_BLOCK;
+  auto scale = [&](int r) { return g.p_scale ? g.p_scale[(int64_t)min(r, g.M - 1) * g.nblocks + blk] : 1.f; };
+  if (g.part) {
+    float4* tile = reinterpret_cast<float4*>(g.part) +
+                   (((int64_t)split * g.m_tiles + mt) * g.n_tiles + nt) * (kBM * kBN / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r = m0 + wm + 32 * i + 8 * e4 + 4 * h;  // rows r .. r+3
+        const float s0 = scale(r), s1 = scale(r + 1), s2 = scale(r + 2), s3 = scale(r + 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tile[(((wave * 4 + i) * 4 + j) * 4 + e4) * 64 + lane] =
+              make_float4(acc[i][j][4 * e4] * s0, acc[i][j][4 * e4 + 1] * s1, acc[i][j][4 * e4 + 2] * s2,
+                          acc[i][j][4 * e4 + 3] * s3);
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (r >= g.M) continue;
+      const float sr = scale(r);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = n0 + wn + 32 * j + l32;
+        if (c >= g.d) continue;
+        const float v = acc[i][j][e] * sr;
+        if (bf16) reinterpret_cast<__bf16*>(g.out)[(int64_t)r * g.ldo + c] = (__bf16)v;
+        else reinterpret_cast<float*>(g.out)[(int64_t)r * g.ldo + c] = v;
+      }
+    }
+}
 
-  // XCD-aware placement: consecutive work-group ids go round-robin over 8 XCDs; give
-  // each XCD a contiguous block of (slice, m tile, n tile) work so the work groups
-  // sharing a K slice run on one XCD.
+// Work placement shared by both kernels (XCD-aware, see the file comment).
+struct TileIdx {
+  int split, mt, nt, m0, n0, k_lo, k_hi;
+};
+__device__ __forceinline__ TileIdx tile_index(const GemmArgs& g) {
   const int nwg = gridDim.x;
   int L = blockIdx.x;
   if ((nwg & 7) == 0) L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   const int per_split = g.m_tiles * g.n_tiles;
-  const int split = L / per_split;
-  const int mt = (L % per_split) / g.n_tiles;
-  const int nt = L % g.n_tiles;
-  const int m0 = mt * kBM, n0 = nt * kBN;
-  const int k_lo = split * g.k_per_split;
-  const int k_hi = min(g.V, k_lo + g.k_per_split);
+  TileIdx t;
+  t.split = L / per_split;
+  t.mt = (L % per_split) / g.n_tiles;
+  t.nt = L % g.n_tiles;
+  t.m0 = t.mt * kBM;
+  t.n0 = t.nt * kBN;
+  t.k_lo = t.split * g.k_per_split;
+  t.k_hi = min(g.V, t.k_lo + g.k_per_split);
+  return t;
+}
+
+template <bool kBf16, bool kFused>
+__global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
+  using T = Tr<kBf16>;
+  constexpr int BK = T::bk, ESZ = T::esz, EPV = T::epv;
+  __shared__ __attribute__((aligned(16))) char lds_a[2][kBM * kRow];
+  __shared__ __attribute__((aligned(16))) char lds_b[2][kBN * kRow];
+
+  const TileIdx ti = tile_index(g);
+  const int m0 = ti.m0, n0 = ti.n0, k_lo = ti.k_lo, k_hi = ti.k_hi;
   const int nsteps = (k_hi - k_lo + BK - 1) / BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
 
-  // A loads: chunk q = i*256 + tid -> row q/8, 16-byte column q%8
+  // A staging: chunk q = i*256 + tid (i < 8) -> row q >> 3, 16-byte chunk q & 7
   const char* pbase = reinterpret_cast<const char*>(g.p);
-  float crow[4];
+  float crow[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = m0 + (i * kThreads + tid) / 8;
+  for (int i = 0; i < 8; ++i) {
+    const int r = m0 + ((i * kThreads + tid) >> 3);
     crow[i] = 0.f;
     if (kFused && r < g.M) crow[i] = -g.row_max[r] * kLog2e - __builtin_amdgcn_logf(g.row_sum[r]);
   }
-  // B loads: thread -> n group nq (EPV columns), k group kq (4 rows)
-  constexpr int NG = kBN / EPV;
-  const int nq = tid % NG, kq = tid / NG;
+  // B staging (E transposed): bf16 - one block of 8 k rows x 8 columns per thread;
+  // fp32 - two blocks of 4 k rows x 4 columns.
   const char* ebase = reinterpret_cast<const char*>(g.e);
+  const uint32_t neutral = kFused ? (kBf16 ? 0xFF80FF80u : 0xFF800000u) : 0u;  // p = 0 past the end
 
-  // Raw A values; out-of-range entries hold a neutral value (0, or -inf in the fused
-  // mode so that 2^(-inf) = 0). The fused transform runs at LDS-store time, after the
-  // current step's MFMAs, so the loads of the next step stay in flight meanwhile.
-  const uint32_t neutral = kFused ? (kBf16 ? 0xFF80FF80u : 0xFF800000u) : 0u;
-  uint4 ra[4], rb[4];
-  auto load_step = [&](int s) {
+  uint4 ra[kStages][8], rb[kStages][8];
+
+  auto load_step = [&](int s, uint4 (&a)[8], uint4 (&b)[8]) {
     const int k0 = k_lo + s * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int q = i * kThreads + tid;
-      const int r = m0 + q / 8, kc = k0 + (q % 8) * EPV;
+      const int r = m0 + (q >> 3), kc = k0 + (q & 7) * EPV;
       if (r < g.M && kc + EPV <= k_hi) {
-        ra[i] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)r * g.ldp + kc) * ESZ);
+        a[i] = *reinterpret_cast<const uint4*>(pbase + ((int64_t)r * g.ldp + kc) * ESZ);
       } else {
-        ra[i] = make_uint4(neutral, neutral, neutral, neutral);
+        a[i] = make_uint4(neutral, neutral, neutral, neutral);
         if (r < g.M)
           for (int e = 0; e < EPV; ++e)
             if (kc + e < k_hi) {
               if (kBf16)
-                reinterpret_cast<uint16_t*>(&ra[i])[e] = reinterpret_cast<const uint16_t*>(pbase)[(int64_t)r * g.ldp + kc + e];
+                reinterpret_cast<uint16_t*>(&a[i])[e] =
+                    reinterpret_cast<const uint16_t*>(pbase)[(int64_t)r * g.ldp + kc + e];
               else
-                reinterpret_cast<float*>(&ra[i])[e] = reinterpret_cast<const float*>(pbase)[(int64_t)r * g.ldp + kc + e];
+                reinterpret_cast<float*>(&a[i])[e] = reinterpret_cast<const float*>(pbase)[(int64_t)r * g.ldp + kc + e];
             }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + kq * 4 + j;
-      rb[j] = k < k_hi ? *reinterpret_cast<const uint4*>(ebase + ((int64_t)k * g.lde + n0 + nq * EPV) * ESZ)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = i * kThreads + tid;
-      const uint4 v = kFused ? to_prob<kBf16>(ra[i], crow[i]) : ra[i];
-      *reinterpret_cast<uint4*>(&lds_a[buf][(q / 8) * kPitch + (q % 8) * 16]) = v;
-    }
-    // transpose 4 (k) x EPV (n) into EPV rows of Bt[n][k]
     if (kBf16) {
+      const int nb = tid & 31, kb = tid >> 5;  // 32 column blocks x 8 k blocks
+      const int col = n0 + nb * 8;
 #pragma unroll
-      for (int c = 0; c < EPV; ++c) {
-        const int w = c >> 1;
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each word
-        const uint32_t k01 = __builtin_amdgcn_perm((&rb[1].x)[w], (&rb[0].x)[w], sel);
-        const uint32_t k23 = __builtin_amdgcn_perm((&rb[3].x)[w], (&rb[2].x)[w], sel);
-        *reinterpret_cast<uint2*>(&lds_b[buf][(nq * EPV + c) * kPitch + kq * 4 * ESZ]) = make_uint2(k01, k23);
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + kb * 8 + j;
+        b[j] = (k < k_hi && col < g.d) ? *reinterpret_cast<const uint4*>(ebase + ((int64_t)k * g.lde + col) * 2)
+                                       : make_uint4(0, 0, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < EPV; ++c)
-        *reinterpret_cast<uint4*>(&lds_b[buf][(nq * EPV + c) * kPitch + kq * 4 * ESZ]) =
-            make_uint4((&rb[0].x)[c], (&rb[1].x)[c], (&rb[2].x)[c], (&rb[3].x)[c]);
+      for (int blk = 0; blk < 2; ++blk) {
+        const int id = blk * kThreads + tid;
+        const int nb = id & 63, kb = id >> 6;  // 64 column blocks x 8 k blocks
+        const int col = n0 + nb * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = k0 + kb * 4 + j;
+          b[blk * 4 + j] = (k < k_hi && col < g.d)
+                               ? *reinterpret_cast<const uint4*>(ebase + ((int64_t)k * g.lde + col) * 4)
+                               : make_uint4(0, 0, 0, 0);
+        }
+      }
     }
   };
 
-  f32x16_t acc[2][2];
+  auto store_step = [&](int buf, const uint4 (&a)[8], const uint4 (&b)[8]) {
+    char* A = lds_a[buf];
+    char* B = lds_b[buf];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int q = i * kThreads + tid;
+      const int row = q >> 3;
+      const uint4 v = kFused ? to_prob<kBf16>(a[i], crow[i]) : a[i];
+      *reinterpret_cast<uint4*>(A + row * kRow + swz_a(row, q & 7) * 16) = v;
+    }
+    if (kBf16) {
+      const int nb = tid & 31, kb = tid >> 5;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int c = 0; c < 8; ++c) {  // column nb*8 + c gets k = kb*8 .. kb*8+7
+        const int w = c >> 1;
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint4 o;
+        o.x = __builtin_amdgcn_perm((&b[1].x)[w], (&b[0].x)[w], sel);
+        o.y = __builtin_amdgcn_perm((&b[3].x)[w], (&b[2].x)[w], sel);
+        o.z = __builtin_amdgcn_perm((&b[5].x)[w], (&b[4].x)[w], sel);
+        o.w = __builtin_amdgcn_perm((&b[7].x)[w], (&b[6].x)[w], sel);
+        const int n = nb * 8 + c;
+        *reinterpret_cast<uint4*>(B + n * kRow + swz_b(n, kb) * 16) = o;
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int id = blk * kThreads + tid;
+        const int nb = id & 63, kb = id >> 6;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = nb * 4 + c;
+          const uint4 o = make_uint4((&b[blk * 4 + 0].x)[c], (&b[blk * 4 + 1].x)[c], (&b[blk * 4 + 2].x)[c],
+                                     (&b[blk * 4 + 3].x)[c]);
+          *reinterpret_cast<uint4*>(B + n * kRow + swz_b(n, kb) * 16) = o;
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int h = lane >> 5, l32 = lane & 31;
-  if (nsteps > 0) load_step(0);
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    store_step(buf);
-    __syncthreads();
-    if (s + 1 < nsteps) load_step(s + 1);
+  auto compute_step = [&](int buf) {
     const char* A = lds_a[buf];
     const char* B = lds_b[buf];
+    if (kBf16) {
 #pragma unroll
-    for (int ks = 0; ks < kRowBytes / (16 * ESZ); ++ks) {
-      const int koff = (ks * 16 + 8 * h) * ESZ;
-      typename MF::Frag fa[2], fb[2];
+      for (int ks = 0; ks < 4; ++ks) {  // 16 k per MFMA, lane half h holds chunk 2ks + h
+        const int kc = 2 * ks + h;
+        uint4 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = MF::load(A + (wm + i * 32 + l32) * kPitch + koff);
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm + 32 * i + l32;
+          fa[i] = *reinterpret_cast<const uint4*>(A + row * kRow + swz_a(row, kc) * 16);
+        }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = MF::load(B + (wn + j * 32 + l32) * kPitch + koff);
+        for (int j = 0; j < 4; ++j) {
+          const int n = wn + 32 * j + l32;
+          fb[j] = *reinterpret_cast<const uint4*>(B + n * kRow + swz_b(n, kc) * 16);
+        }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) MF::step(acc[i][j], fa[i], fb[j]);
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                                __builtin_bit_cast(bf16x8_t, fb[j]), acc[i][j], 0, 0,
+                                                                0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {  // 16 k per step: lane half h holds chunks 4ks+2h, 4ks+2h+1
+        float4 fa[4][2], fb[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm + 32 * i + l32;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            fa[i][c] = *reinterpret_cast<const float4*>(A + row * kRow + swz_a(row, 4 * ks + 2 * h + c) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = wn + 32 * j + l32;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            fb[j][c] = *reinterpret_cast<const float4*>(B + n * kRow + swz_b(n, 4 * ks + 2 * h + c) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][c].x, fb[j][c].x, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][c].y, fb[j][c].y, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][c].z, fb[j][c].z, acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][c].w, fb[j][c].w, acc[i][j], 0, 0, 0);
+            }
+      }
+    }
+  };
+
+  // prologue: the first kStages steps in flight
+#pragma unroll
+  for (int j = 0; j < kStages; ++j)
+    if (j < nsteps) load_step(j, ra[j], rb[j]);
+  // main loop, unrolled by kStages so every register buffer index is static
+  for (int s0 = 0; s0 < nsteps; s0 += kStages) {
+#pragma unroll
+    for (int j = 0; j < kStages; ++j) {
+      const int s = s0 + j;
+      if (s < nsteps) {
+        store_step(s & 1, ra[j], rb[j]);
+        __syncthreads();
+        if (s + kStages < nsteps) load_step(s + kStages, ra[j], rb[j]);
+        compute_step(s & 1);
+      }
     }
   }
 
-  // epilogue: acc[i][j][e] holds C[wm + 32i + 8(e/4) + 4h + e%4][wn + 32j + l32]
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int c = n0 + wn + 32 * j + l32;
-        if (r >= g.M) continue;
-        const float v = acc[i][j][e];
-        if (g.part) {
-          g.part[((int64_t)split * g.M + r) * g.d + c] = v;
-        } else if (kBf16) {
-          reinterpret_cast<__bf16*>(g.out)[(int64_t)r * g.ldo + c] = (__bf16)v;
-        } else {
-          reinterpret_cast<float*>(g.out)[(int64_t)r * g.ldo + c] = v;
-        }
-      }
+  store_tile(g, acc, ti.split, k_lo, ti.mt, ti.nt, wave, lane, kBf16);
 }
 
-// Sum split-K partials in slice order and store in the output dtype; 4 columns per thread.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void selfcond_reduce(const float* __restrict__ part, int splits, int M, int d,
-                                                       void* __restrict__ out, int64_t ldo) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)M * d / 4;
-  if (i >= total) return;
-  const int64_t e = i * 4;
-  const int r = (int)(e / d), c = (int)(e % d);
-  float4 s = *reinterpret_cast<const float4*>(part + e);
-  for (int k = 1; k < splits; ++k) {
-    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)k * M * d + e);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+
+// ---- LDS-DMA kernel (bf16) -------------------------------------------------------
+
+constexpr int kDmaStages = 5;            // LDS ring depth: 4 K steps in flight (160 KB)
+constexpr int kDmaBK = 32;               // k per step
+constexpr int kStageA = kBM * 64;        // 256 rows x 32 bf16
+constexpr int kStageB = kDmaBK * 512;    // 32 k rows x 256 bf16
+constexpr int kStageBytes = kStageA + kStageB;
+
+// s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt left open).
+#define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// s_waitcnt for all LDS reads of this wave (vmcnt left open).
+#define DG_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
+
+// LDS operand reads as inline asm: the compiler's wait insertion would otherwise put a
+// vmcnt(0) before every LDS read that follows an LDS DMA, serialising the ring. Each
+// use of the results is preceded by an explicit DG_WAIT_LGKM0.
+__device__ __forceinline__ uint4 lds_read_b128(uint32_t addr) {
+  uint4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint2 lds_read_tr16(uint32_t addr) {
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// A stage: row r (0..255) holds 32 bf16 = 4 chunks; chunk c sits at c ^ swa(r).
+// B stage: k row kk (0..31) holds 256 bf16 = 32 chunks; chunk c sits at c ^ swb(kk).
+// The XOR masks keep the operand reads (ds_read_b128 over 32 rows; ds_read_b64_tr_b16
+// over 4 k rows x 32 columns) free of bank conflicts with 64 banks of 4 bytes and with
+// 32; the DMA writes are contiguous 1 KB runs either way.
+__device__ __forceinline__ int swa(int r) { return ((r >> 1) & 3) ^ (((r >> 3) & 1) * 3); }
+__device__ __forceinline__ int swb(int kk) { return ((kk & 1) * 4) ^ (((kk >> 1) & 1) * 10); }
+__device__ __forceinline__ uint32_t a_off(int r, int c) { return r * 64 + ((c ^ swa(r)) << 4); }
+__device__ __forceinline__ uint32_t b_off(int kk, int c) { return kStageA + kk * 512 + ((c ^ swb(kk)) << 4); }
+
+__global__ __launch_bounds__(kThreads) void selfcond_gemm_dma(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char lds[kDmaStages][kStageBytes];
+  const TileIdx ti = tile_index(g);
+  const int nsteps = (ti.k_hi - ti.k_lo) / kDmaBK;  // K range is a multiple of 32
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+
+  // Per-lane DMA sources. Each wave fills segments 4*wave .. 4*wave+3 of both the A
+  // and the B region (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the
+  // lane fetches the chunk that the swizzle puts in its slot. Rows past M and columns
+  // past d are clamped to valid memory; their results are never stored.
+  const char* psrc[4];
+  const char* esrc[4];
+  const char* pb = reinterpret_cast<const char*>(g.p);
+  const char* eb = reinterpret_cast<const char*>(g.e);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int seg = 4 * wave + t;
+    const int r = seg * 16 + (lane >> 2);         // A row within the tile
+    const int ca = (lane & 3) ^ swa(r);           // logical chunk stored in this slot
+    const int grow = min(ti.m0 + r, g.M - 1);
+    psrc[t] = pb + ((int64_t)grow * g.ldp + ti.k_lo + ca * 8) * 2;
+    const int kk = seg * 2 + (lane >> 5);         // B k row within the step
+    const int cb = (lane & 31) ^ swb(kk);
+    const int gcol = min(ti.n0 + cb * 8, g.d - 8);
+    esrc[t] = eb + ((int64_t)(ti.k_lo + kk) * g.lde + gcol) * 2;
   }
-  if (kBf16) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (int64_t)r * ldo + c) =
-        make_uint2(pack_bf16(s.x, s.y), pack_bf16(s.z, s.w));
-  } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)r * ldo + c) = s;
+  const int64_t pstep = kDmaBK * 2;                 // bytes per K step along a P row
+  const int64_t estep = (int64_t)kDmaBK * g.lde * 2;  // bytes per K step down E
+  __attribute__((address_space(3))) char* lds0 = (__attribute__((address_space(3))) char*)lds[0];
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
+
+  auto issue = [&](int s) {
+    __attribute__((address_space(3))) char* st = lds0 + (s % kDmaStages) * kStageBytes;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(psrc[t] + s * pstep),
+                                       (__attribute__((address_space(3))) void*)(st + (4 * wave + t) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(esrc[t] + s * estep),
+                                       (__attribute__((address_space(3))) void*)(st + kStageA + (4 * wave + t) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // B operand addresses (tr16): lane group grp = lane/16 covers k rows 8*(grp/2) + 4q
+  // + (lane%16)/4 and columns 16*(grp%2) + 4*(lane%4) of each 32-column block.
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int brow = 8 * (grp >> 1) + (s16 >> 2);
+  const int bcol = 16 * (grp & 1) + 4 * (s16 & 3);  // + wn + 32j
+
+  // One half step = 16 k: A fragments of 4 row blocks, B fragments of 4 column blocks
+  // (two transposing reads of 4 k rows each). The 12 LDS reads of the next half step
+  // are interleaved with the 16 MFMAs of the current one, one read after each MFMA
+  // (sched_barrier pins the order), so every read issues while an MFMA executes.
+  auto a_addr = [&](uint32_t st, int ks, int i) { return st + a_off(wm + 32 * i + l32, 2 * ks + h); };
+  auto b_addr = [&](uint32_t st, int ks, int j, int q) {
+    const int col = wn + 32 * j + bcol;
+    return st + b_off(16 * ks + brow + 4 * q, col >> 3) + ((col & 7) << 1);
+  };
+  uint4 fa[2][4], fb[2][4];
+  auto read_half = [&](uint32_t st, int ks, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[buf][i] = lds_read_b128(a_addr(st, ks, i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 lo = lds_read_tr16(b_addr(st, ks, j, 0)), hi = lds_read_tr16(b_addr(st, ks, j, 1));
+      fb[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  // MFMAs on fragment buffer `buf`; if `next_st` != ~0u, the reads of (next_st, next_ks)
+  // into the other buffer are interleaved (B reads first, since they are two each).
+  auto mma_half = [&](int buf, uint32_t next_st, int next_ks) {
+    const int nb = buf ^ 1;
+    uint2 lo[4], hi[4];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[buf][i]),
+                                                          __builtin_bit_cast(bf16x8_t, fb[buf][j]), acc[i][j], 0, 0, 0);
+      if (next_st != ~0u) {
+        if (t < 8) {
+          if (t & 1) hi[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 1));
+          else lo[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 0));
+        } else if (t < 12) {
+          fa[nb][t - 8] = lds_read_b128(a_addr(next_st, next_ks, t - 8));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (next_st != ~0u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[nb][j] = make_uint4(lo[j].x, lo[j].y, hi[j].x, hi[j].y);
+    }
+  };
+
+  // Pipeline: the barrier that publishes step s+1 sits between the two halves of step
+  // s; a barrier also certifies that every wave is done reading the step two behind,
+  // whose ring slot the next DMA then refills.
+#pragma unroll
+  for (int t = 0; t < kDmaStages - 1; ++t)
+    if (t < nsteps) issue(t);
+  if (nsteps > 0) {
+    if (kDmaStages - 2 < nsteps) DG_WAIT_VM(8 * (kDmaStages - 2));
+    else DG_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    read_half(lbase, 0, 0);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const uint32_t st = lbase + (s % kDmaStages) * kStageBytes;
+    DG_WAIT_LGKM0();       // fragments of (s, 0) in buffer 0
+    mma_half(0, st, 1);    // ... with the reads of (s, 1) into buffer 1
+    if (s + 1 < nsteps) {
+      // step s+1 has landed once at most the DMA groups issued after it remain
+      if (s + kDmaStages - 2 < nsteps) DG_WAIT_VM(8 * (kDmaStages - 3));
+      else DG_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      if (s + kDmaStages - 1 < nsteps) issue(s + kDmaStages - 1);
+    }
+    DG_WAIT_LGKM0();       // fragments of (s, 1) in buffer 1
+    mma_half(1, s + 1 < nsteps ? lbase + ((s + 1) % kDmaStages) * kStageBytes : ~0u, 0);
+  }
+  store_tile(g, acc, ti.split, ti.k_lo, ti.mt, ti.nt, wave, lane, true);
+}
+
+// bf16 logits + row statistics -> probabilities p = 2^(l*log2e + c); 8 per thread.
+__global__ __launch_bounds__(256) void selfcond_normalize(const uint16_t* __restrict__ l, int64_t ldl,
+                                                          const float* __restrict__ row_max,
+                                                          const float* __restrict__ row_sum, int M, int V,
+                                                          uint16_t* __restrict__ p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = V / 8;
+  if (i >= (int64_t)M * per_row) return;
+  const int r = (int)(i / per_row);
+  const int64_t c = (i % per_row) * 8;
+  const float cr = -row_max[r] * kLog2e - __builtin_amdgcn_logf(row_sum[r]);
+  const uint4 v = *reinterpret_cast<const uint4*>(l + (int64_t)r * ldl + c);
+  *reinterpret_cast<uint4*>(p + (int64_t)r * V + c) = to_prob<true>(v, cr);
+}
+
+// Sum split-K partials in slice order (deterministic) and store in the output dtype.
+// Thread = one float4 of the MFMA-layout tile (4 consecutive rows of one column).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict__ part, int splits, int m_tiles,
+                                                       int n_tiles, int M, int d, void* __restrict__ out, int64_t ldo) {
+  constexpr int kTile4 = kBM * kBN / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
+  if (i >= per_split) return;
+  float4 s = part[i];
+  for (int k = 1; k < splits; ++k) {
+    const float4 v = part[(int64_t)k * per_split + i];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  // decode [tile][wave][i][j][e/4][lane] -> 4 rows r..r+3 of column c
+  const int q = (int)(i % kTile4);
+  const int64_t tile = i / kTile4;
+  const int mt = (int)(tile / n_tiles), nt = (int)(tile % n_tiles);
+  const int lane = q & 63, e4 = (q >> 6) & 3, jj = (q >> 8) & 3, ii = (q >> 10) & 3, wave = q >> 12;
+  const int r = mt * kBM + (wave >> 1) * 128 + 32 * ii + 8 * e4 + 4 * (lane >> 5);
+  const int c = nt * kBN + (wave & 1) * 128 + 32 * jj + (lane & 31);
+  if (c >= d) return;
+  const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (r + e >= M) break;
+    if (kBf16) reinterpret_cast<__bf16*>(out)[(int64_t)(r + e) * ldo + c] = (__bf16)v[e];
+    else reinterpret_cast<float*>(out)[(int64_t)(r + e) * ldo + c] = v[e];
   }
 }
 
@@ -272,6 +579,7 @@ __global__ __launch_bounds__(256) void selfcond_reduce(const float* __restrict__
 
 int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(a->workspace);
   GemmArgs g;
   g.p = a->p;
   g.ldp = a->ldp;
@@ -281,7 +589,9 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
   g.lde = a->lde;
   g.out = a->out;
   g.ldo = a->ldo;
-  g.part = plan.splits > 1 ? reinterpret_cast<float*>(a->workspace) : nullptr;
+  g.part = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.part_offset) : nullptr;
+  g.p_scale = a->p_scale;
+  g.nblocks = (a->V + DG_PROB_BLOCK - 1) / DG_PROB_BLOCK;
   g.M = a->M;
   g.V = a->V;
   g.d = a->d;
@@ -291,20 +601,34 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
   g.k_per_split = plan.k_per_split;
   const dim3 grid(plan.m_tiles * plan.n_tiles * plan.splits);
   const bool fused = a->row_max != nullptr;
-  if (a->dtype == DG_BF16) {
-    if (fused) hipLaunchKernelGGL((selfcond_gemm<true, true>), grid, dim3(kThreads), 0, s, g);
-    else hipLaunchKernelGGL((selfcond_gemm<true, false>), grid, dim3(kThreads), 0, s, g);
+  if (plan.dma) {
+    if (fused) {  // rebuild P once into the workspace, then the plain DMA GEMM
+      uint16_t* pn = reinterpret_cast<uint16_t*>(ws + plan.p_offset);
+      const int64_t n8 = (int64_t)a->M * (a->V / 8);
+      hipLaunchKernelGGL(selfcond_normalize, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                         reinterpret_cast<const uint16_t*>(a->p), a->ldp, a->row_max, a->row_sum, a->M, a->V, pn);
+      g.p = pn;
+      g.ldp = a->V;
+      g.row_max = g.row_sum = nullptr;
+    }
+    hipLaunchKernelGGL(selfcond_gemm_dma, grid, dim3(kThreads), 0, s, g);
+  } else if (a->dtype == DG_BF16) {
+    if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<true, true>), grid, dim3(kThreads), 0, s, g);
+    else hipLaunchKernelGGL((selfcond_gemm_reg<true, false>), grid, dim3(kThreads), 0, s, g);
   } else {
-    if (fused) hipLaunchKernelGGL((selfcond_gemm<false, true>), grid, dim3(kThreads), 0, s, g);
-    else hipLaunchKernelGGL((selfcond_gemm<false, false>), grid, dim3(kThreads), 0, s, g);
+    if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<false, true>), grid, dim3(kThreads), 0, s, g);
+    else hipLaunchKernelGGL((selfcond_gemm_reg<false, false>), grid, dim3(kThreads), 0, s, g);
   }
   if (plan.splits > 1) {
-    const int64_t n4 = (int64_t)a->M * a->d / 4;
+    const int64_t n4 = (int64_t)plan.m_tiles * plan.n_tiles * (kBM * kBN / 4);
     const dim3 rg((unsigned)((n4 + 255) / 256));
+    const float4* part = reinterpret_cast<const float4*>(g.part);
     if (a->dtype == DG_BF16)
-      hipLaunchKernelGGL(selfcond_reduce<true>, rg, dim3(256), 0, s, g.part, plan.splits, a->M, a->d, a->out, a->ldo);
+      hipLaunchKernelGGL(selfcond_reduce<true>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles, plan.n_tiles,
+                         a->M, a->d, a->out, a->ldo);
     else
-      hipLaunchKernelGGL(selfcond_reduce<false>, rg, dim3(256), 0, s, g.part, plan.splits, a->M, a->d, a->out, a->ldo);
+      hipLaunchKernelGGL(selfcond_reduce<false>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles, plan.n_tiles,
+                         a->M, a->d, a->out, a->ldo);
   }
   return (int)hipGetLastError();
 }

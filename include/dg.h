@@ -49,6 +49,7 @@ extern "C" {
 #define DG_MAX_SEQS 64      /* requests per dg_attn_mixed call */
 #define DG_MAX_REQS 64      /* requests per dg_sampler_step call */
 #define DG_MAX_CANVAS 1024  /* positions per sampler request */
+#define DG_PROB_BLOCK 8192  /* vocabulary entries per scale of a block-scaled probability matrix */
 
 typedef enum {
   DG_OK = 0,
@@ -142,6 +143,10 @@ size_t dg_attn_workspace_size(const dg_attn_args* args);
  *   prev_argmax  = argmax.
  * With DG_ENTROPY_IN the call reads `entropy` (and, for DG_CONF_MAX_PROB, `conf`)
  * instead of writing them, so a selection can be replayed on given entropies.
+ * Block-scaled probabilities (optional, for dg_selfcond_embed): with probs and
+ * probs_scale set, the call also writes w[i,v] (logits dtype) and s[i,b] (fp32) with
+ *   softmax(l[i,:])[v] = w[i,v] * s[i, v / DG_PROB_BLOCK]   (w rounded to the dtype),
+ * w = exp(l - max over the chunk of the row that holds v), s = the chunk's exp(max - row_max) / row_sum.
  * With DG_INIT_CANVAS the call only starts a block: canvas = Philox token from
  * counter (step, j, 2, 0), prev_argmax = -1, stable_count = 0, converged = 0,
  * num_accepted = 0; logits are not read.
@@ -191,6 +196,9 @@ typedef struct {
   int32_t* num_accepted;       /* device [num_reqs] */
   int32_t* converged;          /* device [num_reqs] (0/1) */
   float* mean_entropy;         /* device [num_reqs] */
+  void* probs;                 /* device [M, ldq] (logits dtype) or NULL: block-scaled probabilities w */
+  int64_t ldq;                 /* row stride of probs in elements, >= V, multiple of 8 */
+  float* probs_scale;          /* device [M, ceil(V / DG_PROB_BLOCK)] or NULL (set both or neither) */
   void* workspace;             /* device, >= dg_sampler_workspace_size(args) bytes */
   size_t workspace_bytes;
 } dg_sampler_args;
@@ -203,9 +211,13 @@ size_t dg_sampler_workspace_size(const dg_sampler_args* args);
  * ([P1] section "안정성을 위한 셀프 컨디셔닝"; [P3] section
  * "Mehanizam odlučivanja o gotovim tokenima"):
  *   out[i, :] = sum_v p[i, v] * embed[v, :]
- * p is either given (row_max == NULL) or rebuilt from logits and the sampler's row
- * statistics, p = exp(l - row_max[i]) / row_sum[i] (both non-NULL). Products are
- * accumulated in fp32; out has the input dtype.
+ * p is given in one of three forms:
+ *   - probabilities (row_max, row_sum and p_scale NULL);
+ *   - logits with the sampler's row statistics, p = exp(l - row_max[i]) / row_sum[i]
+ *     (row_max and row_sum set);
+ *   - block-scaled, p[i,v] = w[i,v] * p_scale[i, v / DG_PROB_BLOCK], as dg_sampler_step
+ *     writes it (p holds w, p_scale set).
+ * Products are accumulated in fp32; out has the input dtype.
  * ------------------------------------------------------------------------------ */
 typedef struct {
   int32_t M, V, d;             /* M >= 1; V >= 1; d a multiple of 128 */
@@ -214,6 +226,7 @@ typedef struct {
   int64_t ldp;                 /* >= V, multiple of 8 */
   const float* row_max;        /* device [M] or NULL */
   const float* row_sum;        /* device [M] or NULL (set both or neither) */
+  const float* p_scale;        /* device [M, ceil(V / DG_PROB_BLOCK)] or NULL; excludes row_max */
   const void* embed;           /* device [V, lde] */
   int64_t lde;                 /* >= d, multiple of 8 */
   void* out;                   /* device [M, ldo], dtype */

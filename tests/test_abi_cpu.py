@@ -134,6 +134,8 @@ def _sampler(**over):
     dict(ld=4100), dict(budget=float("inf")), dict(budget=-1.0), dict(tau=float("nan")), dict(min_accept=-1),
     dict(conf_mode=2), dict(combine=3), dict(renoise=2), dict(stable_k=0), dict(step_limit=0), dict(flags=4),
     dict(logits=None), dict(entropy=None), dict(accept=None), dict(canvas=FAKE + 2), dict(dtype=3),
+    dict(probs=FAKE, ldq=4096), dict(probs_scale=FAKE), dict(probs=FAKE, probs_scale=FAKE, ldq=4000),
+    dict(probs=FAKE + 8, probs_scale=FAKE, ldq=4096),
 ])
 def test_sampler_validation(change):
     a = _sampler(**change)
@@ -165,6 +167,7 @@ def _selfcond(**over):
     (dict(ldp=4000), dg.DG_ERR_INVALID_ARG), (dict(lde=100), dg.DG_ERR_INVALID_ARG),
     (dict(ldo=100), dg.DG_ERR_INVALID_ARG), (dict(field_p=None), dg.DG_ERR_INVALID_ARG),
     (dict(embed=FAKE + 8), dg.DG_ERR_INVALID_ARG), (dict(row_max=FAKE), dg.DG_ERR_INVALID_ARG),
+    (dict(row_max=FAKE, row_sum=FAKE, p_scale=FAKE), dg.DG_ERR_INVALID_ARG),
     (dict(dtype=2), dg.DG_ERR_INVALID_ARG),
 ])
 def test_selfcond_validation(change, status):

@@ -210,3 +210,36 @@ def test_repeat_is_bit_identical():
         outs.append([host(getattr(b, n)).copy() for n in ("entropy", "row_sum", "cand", "accept", "canvas")])
     for a, bb in zip(*outs):
         assert np.array_equal(a, bb)
+
+
+@pytest.mark.parametrize("bf16,V", [(True, 262144), (False, 4096), (True, 40000), (False, 12)])
+def test_block_scaled_probabilities(bf16, V):
+    """w * scale per DG_PROB_BLOCK reproduces the softmax: within the rounding of w to the
+    logits dtype (unit roundoff 2^-8 for bf16) plus fp32 arithmetic in the scale
+    (1e-5 relative), and exactly 0 where p is 0."""
+    rng = np.random.default_rng(V + bf16)
+    M = 40 if V > 100000 else 9
+    l = (rng.standard_normal((M, V)) * rng.uniform(0.1, 10, (M, 1))).astype(np.float32)
+    l[1, ::3] = -np.inf
+    if bf16:
+        l = round_to_bf16(l)
+    ld = (V + 7) // 8 * 8
+    full = np.zeros((M, ld), np.float32)
+    full[:, :V] = l
+    lt = dev(full, bf16)[:, :V]
+    b = dg.SamplerBuffers(M, 1, DEV, vocab=V, probs_dtype=lt.dtype)
+    dg.dg_sampler_step(lt, [(0, M, 3, 0)], V, b, 16.0)
+    torch.cuda.synchronize()
+    w = host(b.probs).astype(np.float64)
+    sc = host(b.probs_scale).astype(np.float64)
+    blk = np.arange(V) // dg.DG_PROB_BLOCK
+    p = w * sc[:, blk]
+    ref = np.exp(l.astype(np.float64) - l.max(axis=1, keepdims=True))
+    ref /= ref.sum(axis=1, keepdims=True)
+    tol = 2.0 ** -8 + 1e-5 if bf16 else 1e-5
+    nz = ref > 1e-30
+    rel = np.abs(p[nz] - ref[nz]) / ref[nz]
+    say(f"[sampler] block-scaled probs V={V} bf16={bf16}: max rel {rel.max():.3e}")
+    assert rel.max() <= tol
+    assert np.all(p[ref == 0] == 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=2e-3 if bf16 else 1e-5)

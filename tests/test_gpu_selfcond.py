@@ -68,10 +68,11 @@ def test_config2_bf16_full_size_sampled_rows():
     assert err2 <= TOL
 
 
-@pytest.mark.parametrize("bf16", [False, True])
-def test_one_hot_bit_exact(bf16):
-    """P-C1 on the GPU: one-hot rows return exactly the embedding row."""
-    V, d, M = 3000, 256, 70
+@pytest.mark.parametrize("bf16,V", [(False, 3000), (True, 3000), (True, 3008)])
+def test_one_hot_bit_exact(bf16, V):
+    """P-C1 on the GPU: one-hot rows return exactly the embedding row (V = 3008 takes
+    the LDS-DMA kernel, V = 3000 the register-staged one)."""
+    d, M = 256, 70
     E = embed_table(9, V, d, bf16=bf16)
     rng = np.random.default_rng(1)
     hot = rng.integers(0, V, M)
@@ -119,3 +120,28 @@ def test_repeat_is_bit_identical():
         torch.cuda.synchronize()
         outs.append(host(o))
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("bf16,M,V,d", [(True, 256, 262144, 2048), (False, 256, 4096, 256), (True, 300, 40000, 384),
+                                        (True, 64, 8200, 128)])
+def test_block_scaled_from_sampler(bf16, M, V, d):
+    """The sampler's block-scaled probabilities feed self-conditioning directly; the
+    result matches the oracle's softmax-weighted average."""
+    rng = np.random.default_rng(M + V + d)
+    l = (rng.standard_normal((M, V)) * rng.uniform(0.1, 10, (M, 1))).astype(np.float32)
+    E = (rng.standard_normal((V, d)) * 0.02).astype(np.float32)
+    if bf16:
+        l, E = round_to_bf16(l), round_to_bf16(E)
+    ld = (V + 7) // 8 * 8
+    full = np.zeros((M, ld), np.float32)
+    full[:, :V] = l
+    lt = dev(full, bf16)[:, :V]
+    b = dg.SamplerBuffers(M, 1, DEV, vocab=V, probs_dtype=lt.dtype)
+    dg.dg_sampler_step(lt, [(0, min(M, 1024), 5, 0)], V, b, 64.0)
+    out = torch.empty(M, d, device=DEV, dtype=lt.dtype)
+    dg.dg_selfcond_embed(b.probs, dev(E, bf16), out, p_scale=b.probs_scale)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, M // 2, M - 1] + list(range(0, M, max(1, M // 8)))))
+    err = max_rel_rows(host(out)[rows], selfcond_embed(E, logits=l[rows]))
+    say(f"[selfcond] block-scaled M={M} V={V} d={d} bf16={bf16}: max-rel {err:.3e}")
+    assert err <= TOL
