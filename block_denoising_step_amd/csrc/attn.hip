@@ -334,10 +334,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 
 // Combine the chunk partials of one (request, KV head, q tile) in chunk order:
 // O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.
+// Merge of a request's key-chunk partials: one thread per 4 output columns of a row,
+// so that one (q tile, kv head) unit spreads over D/8 work groups and every load is
+// an independent, coalesced float4.
+template <int D>
+constexpr int merge_groups_per_unit() { return kRows * (D / 4) / kThreads; }
+
 template <bool kBf16, int D>
 __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
   constexpr int esz = kBf16 ? 2 : 4;
-  const int w = blockIdx.x;
+  constexpr int kTpr = D / 4;             // threads per row
+  constexpr int kRpw = kThreads / kTpr;   // rows per work group
+  constexpr int kGpu = merge_groups_per_unit<D>();
+  const int w = blockIdx.x / kGpu;
   const int s = find_seq(a, w, true);
   const AttnSeqPlan sp = a.seqs[s];
   const int nqt = (sp.num_q + a.tokens_per_tile - 1) / a.tokens_per_tile;
@@ -352,49 +361,388 @@ __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
   const int nonempty = min(sp.num_chunks, (kt_hi - kt_lo) / sp.chunk_tiles + 1);
   const int part0 = sp.part_begin + (g * nqt + qt) * sp.num_chunks;
 
-  // two threads per row, each half of D
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int row = (blockIdx.x % kGpu) * kRpw + threadIdx.x / kTpr;
+  const int c = (threadIdx.x % kTpr) * 4;
   const int tok = i0 + row / a.group;
   const int head = g * a.group + row % a.group;
   if (tok >= sp.num_q) return;
   float mmax = kNegInf;
+#pragma unroll 4
   for (int j = 0; j < nonempty; ++j) mmax = fmaxf(mmax, a.part_ml[((int64_t)(part0 + j) * kRows + row) * 2]);
   float wsum = 0.f;
-  float acc[D / 2];
-#pragma unroll
-  for (int d = 0; d < D / 2; ++d) acc[d] = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int j = 0; j < nonempty; ++j) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)(part0 + j) * kRows + row) * 2);
-    const float f = fast_exp2(ml.x - mmax);
-    if (f == 0.f) continue;
+    const int64_t pr = (int64_t)(part0 + j) * kRows + row;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+    const float4 x = *reinterpret_cast<const float4*>(a.part_o + pr * D + c);
+    const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - mmax);
     wsum = fmaf(f, ml.y, wsum);
-    const float* po = a.part_o + ((int64_t)(part0 + j) * kRows + row) * D + half * (D / 2);
-#pragma unroll
-    for (int d = 0; d < D / 2; d += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(po + d);
-      acc[d] = fmaf(f, x.x, acc[d]);
-      acc[d + 1] = fmaf(f, x.y, acc[d + 1]);
-      acc[d + 2] = fmaf(f, x.z, acc[d + 2]);
-      acc[d + 3] = fmaf(f, x.w, acc[d + 3]);
-    }
+    acc.x = fmaf(f, x.x, acc.x);
+    acc.y = fmaf(f, x.y, acc.y);
+    acc.z = fmaf(f, x.z, acc.z);
+    acc.w = fmaf(f, x.w, acc.w);
   }
   const float inv = 1.f / wsum;
-  char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz + half * (D / 2) * esz;
-#pragma unroll
-  for (int d = 0; d < D / 2; d += 4) {
-    if (kBf16)
-      *reinterpret_cast<uint2*>(orow + d * 2) =
-          make_uint2(pack_bf16(acc[d] * inv, acc[d + 1] * inv), pack_bf16(acc[d + 2] * inv, acc[d + 3] * inv));
-    else
-      *reinterpret_cast<float4*>(orow + d * 4) = make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
+  char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz + c * esz;
+  if (kBf16)
+    *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
+  else
+    *reinterpret_cast<float4*>(orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (a.lse && c == 0) a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (mmax + __builtin_amdgcn_logf(wsum)) * kLn2;
+}
+
+// ---- bf16, head_dim 256: LDS-DMA ring kernel -------------------------------------
+//
+// The same work unit as attn_fwd (128 query rows x one key chunk), in 32-key
+// sub-tiles, software-pipelined by one sub-tile: while the matrix cores compute
+// S(j+1) = K(j+1) . Q^T, the vector units turn S(j) into P(j), and then
+// O^T += V(j)^T . P(j)^T. K and V rows go from HBM straight to LDS
+// through a 4-deep ring whose stage j holds K(j+1) and V(j), so every iteration reads
+// exactly one stage while the next three are in flight. The copies are
+// global_load_lds_dwordx4 (uniform 64-bit base, per-lane 32-bit offset).
+//
+// LDS layout: one DMA instruction writes 1 KB = 2 key rows; inside it, 16-byte chunk
+// c of the row with parity p sits at slot 2c + p, and 2-row pairs are 1056 B (K) and
+// 1152 B (V) apart. With these pitches the S^T operand reads (ds_read_b128, 32 rows x
+// one chunk) and the V^T operand reads (ds_read_b64_tr_b16, 4 rows x 32 columns) hit
+// 64 distinct banks, and every read address is a per-lane base plus an immediate.
+// The V^T reads take keys 4h+0..3 and 8+4h+0..3 of each 16, the order in which the
+// S^T accumulator holds P^T.
+//
+// Softmax: base 2 against a fixed reference per row, the max of the first sub-tile
+// in which the row has a finite score (until then the row's O and sum are exactly
+// zero). Later scores may exceed it: P = 2^(s - ref) then grows, which bf16 and the
+// fp32 accumulators represent with the same relative precision, so O is never
+// rescaled and its 128 accumulators stay in AGPRs, touched only by MFMAs. Should a
+// score exceed the reference by more than 2^64 (beyond any practical attention
+// logit spread, but possible for adversarial inputs), the work group recomputes the
+// chunk with the largest score it saw as the new reference.
+
+constexpr int kSub = 32;                         // keys per sub-tile
+constexpr int kAttStages = 4;
+constexpr int kKPitch = 1056;                    // bytes between K row pairs
+constexpr int kVPitch = 1152;                    // bytes between V row pairs
+constexpr int kKRegion = (kSub / 2) * kKPitch;   // 16896
+constexpr int kVRegion = (kSub / 2) * kVPitch;   // 18432
+constexpr int kAttStage = kKRegion + kVRegion;   // 35328; 4 stages = 138 KB
+constexpr float kOverflow = 64.f;             // log2 headroom of the fixed reference
+
+#define DG_ATT_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// The LDS reads are inline asm, whose results the compiler takes as ready at once:
+// the fence keeps every use of them below the wait.
+#define DG_ATT_WAIT_LGKM0()                                          \
+  do {                                                               \
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); \
+    __builtin_amdgcn_sched_barrier(0);                               \
+  } while (0)
+
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  static __device__ __forceinline__ void run(F&& f) {
+    f(std::integral_constant<int, I>{});
+    StaticFor<I + 1, N>::run(f);
   }
-  if (a.lse && half == 0) a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (mmax + __builtin_amdgcn_logf(wsum)) * kLn2;
+};
+template <int N>
+struct StaticFor<N, N> {
+  template <class F>
+  static __device__ __forceinline__ void run(F&&) {}
+};
+
+template <int kOff>
+__device__ __forceinline__ uint4 att_b128(uint32_t addr) {
+  uint4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+  return r;
+}
+template <int kOff>
+__device__ __forceinline__ uint2 att_tr16(uint32_t addr) {
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+  return r;
+}
+
+// Both halves of the wave get f(x[lane % 32], x[lane % 32 + 32]).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Work groups are dealt round-robin to the 8 XCDs; renumber them so that consecutive
+// indices share an XCD (and its L2): the q tiles of one key chunk read the same K/V.
+__device__ __forceinline__ int xcd_order(int b, int n) {
+  const int q = n >> 3, r = n & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
+__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
+  constexpr int D = 256, KS = 16, DB = 8;
+  __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kAttStage];
+  __shared__ int redo_flag[1];  // set by a wave that saw a score past the reference
+
+  const int w = xcd_order(blockIdx.x, gridDim.x);
+  const int s_ = find_seq(a, w, false);
+  const AttnSeqPlan sp = a.seqs[s_];
+  const int nqt = (sp.num_q + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  const int local = w - sp.work_begin;
+  const int qt = local % nqt;  // q tiles of one (kv head, chunk) are consecutive
+  const int rest = local / nqt;
+  const int chunk = rest % sp.num_chunks;
+  const int g = rest / sp.num_chunks;
+  const int i0 = qt * a.tokens_per_tile;
+  const int nq = min(a.tokens_per_tile, sp.num_q - i0);
+  const int nkeys = sp.prefix_len + sp.num_q;
+  int lo_first, hi_first, lo_last, hi_last;
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0 + nq - 1, lo_last, hi_last);
+  const int kt_lo = lo_first / kKT, kt_hi = hi_last / kKT;
+  const int t_begin = kt_lo + chunk * sp.chunk_tiles;
+  const int t_end = min(kt_hi + 1, t_begin + sp.chunk_tiles);
+  if (t_begin > kt_hi) return;  // empty chunk (uniform across the work group)
+  const int key0 = t_begin * kKT;
+  const int kend = min(t_end * kKT, hi_last + 1);  // <= nkeys
+  const int nsub = (kend - key0 + kSub - 1) / kSub;  // >= 1
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int row = wave * 32 + l32;
+  const int tok = i0 + row / a.group;
+  const int head = g * a.group + row % a.group;
+  const bool valid = tok < sp.num_q;
+  int lo = 0, hi = -1;
+  if (valid) key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, tok, lo, hi);
+
+  uint4 qf[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + (16 * ks + 8 * hh) * 2) : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- DMA: wave w fills pairs 4w..4w+3 of the K and V regions; lane i loads
+  // chunk i/2 of key row 2*pair + i%2 (per-request byte offsets fit in 32 bits).
+  const int rs = a.hkv * D * 2;  // bytes between consecutive keys
+  const int64_t head_off = ((int64_t)sp.kv_start * a.hkv + g) * D * 2;
+  const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
+  uint32_t vo[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) vo[t] = (2 * (4 * wave + t) + (lane & 1)) * rs + (lane >> 1) * 16;
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* lds0 = (lds_char*)lds;
+  // rows kbase .. kbase+31 into the K or V region at `dst` (uniform base + per-lane
+  // 32-bit offset); rows past the request's last key repeat that key (they are masked)
+  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase) {
+    const char* src = base + (int64_t)kbase * rs;
+    if (kbase + kSub <= nkeys) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds((const void*)(src + vo[t]),
+                                         (__attribute__((address_space(3))) void*)(dst + (4 * wave + t) * pitch), 16, 0, 0);
+    } else {
+      const int last = nkeys - 1 - kbase;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t r = min(2 * (4 * wave + t) + (lane & 1), last);
+        __builtin_amdgcn_global_load_lds((const void*)(src + (r * rs + (lane >> 1) * 16)),
+                                         (__attribute__((address_space(3))) void*)(dst + (4 * wave + t) * pitch), 16, 0, 0);
+      }
+    }
+  };
+  // stage j: K of sub-tile j+1 (the last stage repeats sub-tile nsub-1: unused) and V of j
+  auto issue = [&](int j) {
+    lds_char* st = lds0 + (j & 3) * kAttStage;
+    dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
+    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
+  };
+
+  // ---- LDS read addresses: per-lane base + immediates
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
+  const uint32_t k_lane = (l32 >> 1) * kKPitch + 16 * (l32 & 1) + 32 * hh;  // + 64*ks
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int vrow = 4 * (grp >> 1) + (s16 >> 2);  // + 8q + 16 half
+  const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);  // + 32 b
+  const uint32_t v_lane = kKRegion + (vrow >> 1) * kVPitch + 16 * (vrow & 1) + 32 * (vcol >> 3) + 2 * (vcol & 7);
+
+  // mask S(j) where some row's bounds cut sub-tile j; returns the row max (scaled)
+  auto front = [&](f32x16_t& sv, int kbase) {
+    if (!(lo_last <= kbase && kbase + kSub - 1 <= hi_first)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (key < lo || key > hi) sv[e] = kNegInf;
+      }
+    }
+    float t = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    t = fmaxf(t, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    return half_max(t) * a.scale_log2;
+  };
+
+  f32x16_t o[DB];
+  float l_run;
+  float m_ref = kNegInf;  // fixed reference (scaled log2 units) of this lane's row
+  for (;;) {
+    if (tid == 0) redo_flag[0] = 0;
+    // ---- prologue: K(0) into the K region of slot 3, stages 0..2, then S(0)
+    dma_rows(kb, lds0 + 3 * kAttStage, kKPitch, key0);
+    issue(0);
+    if (nsub > 1) issue(1);
+    if (nsub > 2) issue(2);
+    if (nsub > 2) DG_ATT_WAIT_VM(24);
+    else if (nsub > 1) DG_ATT_WAIT_VM(16);
+    else DG_ATT_WAIT_VM(8);
+    DG_ATT_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    f32x16_t scur;
+    {
+      const uint32_t ka = lbase + 3 * kAttStage + k_lane;
+      uint4 kf[KS];
+      StaticFor<0, KS>::run([&](auto ks) { kf[ks] = att_b128<64 * decltype(ks)::value>(ka); });
+      DG_ATT_WAIT_LGKM0();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) scur[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        scur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), scur, 0, 0, 0);
+    }
+    float m_seen = front(scur, key0);
+    if (m_ref == kNegInf) m_ref = m_seen;  // on a retry m_ref already covers this sub-tile
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+    l_run = 0.f;
+
+    bool overflow = false;
+    for (int sub = 0; sub < nsub; ++sub) {
+      const int left = nsub - 1 - sub;
+      if (left >= 2) DG_ATT_WAIT_VM(16);
+      else if (left == 1) DG_ATT_WAIT_VM(8);
+      else DG_ATT_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
+      if (sub + 3 < nsub) issue(sub + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t ka = lbase + (sub & 3) * kAttStage + k_lane;
+      const uint32_t va = lbase + (sub & 3) * kAttStage + v_lane;
+      const float mu = m_ref == kNegInf ? 0.f : m_ref;
+
+      uint4 kf[KS];
+      uint2 v0[DB][2], v1[DB][2];
+      StaticFor<0, 8>::run([&](auto ks) { kf[ks] = att_b128<64 * decltype(ks)::value>(ka); });
+      DG_ATT_WAIT_LGKM0();
+      __builtin_amdgcn_sched_barrier(0);
+
+      // S(sub+1) k-steps 0..7, K reads 8..15, V^T reads of keys 0..15, P(sub)
+      f32x16_t snxt;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) snxt[e] = 0.f;
+      float p[16];
+      StaticFor<0, 8>::run([&](auto ic) {
+        constexpr int ks = decltype(ic)::value;
+        snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), snxt, 0, 0, 0);
+        kf[ks + 8] = att_b128<64 * (ks + 8)>(ka);
+        v0[ks][0] = att_tr16<128 * ks>(va);
+        v0[ks][1] = att_tr16<128 * ks + 4 * kVPitch>(va);
+        p[2 * ks] = fast_exp2(fmaf(scur[2 * ks], a.scale_log2, -mu));
+        p[2 * ks + 1] = fast_exp2(fmaf(scur[2 * ks + 1], a.scale_log2, -mu));
+        l_run += p[2 * ks] + p[2 * ks + 1];
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      uint4 pf[2];
+      pf[0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
+                         pack_bf16(p[14], p[15]));
+      DG_ATT_WAIT_LGKM0();
+      __builtin_amdgcn_sched_barrier(0);
+
+      // O^T += V^T(keys 0..15) . P^T, S(sub+1) k-steps 8..15, V^T reads of keys 16..31
+      StaticFor<0, DB>::run([&](auto ic) {
+        constexpr int b = decltype(ic)::value;
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(v0[b][0].x, v0[b][0].y, v0[b][1].x, v0[b][1].y)),
+            __builtin_bit_cast(bf16x8_t, pf[0]), o[b], 0, 0, 0);
+        snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[8 + b]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
+        v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
+        v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      DG_ATT_WAIT_LGKM0();
+      __builtin_amdgcn_sched_barrier(0);
+      StaticFor<0, DB>::run([&](auto ic) {
+        constexpr int b = decltype(ic)::value;
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(v1[b][0].x, v1[b][0].y, v1[b][1].x, v1[b][1].y)),
+            __builtin_bit_cast(bf16x8_t, pf[1]), o[b], 0, 0, 0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+
+      // next sub-tile: mask, max, reference of rows seeing their first finite score
+      if (sub + 1 < nsub) {
+        scur = snxt;
+        const float tmax = front(scur, key0 + kSub * (sub + 1));
+        m_seen = fmaxf(m_seen, tmax);
+        if (m_ref == kNegInf) m_ref = tmax;
+        overflow |= tmax > m_ref + kOverflow;
+      }
+    }
+    // the loop ends with the ring drained; a rare overflow anywhere redoes the chunk
+    if (__any(overflow) && lane == 0) redo_flag[0] = 1;
+    __syncthreads();
+    const int redo = redo_flag[0];
+    if (!redo) break;
+    __syncthreads();  // every wave has read the flag before it is cleared
+    m_ref = fmaxf(m_ref, m_seen);
+  }
+
+  // ---- epilogue: o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]
+  const float l_tot = half_sum(l_run);
+  if (!valid) return;
+  if (sp.num_chunks == 1) {
+    const float inv = 1.f / l_tot;
+    char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = 32 * b + 8 * e4 + 4 * hh;
+        *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(pack_bf16(o[b][4 * e4] * inv, o[b][4 * e4 + 1] * inv),
+                                                             pack_bf16(o[b][4 * e4 + 2] * inv, o[b][4 * e4 + 3] * inv));
+      }
+    if (a.lse && hh == 0)
+      a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  } else {
+    const int part = sp.part_begin + (g * nqt + qt) * sp.num_chunks + chunk;
+    float* po = a.part_o + ((int64_t)part * kRows + row) * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<float4*>(po + 32 * b + 8 * e4 + 4 * hh) =
+            make_float4(o[b][4 * e4], o[b][4 * e4 + 1], o[b][4 * e4 + 2], o[b][4 * e4 + 3]);
+    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_ref, l_tot);
+  }
 }
 
 template <bool kBf16, int D>
 int launch_typed(const AttnArgs& args, const AttnPlan& plan, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd<kBf16, D>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
-  if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
+  if (kBf16 && D == 256 && plan.dma)
+    hipLaunchKernelGGL(attn_fwd_bf16_d256, dim3(plan.num_work), dim3(kThreads), 0, s, args);
+  else
+    hipLaunchKernelGGL((attn_fwd<kBf16, D>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
+  if (plan.num_merge > 0)
+    hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge * merge_groups_per_unit<D>()), dim3(kThreads), 0, s,
+                       args);
   return (int)hipGetLastError();
 }
 

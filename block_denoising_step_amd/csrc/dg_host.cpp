@@ -43,14 +43,14 @@ void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int*
 //
 // A request with a single chunk per q tile writes its output directly; one with
 // several writes fp32 partials that the merge kernel combines in chunk order.
-// A request's chunk length gives it about kTargetGroups work groups, but never
-// under kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write
-// and read.
+// A request's chunk length gives it about kTargetGroups work groups (one per compute
+// unit: a work group of the bf16 head_dim-256 kernel fills a CU), but never under
+// kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write and read.
 
 static constexpr int kKeyTile = kAttnKeyTile;
 static constexpr int kTileRows = kAttnTileRows;
-static constexpr int kTargetGroups = 512;
-static constexpr int kMinChunkTiles = 8;
+static constexpr int kTargetGroups = 256;
+static constexpr int kMinChunkTiles = 4;
 
 dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
@@ -96,6 +96,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   const int tok_per_tile = kTileRows / G;
   int64_t num_work = 0, num_merge = 0, num_parts = 0;
   plan->num_seqs = a->num_seqs;
+  plan->dma = a->dtype == DG_BF16 && a->head_dim == 256;
   for (int s = 0; s < a->num_seqs; ++s) {
     const dg_seq& q = a->seqs[s];
     const int64_t ntiles_q = ceil_div(q.num_q, tok_per_tile);
@@ -113,6 +114,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     if (a->kv_chunk > 0) chunk_tiles = a->kv_chunk / kKeyTile;
     else chunk_tiles = std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
     const int64_t nch = max_tiles > 0 ? ceil_div(max_tiles, chunk_tiles) : 0;
+    if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
     AttnSeqPlan& sp = plan->seqs[s];
     sp.q_start = q.q_start;
     sp.num_q = q.num_q;

@@ -366,7 +366,11 @@ constexpr int kStageBytes = kStageA + kStageB;
 // s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt left open).
 #define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // s_waitcnt for all LDS reads of this wave (vmcnt left open).
-#define DG_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
+#define DG_WAIT_LGKM0()                                              \
+  do {                                                               \
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); \
+    __builtin_amdgcn_sched_barrier(0);                               \
+  } while (0)
 
 // LDS operand reads as inline asm: the compiler's wait insertion would otherwise put a
 // vmcnt(0) before every LDS read that follows an LDS DMA, serialising the ring. Each

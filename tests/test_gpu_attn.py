@@ -18,19 +18,19 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
-def _gpu(case_seqs, window, q, k, v, hq, hkv, bf16, kv_chunk=0, out_fill=np.nan):
+def _gpu(case_seqs, window, q, k, v, hq, hkv, bf16, kv_chunk=0, out_fill=np.nan, scale=0.0):
     qt, kt, vt = dev(q, bf16), dev(k, bf16), dev(v, bf16)
     out = torch.full(qt.shape, out_fill, device=DEV, dtype=qt.dtype)
     lse = torch.full(qt.shape[:2], np.nan, device=DEV, dtype=torch.float32)
-    dg.dg_attn_mixed(qt, kt, vt, out, case_seqs, window, hq, hkv, lse=lse, kv_chunk=kv_chunk)
+    dg.dg_attn_mixed(qt, kt, vt, out, case_seqs, window, hq, hkv, lse=lse, kv_chunk=kv_chunk, scale=scale)
     torch.cuda.synchronize()
     return host(out), host(lse)
 
 
-def _compare(seqs, window, q, k, v, hq, hkv, bf16, rows=None, kv_chunk=0, label=""):
+def _compare(seqs, window, q, k, v, hq, hkv, bf16, rows=None, kv_chunk=0, label="", scale=0.0):
     say(f"[attn] {label}: W={window} rows={'all' if rows is None else len(rows)} chunk={kv_chunk}")
-    out, lse = _gpu(seqs, window, q, k, v, hq, hkv, bf16, kv_chunk)
-    want, wlse = ref_attn(seqs, window, q, k, v, hq, hkv, rows=rows)
+    out, lse = _gpu(seqs, window, q, k, v, hq, hkv, bf16, kv_chunk, scale=scale)
+    want, wlse = ref_attn(seqs, window, q, k, v, hq, hkv, scale=scale or None, rows=rows)
     sel = np.arange(q.shape[0]) if rows is None else np.array(rows)
     err = max_rel_rows(out[sel], want[sel])
     lerr = float(np.abs(lse[sel] - wlse[sel]).max())
@@ -123,3 +123,23 @@ def test_repeat_is_bit_identical():
     a, la = _gpu(c.seqs, -1, q, k, v, 16, 8, True)
     b, lb = _gpu(c.seqs, -1, q, k, v, 16, 8, True)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("D,bf16", [(256, True), (128, True), (128, False)])
+def test_score_jump_far_past_first_tile(D, bf16):
+    """Keys after the first 32 score far above the first ones (by 2^91 in log2 units at
+    head_dim 256): a
+    kernel that fixes each row's softmax reference from its first scores has to
+    recompute, and the result still matches the oracle."""
+    P, N, H = 96, 40, 2
+    rng = np.random.default_rng(77 + D)
+    q = 0.5 + 0.05 * rng.standard_normal((N, H, D))
+    k = 0.25 + 0.05 * rng.standard_normal((P + N, H, D))
+    k[:32] *= -1.0
+    v = rng.standard_normal((P + N, H, D))
+    q, k, v = (x.astype(np.float32) for x in (q, k, v))
+    if bf16:
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    seqs = pack_seqs([(P, N, BIDIR)])
+    for chunk in (0, 64):
+        _compare(seqs, -1, q, k, v, H, H, bf16, kv_chunk=chunk, scale=1.0, label=f"score jump D={D}")
