@@ -53,28 +53,58 @@ def algorithmic():
                 sc_bytes=sc_bytes)
 
 
-def cpu_baseline(q, k, v, logits0, E, seqs, seed, rows=32):
-    """The oracle, as it stands, on `rows` of the 256 canvas rows of one step; the
-    time is scaled to a whole step (every part is per canvas row)."""
+def cpu_baseline(q, k, v, logits_by_step, E, seqs, seed, min_seconds=10.0, max_steps=6):
+    """The oracle, as it stands, on whole steps of the same workload (all canvas rows:
+    attention, sampler with its state carried from step to step, self-conditioning),
+    run until `min_seconds` have passed."""
     from oracle.attn import attn_mixed
-    from oracle.sampler import sampler_step, CONV_OR
+    from oracle.sampler import sampler_step, init_canvas, CONV_OR
     from oracle.selfcond import selfcond_embed
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    canvas = init_canvas([(0, CANVAS, seed, 0)], VOCAB)
+    prev = np.full(CANVAS, -1, np.int64)
+    stable = [0]
+    steps = 0
     t0 = time.perf_counter()
-    attn_mixed(seqs, -1, q, k, v, HQ, HKV, rows=range(rows))
-    sampler_step(logits0[:rows], [(0, rows, seed, 0)], VOCAB, BUDGET, 1, np.zeros(rows, np.int64),
-                 np.full(rows, -1), [0], stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=CONV_OR)
-    selfcond_embed(E, logits=logits0[:rows])
+    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
+        logits = logits_by_step(steps)
+        attn_mixed(seqs, -1, q, k, v, HQ, HKV)
+        r = sampler_step(logits, [(0, CANVAS, seed, steps)], VOCAB, BUDGET, 1, canvas, prev, stable,
+                         stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=CONV_OR)
+        canvas, prev, stable = r["canvas"], r["prev_argmax"], list(r["stable_count"])
+        selfcond_embed(E, logits=logits)
+        steps += 1
     dt = time.perf_counter() - t0
-    per_step = dt * CANVAS / rows
-    return {"value": round(1.0 / per_step, 6), "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {CANVAS} canvas rows of one step (attention, sampler, self-conditioning), "
-                      f"{dt:.1f} s measured, scaled x{CANVAS // rows} to a whole step",
-            "cpu": _cpu_model()}
+    return {"value": round(steps / dt, 6), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} whole steps of the same workload (all {CANVAS} canvas rows: attention, sampler "
+                      f"with state carried, self-conditioning) in {dt:.1f} s", "cpu": _cpu_model()}
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "denoise_step_prefix4096_canvas256_hbm_counters.md")
+SELFCOND_SOURCES = ["selfcond.hip", "dg_host.cpp", "dg_common.cuh", "dg_internal.h"]
+
+
+def counted_traffic():
+    """HBM bytes per dg_selfcond_embed call from the committed counter summary (two
+    rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None
+    once the sources the counters were taken from have changed."""
+    import hashlib
+    try:
+        with open(COUNTERS) as f:
+            fields = dict(line.strip().split(": ", 1) for line in f if line.startswith(("traffic_", "source_")))
+        h = hashlib.sha256()
+        for name in SELFCOND_SOURCES:
+            with open(os.path.join(ROOT, "block_denoising_step_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+    except (OSError, ValueError):
+        return None
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_call"])
 
 
 def _cpu_model():
@@ -249,7 +279,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(sc_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(),
+            "traffic_unit": "bytes per call",
         },
         "kernels": {
             "attn_mixed": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 1),
@@ -261,8 +292,8 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        logits0 = pool_np[driver_rows(0)]
-        line["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, logits0, E_np, case.seqs, seed)
+        line["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, lambda t: pool_np[driver_rows(t)], E_np, case.seqs,
+                                            seed)
     print(json.dumps(line), flush=True)
 
 
