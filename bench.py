@@ -92,19 +92,32 @@ def counted_traffic():
     """HBM bytes per dg_selfcond_embed call from the committed counter summary (two
     rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None
     once the sources the counters were taken from have changed."""
-    import hashlib
     try:
         with open(COUNTERS) as f:
             fields = dict(line.strip().split(": ", 1) for line in f if line.startswith(("traffic_", "source_")))
-        h = hashlib.sha256()
+        texts = []
         for name in SELFCOND_SOURCES:
-            with open(os.path.join(ROOT, "block_denoising_step_amd", "csrc", name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(ROOT, "block_denoising_step_amd", "csrc", name)) as f:
+                texts.append(f.read())
     except (OSError, ValueError):
         return None
-    if fields.get("source_sha256") != h.hexdigest():
+    if fields.get("source_sha256") != code_hash(texts):
         return None
     return int(fields["traffic_bytes_per_call"])
+
+
+def code_hash(texts):
+    """sha256 of source files with // comments, trailing blanks and empty lines removed,
+    so that comment edits do not count as kernel changes."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for text in texts:
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
 
 
 def _cpu_model():

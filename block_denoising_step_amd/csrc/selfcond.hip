@@ -10,8 +10,8 @@
 // chunks so staging writes and operand reads are free of bank conflicts.
 //
 //   selfcond_gemm_dma  bf16, V a multiple of 32: the P and E tiles go straight from
-//                      HBM to LDS (global_load_lds_dwordx4) through a 4-stage ring,
-//                      so three K steps are in flight with no register staging. E
+//                      HBM to LDS (global_load_lds_dwordx4) through a 5-stage ring,
+//                      so four K steps are in flight with no register staging. E
 //                      stays row-major in LDS; its MFMA operand (8 consecutive k of one
 //                      column per lane) comes from two ds_read_b64_tr_b16 transposing
 //                      reads. One fence-free barrier per K step.
