@@ -42,6 +42,26 @@ __device__ __forceinline__ int wave_min_int(int v) {
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
   return v;
 }
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Inclusive prefix sum over the lanes, in lane order.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+// The value of the previous lane (0 in lane 0): an exclusive scan from an inclusive one.
+__device__ __forceinline__ float wave_shift_up(float x) {
+  const float y = __shfl_up(x, 1, 64);
+  return (threadIdx.x & 63) ? y : 0.f;
+}
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) ---------------------------
 // One round maps (x0,x1,x2,x3) under key (k0,k1) to

@@ -191,8 +191,8 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   plan->chunk = a->dtype == DG_BF16 ? 16384 : 8192;
   plan->num_chunks = (int)ceil_div(a->vocab, plan->chunk);
   if (plan->num_chunks > 1024) return bad(DG_ERR_UNSUPPORTED, "vocab too large (more than 1024 row-pass chunks)");
-  plan->counter_offset = align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
-  plan->bytes = init ? 0 : plan->counter_offset + align_up(DG_MAX_REQS * sizeof(int32_t), 256);
+  plan->sub_offset = align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
+  plan->bytes = init ? 0 : plan->sub_offset + align_up((size_t)a->num_rows * plan->num_chunks * 32 * sizeof(float), 256);
   return DG_OK;
 }
 

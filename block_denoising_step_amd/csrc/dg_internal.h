@@ -52,8 +52,8 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg);
 struct SamplerPlan {
   int chunk;              // vocabulary entries per row-pass work group
   int num_chunks;         // chunks per row
-  size_t counter_offset;  // workspace: per-request completion counters (int32)
-  size_t bytes;           // workspace bytes (per-chunk statistics, counters)
+  size_t sub_offset;      // workspace: sub-chunk masses [rows][chunks][32] fp32
+  size_t bytes;           // workspace bytes (per-chunk statistics, sub-chunk masses)
 };
 dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char** msg);
 

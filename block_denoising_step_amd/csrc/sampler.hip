@@ -1,18 +1,23 @@
-// DiffusionSampler denoise step on gfx950: three launches.
+// DiffusionSampler denoise step on gfx950: three launches, none of which waits on
+// another work group (no atomics, no device-scope fences: on a multi-XCD part a
+// device-scope release writes back the L2, which costs more than a kernel boundary).
 //
 //   sampler_rowpass   one streaming, read-only pass over the logits. Each work group
 //                     owns one 32 KB chunk of one row, holds it in registers, and
 //                     writes the chunk's (max, sum of 2^y, sum of 2^y*y, argmax) with
-//                     y = l*log2(e) - max*log2(e). 16-byte loads, all issued before
-//                     the first use, give 32 KB in flight per work group.
-//   sampler_finalize  one work group per row: merges the chunk statistics in chunk
-//                     order, writes max, sum, entropy, confidence and argmax, then
-//                     draws the candidate by inverse CDF - walk the chunk masses to
-//                     the chunk holding u*Z, re-read that one chunk (vector loads, a
-//                     block prefix scan). The last row of a request to finish (an
-//                     atomic count per request) then runs the request's selection:
-//                     rank sort by confidence, exact integer prefix sum of entropies,
-//                     budget cut, canvas update and convergence bookkeeping.
+//                     y = l*log2(e) - max*log2(e), plus 32 sub-chunk masses (one per
+//                     wave and 16-byte load: 64 * 16 contiguous bytes each). 16-byte
+//                     loads, all issued before the first use, give 32 KB in flight
+//                     per work group. Optionally it writes w = 2^y (block-scaled
+//                     probabilities for self-conditioning).
+//   sampler_finalize  one wave per row: merges the chunk statistics in chunk order,
+//                     writes max, sum, entropy, confidence and argmax, then draws the
+//                     candidate by inverse CDF at u*Z - a wave prefix scan over the
+//                     chunk masses, then over the chosen chunk's sub-chunk masses,
+//                     then over one re-read 16-byte vector per lane.
+//   sampler_select    one work group per request: rank sort by confidence, exact
+//                     integer prefix sum of entropies, budget cut, canvas update and
+//                     convergence bookkeeping.
 //   sampler_init      start of a block: random canvas, state reset.
 //
 // What these compute is stated in [P1] ("DiffusionGemma: vLLM에서 네이티브로 처음
@@ -30,6 +35,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLoads = 8;  // 16-byte loads per thread per chunk
+constexpr int kWaves = kThreads / 64;
+constexpr int kSubs = kLoads * kWaves;  // sub-chunks per chunk: one per (load, wave)
 constexpr int kPerThread = DG_MAX_CANVAS / kThreads;  // canvas positions per thread in the selection
 
 struct ReqTable {
@@ -160,13 +167,15 @@ __device__ __forceinline__ int block_min_int(int v, int* red) {
 template <bool kBf16, bool kStore, bool kTail>
 __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restrict__ logits, int64_t ld, int V,
                                                             int chunk, int num_chunks, int nfull,
-                                                            float4* __restrict__ stats, void* __restrict__ probs,
-                                                            int64_t ldq, int* __restrict__ counters, int num_reqs) {
+                                                            float4* __restrict__ stats, float* __restrict__ sub,
+                                                            void* __restrict__ probs, int64_t ldq) {
   using VT = Vec<kBf16>;
   __shared__ float redf[kThreads / 64];
   __shared__ int redi[kThreads / 64];
-  const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid < num_reqs) counters[tid] = 0;  // finalize counts finished rows per request
+  const int tid = threadIdx.x, lane = tid & 63;
+  // sub-chunk (load i, wave w) holds elements c0 + (i * kThreads + 64 w) * n + [0, 64 n)
+  float* subp = sub + (((int64_t)(kTail ? blockIdx.x : blockIdx.x / nfull) * num_chunks +
+                        (kTail ? num_chunks - 1 : blockIdx.x % nfull)) * kWaves + (tid >> 6)) * kLoads;
   const int c = kTail ? num_chunks - 1 : blockIdx.x % nfull;
   const int row = kTail ? blockIdx.x : blockIdx.x / nfull;
   const char* rowp = reinterpret_cast<const char*>(logits) + (int64_t)row * ld * (kBf16 ? 2 : 4);
@@ -188,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
   const float m = block_max(mx, redf);
   if (m == kNegInf) {  // chunk without a finite logit carries no mass
     if (tid == 0) stats[(int64_t)row * num_chunks + c] = make_float4(kNegInf, 0.f, 0.f, __int_as_float(INT_MAX));
+    subp[lane >> 3] = 0.f;
     if (kStore) {
       char* qrow = reinterpret_cast<char*>(probs) + (int64_t)row * ldq * (kBf16 ? 2 : 4);
       for (int i = 0; i < kLoads; ++i)
@@ -203,18 +213,21 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
   }
   const float nm2 = -m * kLog2e;
   float z = 0.f, t = 0.f;
+  float zl[kLoads];  // this lane's mass in each load
   int first = INT_MAX;
   // With kStore the pass also writes w = 2^y of the chunk (block-scaled probabilities).
   char* qrow = kStore ? reinterpret_cast<char*>(probs) + (int64_t)row * ldq * (kBf16 ? 2 : 4) : nullptr;
 #pragma unroll
   for (int i = kLoads - 1; i >= 0; --i) {
     float wl[VT::n];
+    zl[i] = 0.f;
 #pragma unroll
     for (int e = VT::n - 1; e >= 0; --e) {
       const float v = VT::get(buf[i], e);
       const float y = fmaxf(fmaf(v, kLog2e, nm2), -200.f);  // clamp keeps 0 * y finite for -inf logits
       const float w = fast_exp2(y);
       wl[e] = w;
+      zl[i] += w;
       z += w;
       t = fmaf(w, y, t);
       if (v == m) first = c0 + (i * kThreads + tid) * VT::n + e;  // ends at the lowest index
@@ -238,6 +251,22 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
       __builtin_amdgcn_sched_barrier(0);  // keep one 16-byte group's values live at a time
     }
   }
+  // sub-chunk masses: sum each load's values over the wave by halving exchanges
+  // (xor 32 keeps 4 of the 8 sums, xor 16 keeps 2, xor 8 keeps 1, then xor 4/2/1
+  // finish), after which lane 8i holds the sum of load i
+  {
+    float k4[4], k2[2], k1;
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) k4[k] = (b5 ? zl[k + 4] : zl[k]) + __shfl_xor(b5 ? zl[k] : zl[k + 4], 32, 64);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) k2[k] = (b4 ? k4[k + 2] : k4[k]) + __shfl_xor(b4 ? k4[k] : k4[k + 2], 16, 64);
+    k1 = (b3 ? k2[1] : k2[0]) + __shfl_xor(b3 ? k2[0] : k2[1], 8, 64);
+    k1 += __shfl_xor(k1, 4, 64);
+    k1 += __shfl_xor(k1, 2, 64);
+    k1 += __shfl_xor(k1, 1, 64);
+    subp[lane >> 3] = k1;  // the 8 lanes of a group hold the same sum (a branch here costs registers)
+  }
   const float zs = block_sum(z, redf);
   const float ts = block_sum(t, redf);
   const int am = block_min_int(first, redi);
@@ -259,7 +288,6 @@ struct RowOut {
   uint8_t* accept;
   int *canvas, *prev_argmax, *stable_count, *num_accepted, *converged;
   float* mean_entropy;
-  int* counters;
 };
 
 __device__ __forceinline__ int renoise_token(uint64_t seed, int step, int j, int stream, int vocab) {
@@ -267,30 +295,54 @@ __device__ __forceinline__ int renoise_token(uint64_t seed, int step, int j, int
   return (int)(((x >> 32) * (uint64_t)vocab) >> 32);
 }
 
+// Exclusive prefix sum of int64 values over the block in thread order.
+__device__ __forceinline__ long long block_exclusive_scan_ll(long long v, long long* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  long long x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  long long off = 0;
+  for (int i = 0; i < w; ++i) off += red[i];
+  return off + x - v;
+}
+
 // Selection for request r by one work group of kThreads: rank sort by (confidence
 // desc, position asc), exact integer prefix sum of floor(H * 2^40), budget cut, canvas
-// update and convergence bookkeeping. Positions j = tid + kThreads * q.
+// update and convergence bookkeeping. Every input is loaded up front.
 __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& sp, const RowOut& o) {
   __shared__ float key[DG_MAX_CANVAS];
   __shared__ long long sorted[DG_MAX_CANVAS];
-  __shared__ long long wred[kThreads / 64];
-  __shared__ int ired[kThreads / 64];
-  __shared__ long long chunk_tot[kThreads];
+  __shared__ long long wred[kWaves];
+  __shared__ int ired[kWaves];
+  __shared__ int conv_flag;
   const int tid = threadIdx.x;
   const int n = reqs.num_rows[r], step = reqs.step[r], row0 = reqs.row_start[r];
   const uint64_t seed = reqs.seed[r];
   float c[kPerThread];
   long long fx[kPerThread];
+  int am[kPerThread], cand[kPerThread], old[kPerThread];
   long long sum = 0;
+  int same = 1;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int j = tid + kThreads * q;
     c[q] = kNegInf;
     fx[q] = 0;
+    am[q] = cand[q] = old[q] = 0;
     if (j < n) {
       const float h = o.entropy[row0 + j];
       c[q] = sp.conf_mode == DG_CONF_NEG_ENTROPY ? -h : o.conf[row0 + j];
       fx[q] = (long long)floor((double)h * 0x1p40);  // exact: h * 2^40 is exact in double
+      am[q] = o.argmax[row0 + j];
+      same &= am[q] == o.prev_argmax[row0 + j];
+      cand[q] = o.cand[row0 + j];
+      old[q] = o.canvas[row0 + j];
       sum += fx[q];
       key[j] = c[q];
     }
@@ -312,7 +364,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
     }
   }
   __syncthreads();
-  // inclusive scan of sorted[0, n): each thread owns 4 consecutive ranks
+  // inclusive scan of sorted[0, n): each thread owns kPerThread consecutive ranks
   long long part[kPerThread];
   long long run = 0;
 #pragma unroll
@@ -321,10 +373,8 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
     run += i < n ? sorted[i] : 0;
     part[q] = run;
   }
-  chunk_tot[tid] = run;
-  __syncthreads();
-  long long off = 0;
-  for (int t = 0; t < tid; ++t) off += chunk_tot[t];
+  const long long off = block_exclusive_scan_ll(run, wred);
+  __syncthreads();  // every thread has read sorted[] before it is overwritten
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int i = tid * kPerThread + q;
@@ -333,18 +383,16 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
   __syncthreads();
   const long long limit = (long long)floor((double)sp.budget * 0x1p40);
   bool acc[kPerThread];
-  int cnt = 0, same = 1;
+  int cnt = 0;
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int j = tid + kThreads * q;
     acc[q] = j < n && (sorted[rank[q]] <= limit || rank[q] < sp.min_accept);
     cnt += acc[q];
-    if (j < n) same &= o.argmax[row0 + j] == o.prev_argmax[row0 + j];
   }
   const long long total = block_sum_ll(sum, wred);
   const int count = (int)block_sum_ll(cnt, wred);
-  const int all_same = -block_max_int(-same, ired) ;  // min over threads
-  __shared__ int conv_flag;
+  const int all_same = -block_max_int(-same, ired);  // min over threads
   if (tid == 0) {
     const int stable = (step > 0 && all_same) ? o.stable_count[r] + 1 : 0;
     const long long thr = (long long)ceil((double)sp.tau * (double)n * 0x1p40);
@@ -364,40 +412,40 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
     const int j = tid + kThreads * q;
     if (j >= n) continue;
     const int row = row0 + j;
-    const int am = o.argmax[row];
     int tok;
-    if (acc[q]) tok = o.cand[row];
-    else if (conv_flag) tok = am;
+    if (acc[q]) tok = cand[q];
+    else if (conv_flag) tok = am[q];
     else if (sp.renoise) tok = renoise_token(seed, step, j, 1, sp.vocab);
-    else tok = o.canvas[row];
+    else tok = old[q];
     o.canvas[row] = tok;
     o.accept[row] = acc[q];
-    o.prev_argmax[row] = am;
+    o.prev_argmax[row] = am[q];
   }
 }
 
+// One wave per row (kWaves rows per work group, no barriers).
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restrict__ logits, int64_t ld, int V,
-                                                             int chunk, int num_chunks,
-                                                             const float4* __restrict__ stats, ReqTable reqs,
+                                                             int chunk, int num_chunks, int num_rows,
+                                                             const float4* __restrict__ stats,
+                                                             const float* __restrict__ sub, ReqTable reqs,
                                                              SelectParams sp, RowOut o) {
   using VT = Vec<kBf16>;
-  __shared__ float redf[kThreads / 64];
-  __shared__ int redi[kThreads / 64];
-  __shared__ float mass[1024];
-  __shared__ int pick_chunk, fallback, is_last;
-  __shared__ float before;
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ float mass_s[kWaves][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * kWaves + wave;
+  if (row >= num_rows) return;
+  float* mass = mass_s[wave];
   const float4* st = stats + (int64_t)row * num_chunks;
 
-  // merge the chunk statistics in chunk order
+  // merge the chunk statistics (lane c, c + 64, ... in order)
   float mx = kNegInf;
-  for (int c = tid; c < num_chunks; c += kThreads) mx = fmaxf(mx, st[c].x);
-  const float m = block_max(mx, redf);
+  for (int c = lane; c < num_chunks; c += 64) mx = fmaxf(mx, st[c].x);
+  const float m = wave_max(mx);
   const float nm2 = -m * kLog2e;
   float z = 0.f, t = 0.f;
   int am = INT_MAX;
-  for (int c = tid; c < num_chunks; c += kThreads) {
+  for (int c = lane; c < num_chunks; c += 64) {
     const float4 s = st[c];
     float mc = 0.f;
     if (s.x != kNegInf) {
@@ -410,21 +458,21 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restr
     }
     mass[c] = mc;
   }
-  const float Z = block_sum(z, redf);
-  const float T = block_sum(t, redf);
-  const int amax = block_min_int(am, redi);
+  const float Z = wave_sum(z);
+  const float T = wave_sum(t);
+  const int amax = wave_min_int(am);
   if (o.probs_scale) {
     // p = w * 2^(chunk offset) / Z: one scale per DG_PROB_BLOCK entries (a chunk spans
     // chunk / DG_PROB_BLOCK blocks, all with the chunk's scale)
     const int per = chunk / DG_PROB_BLOCK;
     const int nblocks = (V + DG_PROB_BLOCK - 1) / DG_PROB_BLOCK;
     const float invz = 1.f / Z;
-    for (int c = tid; c < num_chunks; c += kThreads) {
+    for (int c = lane; c < num_chunks; c += 64) {
       const float sc = mass[c] > 0.f ? mass[c] / st[c].y * invz : 0.f;
       for (int b = c * per; b < min(nblocks, (c + 1) * per); ++b) o.probs_scale[(int64_t)row * nblocks + b] = sc;
     }
   }
-  if (tid == 0) {
+  if (lane == 0) {
     // entropy in nats: ln Z - (sum p*y) * ln 2, with y the log2-scaled logit offsets
     const double h = (double)kLn2 * (log2((double)Z) - (double)T / (double)Z);
     const float H = fmaxf(0.f, (float)h);
@@ -445,72 +493,90 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restr
   for (int i = 0; i < reqs.n; ++i)
     if (row >= reqs.row_start[i] && row < reqs.row_start[i] + reqs.num_rows[i]) r = i;
   if (r < 0) {
-    if (tid == 0) o.cand[row] = -1;
+    if (lane == 0) o.cand[row] = -1;
     return;
   }
-  // candidate: inverse CDF at u*Z; walk the chunk masses, then re-read one chunk
+  // candidate: the first token whose cumulative mass exceeds u*Z. Rounding can leave
+  // u*Z past the mass a level sums to; then the last token with mass is taken.
   const int j = row - reqs.row_start[r];
   const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)reqs.step[r], (uint64_t)j, 0);
   const float u = (float)(x0 >> 40) * 0x1p-24f;
   const float target = u * Z;
-  __syncthreads();  // mass[] complete
-  if (tid == 0) {
-    float cum = 0.f;
-    int pc = -1, last = 0;
-    for (int c = 0; c < num_chunks; ++c) {
-      if (mass[c] > 0.f) last = c;
-      if (pc < 0 && cum + mass[c] > target) { pc = c; break; }
-      cum += mass[c];
+  // level 1: chunks
+  float carry = 0.f, rem = 0.f;
+  int pc = -1, last = 0;
+  for (int base = 0; base < num_chunks; base += 64) {
+    const int c = base + lane;
+    const float mc = c < num_chunks ? mass[c] : 0.f;
+    const float incl = wave_incl_scan(mc);
+    const uint64_t pos = __ballot(mc > 0.f);
+    if (pos) last = base + 63 - __clzll(pos);
+    const uint64_t hit = __ballot(carry + incl > target);
+    if (hit) {
+      const int k = __ffsll((long long)hit) - 1;
+      pc = base + k;
+      rem = target - (carry + __shfl(wave_shift_up(incl), k, 64));
+      break;
     }
-    fallback = pc < 0;
-    pick_chunk = pc < 0 ? last : pc;
-    before = cum;
+    carry += __shfl(incl, 63, 64);
   }
-  __syncthreads();
-  // thread tid owns the contiguous run [e0, e0 + per) of the chosen chunk: 8 x 16 bytes
-  constexpr int per = kLoads * VT::n;
-  const int e0 = pick_chunk * chunk + tid * per;
+  bool fallback = pc < 0;
+  if (fallback) pc = last;
+  // level 2: the chunk's sub-chunks, in the row's reference
+  const float fch = st[pc].x == kNegInf ? 0.f : fast_exp2(nm2 + st[pc].x * kLog2e);
+  const float* subp = sub + ((int64_t)row * num_chunks + pc) * kSubs;
+  const int si = lane >> 2, sw = lane & 3;  // lane s < 32 takes sub-chunk s = 4 i + w
+  const float sm = lane < kSubs ? subp[sw * kLoads + si] * fch : 0.f;
+  const float sincl = wave_incl_scan(sm);
+  const uint64_t spos = __ballot(sm > 0.f);
+  const uint64_t shit = fallback ? 0 : __ballot(sincl > rem);
+  int ps;
+  if (shit) {
+    ps = __ffsll((long long)shit) - 1;
+    rem -= __shfl(wave_shift_up(sincl), ps, 64);
+  } else {
+    fallback = true;
+    ps = spos ? 63 - __clzll(spos) : 0;
+  }
+  // level 3: one 16-byte vector per lane of that sub-chunk
+  const int e0 = pc * chunk + ((ps >> 2) * kThreads + (ps & 3) * 64 + lane) * VT::n;
   const char* rowp = reinterpret_cast<const char*>(logits) + (int64_t)row * ld * (kBf16 ? 2 : 4);
-  float w[per];
+  const uint4 v = load_vec<kBf16>(rowp, e0, V);
+  float w[VT::n];
   float seg = 0.f;
   int last_pos = -1;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const uint4 v = load_vec<kBf16>(rowp, e0 + i * VT::n, V);
-#pragma unroll
-    for (int e = 0; e < VT::n; ++e) {
-      const float x = fast_exp2(fmaf(VT::get(v, e), kLog2e, nm2));
-      w[i * VT::n + e] = x;
-      seg += x;
-      if (x > 0.f) last_pos = e0 + i * VT::n + e;
-    }
+  for (int e = 0; e < VT::n; ++e) {
+    w[e] = fast_exp2(fmaf(VT::get(v, e), kLog2e, nm2));
+    seg += w[e];
+    if (w[e] > 0.f) last_pos = e0 + e;
   }
-  const float pre = block_exclusive_scan(seg, redf);
-  const float rem = target - before;
-  const bool hit = !fallback && pre + seg > rem;
-  const int first_hit = block_min_int(hit ? tid : INT_MAX, redi);
-  if (first_hit == INT_MAX) {  // rounding left u*Z past the re-read mass: last token with mass
-    const int lp = block_max_int(last_pos, redi);
-    if (tid == 0) o.cand[row] = lp;
-  } else if (tid == first_hit) {
-    float acc = pre;
-    int got = last_pos;
+  const float lincl = wave_incl_scan(seg);
+  const float lexcl = wave_shift_up(lincl);
+  const uint64_t lhit = fallback ? 0 : __ballot(lincl > rem);
+  if (lhit) {
+    const int k = __ffsll((long long)lhit) - 1;
+    if (lane == k) {
+      float acc = lexcl;
+      int got = last_pos;
 #pragma unroll
-    for (int e = 0; e < per; ++e) {
-      acc += w[e];
-      if (acc > rem) { got = e0 + e; break; }
+      for (int e = 0; e < VT::n; ++e) {
+        acc += w[e];
+        if (acc > rem) {
+          got = e0 + e;
+          break;
+        }
+      }
+      o.cand[row] = got;
     }
-    o.cand[row] = got;
+  } else {
+    const int lp = wave_max_int(last_pos);
+    if (lane == 0) o.cand[row] = lp;
   }
+}
 
-  // the last finished row of the request runs its selection
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&o.counters[r], 1) == reqs.num_rows[r] - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  select_request(r, reqs, sp, o);
+__global__ __launch_bounds__(kThreads) void sampler_select(ReqTable reqs, SelectParams sp, RowOut o) {
+  select_request(blockIdx.x, reqs, sp, o);
 }
 
 // Start of a block: a uniform random canvas (Philox stream 2), state reset.
@@ -543,9 +609,9 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
     t.seed[i] = a->reqs[i].seed;
   }
   float4* stats = reinterpret_cast<float4*>(a->workspace);
+  float* sub = reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + plan.sub_offset);
   RowOut o{a->entropy, a->conf, a->row_max, a->row_sum, a->argmax, a->cand, a->probs_scale, a->accept, a->canvas,
-           a->prev_argmax, a->stable_count, a->num_accepted, a->converged, a->mean_entropy,
-           reinterpret_cast<int*>(reinterpret_cast<char*>(a->workspace) + plan.counter_offset)};
+           a->prev_argmax, a->stable_count, a->num_accepted, a->converged, a->mean_entropy};
   if (a->flags & DG_INIT_CANVAS) {
     hipLaunchKernelGGL(sampler_init, dim3(a->num_reqs), dim3(kThreads), 0, s, t, a->vocab, o);
     return (int)hipGetLastError();
@@ -555,27 +621,29 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
   const int nfull = a->vocab / plan.chunk;
   const bool tail = nfull < plan.num_chunks;
   const dim3 gfull((unsigned)nfull * a->num_rows), gtail(a->num_rows), blk(kThreads);
-#define DG_ROWPASS(BF, ST)                                                                                     \
-  do {                                                                                                         \
-    if (nfull)                                                                                                 \
-      hipLaunchKernelGGL((sampler_rowpass<BF, ST, false>), gfull, blk, 0, s, a->logits, a->ld, a->vocab,      \
-                         plan.chunk, plan.num_chunks, nfull, stats, a->probs, a->ldq, o.counters, a->num_reqs); \
-    if (tail)                                                                                                  \
-      hipLaunchKernelGGL((sampler_rowpass<BF, ST, true>), gtail, blk, 0, s, a->logits, a->ld, a->vocab,       \
-                         plan.chunk, plan.num_chunks, nfull, stats, a->probs, a->ldq, o.counters, a->num_reqs); \
+  const dim3 gfin((unsigned)((a->num_rows + kWaves - 1) / kWaves));
+#define DG_ROWPASS(BF, ST)                                                                                \
+  do {                                                                                                    \
+    if (nfull)                                                                                            \
+      hipLaunchKernelGGL((sampler_rowpass<BF, ST, false>), gfull, blk, 0, s, a->logits, a->ld, a->vocab, \
+                         plan.chunk, plan.num_chunks, nfull, stats, sub, a->probs, a->ldq);              \
+    if (tail)                                                                                             \
+      hipLaunchKernelGGL((sampler_rowpass<BF, ST, true>), gtail, blk, 0, s, a->logits, a->ld, a->vocab,  \
+                         plan.chunk, plan.num_chunks, nfull, stats, sub, a->probs, a->ldq);              \
   } while (0)
   if (a->dtype == DG_BF16) {
     if (a->probs) DG_ROWPASS(true, true);
     else DG_ROWPASS(true, false);
-    hipLaunchKernelGGL(sampler_finalize<true>, dim3(a->num_rows), blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk,
-                       plan.num_chunks, stats, t, sp, o);
+    hipLaunchKernelGGL(sampler_finalize<true>, gfin, blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk, plan.num_chunks,
+                       a->num_rows, stats, sub, t, sp, o);
   } else {
     if (a->probs) DG_ROWPASS(false, true);
     else DG_ROWPASS(false, false);
-    hipLaunchKernelGGL(sampler_finalize<false>, dim3(a->num_rows), blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk,
-                       plan.num_chunks, stats, t, sp, o);
+    hipLaunchKernelGGL(sampler_finalize<false>, gfin, blk, 0, s, a->logits, a->ld, a->vocab, plan.chunk,
+                       plan.num_chunks, a->num_rows, stats, sub, t, sp, o);
   }
 #undef DG_ROWPASS
+  hipLaunchKernelGGL(sampler_select, dim3(a->num_reqs), blk, 0, s, t, sp, o);
   return (int)hipGetLastError();
 }
 
