@@ -214,8 +214,11 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   const bool scaled = a->p_scale != nullptr;
   const bool fused = a->row_max != nullptr;
   plan->dma = a->dtype == DG_BF16 && a->V % 32 == 0;
-  plan->tile_m = 256;
-  plan->tile_n = 256;
+  // The DMA kernel's 128 x 512 tile spends less of its LDS ring on P (an L2-resident
+  // operand shared by the tile's neighbours) and more on E, the stream from HBM.
+  const bool wide = plan->dma && a->d % 512 == 0;
+  plan->tile_m = wide ? 128 : 256;
+  plan->tile_n = wide ? 512 : 256;
   plan->tile_k = plan->dma ? 32 : (a->dtype == DG_BF16 ? 64 : 32);
   plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
   plan->n_tiles = (int)ceil_div(a->d, plan->tile_n);
@@ -236,7 +239,7 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   plan->splits = (int)ceil_div(a->V, k_per_split);
   plan->k_per_split = (int)k_per_split;
   plan->part_offset = 0;
-  // partials in whole 256 x 256 tiles (MFMA register layout)
+  // partials in whole tiles (MFMA register layout)
   size_t bytes = plan->splits > 1 ? align_up((size_t)plan->splits * plan->m_tiles * plan->n_tiles *
                                              plan->tile_m * plan->tile_n * sizeof(float), 256) : 0;
   plan->p_offset = bytes;

@@ -3,19 +3,20 @@
 // 첫 번째 Diffusion LLM", section "안정성을 위한 셀프 컨디셔닝"; [P3] "DiffusionGemma u vLLM:
 // ...", section "Mehanizam odlučivanja o gotovim tokenima").
 //
-// Both GEMM kernels compute a 256 x 256 output tile per work group with 4 waves,
-// each 128 x 128 as 4 x 4 MFMA 32x32 blocks (256 accumulator registers per lane),
-// split-K over V with the work groups that share a K slice placed on one XCD so
-// their re-reads of it hit that XCD's L2. LDS rows are XOR-swizzled in 16-byte
-// chunks so staging writes and operand reads are free of bank conflicts.
+// Both GEMM kernels compute a 256 x 256 output tile per work group, split-K over V
+// with the work groups that share a K slice placed on one XCD so their re-reads of it
+// hit that XCD's L2. LDS rows are XOR-swizzled in 16-byte chunks so staging writes and
+// operand reads are free of bank conflicts.
 //
-//   selfcond_gemm_dma  bf16, V a multiple of 32: the P and E tiles go straight from
+//   selfcond_gemm_dma  bf16, V a multiple of 32; 8 waves, two per SIMD, each 64 x 128
+//                      as 2 x 4 MFMA 32x32 blocks. The P and E tiles go straight from
 //                      HBM to LDS (global_load_lds_dwordx4) through a 5-stage ring,
 //                      so four K steps are in flight with no register staging. E
 //                      stays row-major in LDS; its MFMA operand (8 consecutive k of one
 //                      column per lane) comes from two ds_read_b64_tr_b16 transposing
 //                      reads. One fence-free barrier per K step.
-//   selfcond_gemm_reg  general case (fp32, any V): tiles staged through registers
+//   selfcond_gemm_reg  general case (fp32, any V); 4 waves, each 128 x 128 as 4 x 4
+//                      blocks. Tiles are staged through registers
 //                      one K step ahead, E transposed in registers on its way to LDS;
 //                      in the logits mode P is rebuilt at LDS-store time.
 //   selfcond_normalize bf16 logits + row statistics -> probabilities, so the logits
@@ -87,39 +88,47 @@ template <> __device__ __forceinline__ uint4 to_prob<false>(uint4 v, float c) {
 // Split-K partials keep the MFMA register layout: per 256 x 256 tile, float4 q =
 // [wave][i][j][e/4][lane] holds acc[i][j][e/4*4 .. +3], so every store is a coalesced
 // 1 KB wave write; selfcond_reduce maps them back to rows and columns.
-__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[4][4], int split, int k_lo, int mt,
-                                           int nt, int wave, int lane, bool bf16) {
+// Epilogue of a BM x BN tile held as NI x 4 blocks of 32x32 per wave: the wave's rows
+// start at 32-row block `rb0`, its columns at 128-column group `ch`.
+// Split-K partials are stored in the accumulators' native order (so stores and the
+// reduce's reads are whole 16-byte vectors), with kCh = BN / 128:
+//   float4 index = (((rb * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane, holding rows
+//   32 rb + 8 e4 + 4 (lane / 32) + 0..3 of column 128 ch + 32 j + lane % 32.
+template <int BM, int BN, int NI>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI][4], int split, int k_lo, int mt,
+                                           int nt, int rb0, int ch, int lane, bool bf16) {
+  constexpr int kCh = BN / 128;
   const int h = lane >> 5, l32 = lane & 31;
-  const int m0 = mt * kBM, n0 = nt * kBN, wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int blk = k_lo / DG_PROB_BLOCK;
   auto scale = [&](int r) { return g.p_scale ? g.p_scale[(int64_t)min(r, g.M - 1) * g.nblocks + blk] : 1.f; };
   if (g.part) {
     float4* tile = reinterpret_cast<float4*>(g.part) +
-                   (((int64_t)split * g.m_tiles + mt) * g.n_tiles + nt) * (kBM * kBN / 4);
+                   (((int64_t)split * g.m_tiles + mt) * g.n_tiles + nt) * (BM * BN / 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int r = m0 + wm + 32 * i + 8 * e4 + 4 * h;  // rows r .. r+3
+        const int r = m0 + 32 * (rb0 + i) + 8 * e4 + 4 * h;  // rows r .. r+3
         const float s0 = scale(r), s1 = scale(r + 1), s2 = scale(r + 2), s3 = scale(r + 3);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          tile[(((wave * 4 + i) * 4 + j) * 4 + e4) * 64 + lane] =
+          tile[((((rb0 + i) * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane] =
               make_float4(acc[i][j][4 * e4] * s0, acc[i][j][4 * e4 + 1] * s1, acc[i][j][4 * e4 + 2] * s2,
                           acc[i][j][4 * e4 + 3] * s3);
       }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int r = m0 + 32 * (rb0 + i) + 8 * (e >> 2) + 4 * h + (e & 3);
       if (r >= g.M) continue;
       const float sr = scale(r);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = n0 + wn + 32 * j + l32;
+        const int c = n0 + 128 * ch + 32 * j + l32;
         if (c >= g.d) continue;
         const float v = acc[i][j][e] * sr;
         if (bf16) reinterpret_cast<__bf16*>(g.out)[(int64_t)r * g.ldo + c] = (__bf16)v;
@@ -132,6 +141,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[4]
 struct TileIdx {
   int split, mt, nt, m0, n0, k_lo, k_hi;
 };
+template <int BM, int BN>
 __device__ __forceinline__ TileIdx tile_index(const GemmArgs& g) {
   const int nwg = gridDim.x;
   int L = blockIdx.x;
@@ -141,8 +151,8 @@ __device__ __forceinline__ TileIdx tile_index(const GemmArgs& g) {
   t.split = L / per_split;
   t.mt = (L % per_split) / g.n_tiles;
   t.nt = L % g.n_tiles;
-  t.m0 = t.mt * kBM;
-  t.n0 = t.nt * kBN;
+  t.m0 = t.mt * BM;
+  t.n0 = t.nt * BN;
   t.k_lo = t.split * g.k_per_split;
   t.k_hi = min(g.V, t.k_lo + g.k_per_split);
   return t;
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char lds_a[2][kBM * kRow];
   __shared__ __attribute__((aligned(16))) char lds_b[2][kBN * kRow];
 
-  const TileIdx ti = tile_index(g);
+  const TileIdx ti = tile_index<kBM, kBN>(g);
   const int m0 = ti.m0, n0 = ti.n0, k_lo = ti.k_lo, k_hi = ti.k_hi;
   const int nsteps = (k_hi - k_lo + BK - 1) / BK;
 
@@ -351,18 +361,13 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     }
   }
 
-  store_tile(g, acc, ti.split, k_lo, ti.mt, ti.nt, wave, lane, kBf16);
+  store_tile<kBM, kBN, 4>(g, acc, ti.split, k_lo, ti.mt, ti.nt, (wave >> 1) * 4, wave & 1, lane, kBf16);
 }
 
 
 // ---- LDS-DMA kernel (bf16) -------------------------------------------------------
 
-constexpr int kDmaStages = 5;            // LDS ring depth: 4 K steps in flight (160 KB)
-constexpr int kDmaBK = 32;               // k per step
-constexpr int kStageA = kBM * 64;        // 256 rows x 32 bf16
-constexpr int kStageB = kDmaBK * 512;    // 32 k rows x 256 bf16
-constexpr int kStageBytes = kStageA + kStageB;
-
+constexpr int kDmaBK = 32;  // k per step
 // s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt left open).
 #define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // s_waitcnt for all LDS reads of this wave (vmcnt left open).
@@ -386,41 +391,70 @@ __device__ __forceinline__ uint2 lds_read_tr16(uint32_t addr) {
   return r;
 }
 
-// A stage: row r (0..255) holds 32 bf16 = 4 chunks; chunk c sits at c ^ swa(r).
-// B stage: k row kk (0..31) holds 256 bf16 = 32 chunks; chunk c sits at c ^ swb(kk).
+// A stage: row r (0..BM-1) holds 32 bf16 = 4 chunks; chunk c sits at c ^ swa(r).
+// B stage: k row kk (0..31) holds BN bf16 = BN/8 chunks; chunk c sits at c ^ swb(kk).
 // The XOR masks keep the operand reads (ds_read_b128 over 32 rows; ds_read_b64_tr_b16
 // over 4 k rows x 32 columns) free of bank conflicts with 64 banks of 4 bytes and with
 // 32; the DMA writes are contiguous 1 KB runs either way.
 __device__ __forceinline__ int swa(int r) { return ((r >> 1) & 3) ^ (((r >> 3) & 1) * 3); }
 __device__ __forceinline__ int swb(int kk) { return ((kk & 1) * 4) ^ (((kk >> 1) & 1) * 10); }
 __device__ __forceinline__ uint32_t a_off(int r, int c) { return r * 64 + ((c ^ swa(r)) << 4); }
-__device__ __forceinline__ uint32_t b_off(int kk, int c) { return kStageA + kk * 512 + ((c ^ swb(kk)) << 4); }
 
-__global__ __launch_bounds__(kThreads) void selfcond_gemm_dma(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) char lds[kDmaStages][kStageBytes];
-  const TileIdx ti = tile_index(g);
+// 8 waves (two per SIMD, so one wave's LDS waits and barriers overlap the other's
+// MFMAs), each 64 x 128 as 2 x 4 MFMA blocks of 32x32 (128 accumulators), over a
+// BM x BN tile: 256 x 256 (5-stage ring), or 128 x 512 (4-stage ring) whose stages
+// hold 8 KB of P and 32 KB of E, so more of E - the stream from HBM - is in flight.
+constexpr int kDmaThreads = 512;
+constexpr int kDmaWaves = kDmaThreads / 64;
+
+template <int BN>
+struct DmaTile {
+  static constexpr int BM = 65536 / BN;
+  static constexpr int kWN = BN / 128;                 // waves along N
+  static constexpr int kStageA = BM * 64;              // BM rows x 32 bf16
+  static constexpr int kRowB = BN * 2;                 // bytes per B k row
+  static constexpr int kStageB = kDmaBK * kRowB;
+  static constexpr int kStageBytes = kStageA + kStageB;
+  static constexpr int kStages = 163840 / kStageBytes;  // 5 or 4
+  static constexpr int kSegA = kStageA / 1024 / kDmaWaves;  // 1 KB DMA segments per wave
+  static constexpr int kSegB = kStageB / 1024 / kDmaWaves;
+  static constexpr int kRowsPerSegB = 1024 / kRowB;    // k rows per B segment (2 or 1)
+};
+
+template <int BN>
+__global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
+  using T = DmaTile<BN>;
+  constexpr int BM = T::BM, kStages = T::kStages, kStageA = T::kStageA, kStageBytes = T::kStageBytes;
+  constexpr int kSegA = T::kSegA, kSegB = T::kSegB;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages][kStageBytes];
+  const TileIdx ti = tile_index<BM, BN>(g);
   const int nsteps = (ti.k_hi - ti.k_lo) / kDmaBK;  // K range is a multiple of 32
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave / T::kWN) * 64, wn = (wave % T::kWN) * 128;
 
-  // Per-lane DMA sources. Each wave fills segments 4*wave .. 4*wave+3 of both the A
-  // and the B region (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the
-  // lane fetches the chunk that the swizzle puts in its slot. Rows past M and columns
-  // past d are clamped to valid memory; their results are never stored.
-  const char* psrc[4];
-  const char* esrc[4];
+  // Per-lane DMA sources. Wave w fills A segments kSegA*w .. and B segments kSegB*w ..
+  // (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the lane fetches the
+  // chunk that the swizzle puts in its slot. Rows past M and columns past d are
+  // clamped to valid memory; their results are never stored.
+  const char* psrc[kSegA];
+  const char* esrc[kSegB];
   const char* pb = reinterpret_cast<const char*>(g.p);
   const char* eb = reinterpret_cast<const char*>(g.e);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int seg = 4 * wave + t;
+  for (int t = 0; t < kSegA; ++t) {
+    const int seg = kSegA * wave + t;
     const int r = seg * 16 + (lane >> 2);         // A row within the tile
     const int ca = (lane & 3) ^ swa(r);           // logical chunk stored in this slot
     const int grow = min(ti.m0 + r, g.M - 1);
     psrc[t] = pb + ((int64_t)grow * g.ldp + ti.k_lo + ca * 8) * 2;
-    const int kk = seg * 2 + (lane >> 5);         // B k row within the step
-    const int cb = (lane & 31) ^ swb(kk);
+  }
+#pragma unroll
+  for (int t = 0; t < kSegB; ++t) {
+    const int seg = kSegB * wave + t;
+    const int kk = seg * T::kRowsPerSegB + (T::kRowsPerSegB == 2 ? (lane >> 5) : 0);  // B k row
+    const int cb = (T::kRowsPerSegB == 2 ? (lane & 31) : lane) ^ swb(kk);
     const int gcol = min(ti.n0 + cb * 8, g.d - 8);
     esrc[t] = eb + ((int64_t)(ti.k_lo + kk) * g.lde + gcol) * 2;
   }
@@ -430,21 +464,23 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_dma(GemmArgs g) {
   const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
 
   auto issue = [&](int s) {
-    __attribute__((address_space(3))) char* st = lds0 + (s % kDmaStages) * kStageBytes;
+    __attribute__((address_space(3))) char* st = lds0 + (s % kStages) * kStageBytes;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kSegA; ++t)
       __builtin_amdgcn_global_load_lds((const void*)(psrc[t] + s * pstep),
-                                       (__attribute__((address_space(3))) void*)(st + (4 * wave + t) * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(st + (kSegA * wave + t) * 1024), 16, 0,
+                                       0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kSegB; ++t)
       __builtin_amdgcn_global_load_lds((const void*)(esrc[t] + s * estep),
-                                       (__attribute__((address_space(3))) void*)(st + kStageA + (4 * wave + t) * 1024),
+                                       (__attribute__((address_space(3))) void*)(st + kStageA + (kSegB * wave + t) * 1024),
                                        16, 0, 0);
   };
+  constexpr int kGroup = kSegA + kSegB;  // DMA instructions per stage per wave
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -456,42 +492,38 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_dma(GemmArgs g) {
   const int brow = 8 * (grp >> 1) + (s16 >> 2);
   const int bcol = 16 * (grp & 1) + 4 * (s16 & 3);  // + wn + 32j
 
-  // One half step = 16 k: A fragments of 4 row blocks, B fragments of 4 column blocks
-  // (two transposing reads of 4 k rows each). The 12 LDS reads of the next half step
-  // are interleaved with the 16 MFMAs of the current one, one read after each MFMA
-  // (sched_barrier pins the order), so every read issues while an MFMA executes.
+  // One half step = 16 k: A fragments of 2 row blocks, B fragments of 4 column blocks
+  // (two transposing reads of 4 k rows each). The 10 LDS reads of the next half step
+  // are interleaved with the 8 MFMAs of the current one (sched_barrier pins the order).
   auto a_addr = [&](uint32_t st, int ks, int i) { return st + a_off(wm + 32 * i + l32, 2 * ks + h); };
   auto b_addr = [&](uint32_t st, int ks, int j, int q) {
     const int col = wn + 32 * j + bcol;
-    return st + b_off(16 * ks + brow + 4 * q, col >> 3) + ((col & 7) << 1);
+    const int kk = 16 * ks + brow + 4 * q;
+    return st + kStageA + kk * T::kRowB + (((col >> 3) ^ swb(kk)) << 4) + ((col & 7) << 1);
   };
-  uint4 fa[2][4], fb[2][4];
+  uint4 fa[2][2], fb[2][4];
   auto read_half = [&](uint32_t st, int ks, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[buf][i] = lds_read_b128(a_addr(st, ks, i));
+    for (int i = 0; i < 2; ++i) fa[buf][i] = lds_read_b128(a_addr(st, ks, i));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint2 lo = lds_read_tr16(b_addr(st, ks, j, 0)), hi = lds_read_tr16(b_addr(st, ks, j, 1));
       fb[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
-  // MFMAs on fragment buffer `buf`; if `next_st` != ~0u, the reads of (next_st, next_ks)
-  // into the other buffer are interleaved (B reads first, since they are two each).
   auto mma_half = [&](int buf, uint32_t next_st, int next_ks) {
     const int nb = buf ^ 1;
     uint2 lo[4], hi[4];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < 8; ++t) {
       const int i = t >> 2, j = t & 3;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[buf][i]),
                                                           __builtin_bit_cast(bf16x8_t, fb[buf][j]), acc[i][j], 0, 0, 0);
       if (next_st != ~0u) {
-        if (t < 8) {
-          if (t & 1) hi[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 1));
-          else lo[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 0));
-        } else if (t < 12) {
-          fa[nb][t - 8] = lds_read_b128(a_addr(next_st, next_ks, t - 8));
-        }
+        if (t & 1) hi[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 1));
+        else lo[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 0));
+        if (t == 3) fa[nb][0] = lds_read_b128(a_addr(next_st, next_ks, 0));
+        if (t == 7) fa[nb][1] = lds_read_b128(a_addr(next_st, next_ks, 1));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -501,33 +533,41 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_dma(GemmArgs g) {
     }
   };
 
-  // Pipeline: the barrier that publishes step s+1 sits between the two halves of step
-  // s; a barrier also certifies that every wave is done reading the step two behind,
-  // whose ring slot the next DMA then refills.
-#pragma unroll
-  for (int t = 0; t < kDmaStages - 1; ++t)
-    if (t < nsteps) issue(t);
+  // Pipeline: step s's fragments are all in registers once the reads issued during
+  // its first half have landed, so its ring slot is refilled (with step s+kStages)
+  // right after the barrier that follows; the same barrier publishes step s+1.
+  // kStages-1 steps stay in flight while one is consumed.
+  const int pro = min(nsteps, kStages);
+  for (int t = 0; t < pro; ++t) issue(t);
   if (nsteps > 0) {
-    if (kDmaStages - 2 < nsteps) DG_WAIT_VM(8 * (kDmaStages - 2));
+    // step 0 has landed once at most the pro-1 groups issued after it remain
+    if (pro == 5) DG_WAIT_VM(kGroup * 4);
+    else if (pro == 4) DG_WAIT_VM(kGroup * 3);
+    else if (pro == 3) DG_WAIT_VM(kGroup * 2);
+    else if (pro == 2) DG_WAIT_VM(kGroup * 1);
     else DG_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     read_half(lbase, 0, 0);
   }
   for (int s = 0; s < nsteps; ++s) {
-    const uint32_t st = lbase + (s % kDmaStages) * kStageBytes;
+    const uint32_t st = lbase + (s % kStages) * kStageBytes;
     DG_WAIT_LGKM0();       // fragments of (s, 0) in buffer 0
     mma_half(0, st, 1);    // ... with the reads of (s, 1) into buffer 1
+    DG_WAIT_LGKM0();       // fragments of (s, 1) in buffer 1: this wave is done with slot s
     if (s + 1 < nsteps) {
-      // step s+1 has landed once at most the DMA groups issued after it remain
-      if (s + kDmaStages - 2 < nsteps) DG_WAIT_VM(8 * (kDmaStages - 3));
+      // step s+1 has landed once at most the groups issued after it (steps s+2 ..
+      // min(s+kStages-1, nsteps-1)) remain
+      const int after = min(kStages - 2, nsteps - 2 - s);
+      if (after >= 3) DG_WAIT_VM(kGroup * 3);
+      else if (after == 2) DG_WAIT_VM(kGroup * 2);
+      else if (after == 1) DG_WAIT_VM(kGroup * 1);
       else DG_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();
-      if (s + kDmaStages - 1 < nsteps) issue(s + kDmaStages - 1);
+      if (s + kStages < nsteps) issue(s + kStages);  // into slot s
     }
-    DG_WAIT_LGKM0();       // fragments of (s, 1) in buffer 1
-    mma_half(1, s + 1 < nsteps ? lbase + ((s + 1) % kDmaStages) * kStageBytes : ~0u, 0);
+    mma_half(1, s + 1 < nsteps ? lbase + ((s + 1) % kStages) * kStageBytes : ~0u, 0);
   }
-  store_tile(g, acc, ti.split, ti.k_lo, ti.mt, ti.nt, wave, lane, true);
+  store_tile<BM, BN, 2>(g, acc, ti.split, ti.k_lo, ti.mt, ti.nt, (wave / T::kWN) * 2, wave % T::kWN, lane, true);
 }
 
 // bf16 logits + row statistics -> probabilities p = 2^(l*log2e + c); 8 per thread.
@@ -549,8 +589,9 @@ __global__ __launch_bounds__(256) void selfcond_normalize(const uint16_t* __rest
 // Thread = one float4 of the MFMA-layout tile (4 consecutive rows of one column).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict__ part, int splits, int m_tiles,
-                                                       int n_tiles, int M, int d, void* __restrict__ out, int64_t ldo) {
-  constexpr int kTile4 = kBM * kBN / 4;
+                                                       int n_tiles, int tile_m, int tile_n, int M, int d,
+                                                       void* __restrict__ out, int64_t ldo) {
+  constexpr int kTile4 = 65536 / 4;  // every tile shape holds 64K values
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
   if (i >= per_split) return;
@@ -562,13 +603,14 @@ __global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict_
     s.z += v.z;
     s.w += v.w;
   }
-  // decode [tile][wave][i][j][e/4][lane] -> 4 rows r..r+3 of column c
+  // decode [tile][32-row block][128-column group][j][e/4][lane] -> rows r..r+3 of column c
   const int q = (int)(i % kTile4);
   const int64_t tile = i / kTile4;
   const int mt = (int)(tile / n_tiles), nt = (int)(tile % n_tiles);
-  const int lane = q & 63, e4 = (q >> 6) & 3, jj = (q >> 8) & 3, ii = (q >> 10) & 3, wave = q >> 12;
-  const int r = mt * kBM + (wave >> 1) * 128 + 32 * ii + 8 * e4 + 4 * (lane >> 5);
-  const int c = nt * kBN + (wave & 1) * 128 + 32 * jj + (lane & 31);
+  const int chs = tile_n / 128;
+  const int lane = q & 63, e4 = (q >> 6) & 3, jj = (q >> 8) & 3, ch = (q >> 10) % chs, rb = (q >> 10) / chs;
+  const int r = mt * tile_m + 32 * rb + 8 * e4 + 4 * (lane >> 5);
+  const int c = nt * tile_n + 128 * ch + 32 * jj + (lane & 31);
   if (c >= d) return;
   const float v[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
@@ -615,7 +657,8 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
       g.ldp = a->V;
       g.row_max = g.row_sum = nullptr;
     }
-    hipLaunchKernelGGL(selfcond_gemm_dma, grid, dim3(kThreads), 0, s, g);
+    if (plan.tile_n == 512) hipLaunchKernelGGL(selfcond_gemm_dma<512>, grid, dim3(kDmaThreads), 0, s, g);
+    else hipLaunchKernelGGL(selfcond_gemm_dma<256>, grid, dim3(kDmaThreads), 0, s, g);
   } else if (a->dtype == DG_BF16) {
     if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<true, true>), grid, dim3(kThreads), 0, s, g);
     else hipLaunchKernelGGL((selfcond_gemm_reg<true, false>), grid, dim3(kThreads), 0, s, g);
@@ -624,15 +667,15 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
     else hipLaunchKernelGGL((selfcond_gemm_reg<false, false>), grid, dim3(kThreads), 0, s, g);
   }
   if (plan.splits > 1) {
-    const int64_t n4 = (int64_t)plan.m_tiles * plan.n_tiles * (kBM * kBN / 4);
+    const int64_t n4 = (int64_t)plan.m_tiles * plan.n_tiles * (plan.tile_m * plan.tile_n / 4);
     const dim3 rg((unsigned)((n4 + 255) / 256));
     const float4* part = reinterpret_cast<const float4*>(g.part);
     if (a->dtype == DG_BF16)
       hipLaunchKernelGGL(selfcond_reduce<true>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles, plan.n_tiles,
-                         a->M, a->d, a->out, a->ldo);
+                         plan.tile_m, plan.tile_n, a->M, a->d, a->out, a->ldo);
     else
       hipLaunchKernelGGL(selfcond_reduce<false>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles, plan.n_tiles,
-                         a->M, a->d, a->out, a->ldo);
+                         plan.tile_m, plan.tile_n, a->M, a->d, a->out, a->ldo);
   }
   return (int)hipGetLastError();
 }

@@ -68,11 +68,12 @@ def test_config2_bf16_full_size_sampled_rows():
     assert err2 <= TOL
 
 
-@pytest.mark.parametrize("bf16,V", [(False, 3000), (True, 3000), (True, 3008)])
-def test_one_hot_bit_exact(bf16, V):
+@pytest.mark.parametrize("bf16,V,d", [(False, 3000, 256), (True, 3000, 256), (True, 3008, 256), (True, 3008, 1024)])
+def test_one_hot_bit_exact(bf16, V, d):
     """P-C1 on the GPU: one-hot rows return exactly the embedding row (V = 3008 takes
-    the LDS-DMA kernel, V = 3000 the register-staged one)."""
-    d, M = 256, 70
+    the LDS-DMA kernel - its 128 x 512 tile when d is a multiple of 512 - and V = 3000
+    the register-staged one)."""
+    M = 70
     E = embed_table(9, V, d, bf16=bf16)
     rng = np.random.default_rng(1)
     hot = rng.integers(0, V, M)
@@ -85,7 +86,7 @@ def test_one_hot_bit_exact(bf16, V):
 
 
 @pytest.mark.parametrize("bf16,M,V,d", [(True, 130, 1000, 256), (False, 5, 77, 128), (True, 1, 262144, 128),
-                                        (True, 300, 4104, 384)])
+                                        (True, 300, 4104, 384), (True, 300, 4096, 512), (True, 129, 8192, 1536)])
 def test_ragged_shapes(bf16, M, V, d):
     """M not a multiple of the tile, V ending mid-step and mid-vector, small d."""
     rng = np.random.default_rng(M + V)
