@@ -47,10 +47,11 @@ def algorithmic():
     attn_flop = 4 * D * HQ * pairs
     attn_bytes = 2 * (2 * CANVAS * HQ * D + 2 * (PREFIX + CANVAS) * HKV * D)  # Q, O, K, V in bf16
     samp_bytes = 2 * CANVAS * VOCAB + 32 * CANVAS  # logits once + per-row outputs
+    samp_probs_bytes = 2 * CANVAS * VOCAB  # block-scaled probabilities written for self-conditioning
     sc_flop = 2 * CANVAS * VOCAB * EMBED
     sc_bytes = 2 * (VOCAB * EMBED + CANVAS * VOCAB + CANVAS * EMBED)
-    return dict(attn_flop=attn_flop, attn_bytes=attn_bytes, samp_bytes=samp_bytes, sc_flop=sc_flop,
-                sc_bytes=sc_bytes)
+    return dict(attn_flop=attn_flop, attn_bytes=attn_bytes, samp_bytes=samp_bytes, samp_probs_bytes=samp_probs_bytes,
+                sc_flop=sc_flop, sc_bytes=sc_bytes)
 
 
 def cpu_baseline(q, k, v, logits_by_step, E, seqs, seed, min_seconds=10.0, max_steps=6):
@@ -261,6 +262,7 @@ def main():
 
     attn_tflops = alg["attn_flop"] / (attn_ms * 1e-3) / 1e12
     samp_gbs = alg["samp_bytes"] / (samp_ms * 1e-3) / 1e9
+    samp_rw_gbs = (alg["samp_bytes"] + alg["samp_probs_bytes"]) / (samp_ms * 1e-3) / 1e9
     sc_gbs = alg["sc_bytes"] / (sc_ms * 1e-3) / 1e9
     sc_tflops = alg["sc_flop"] / (sc_ms * 1e-3) / 1e12
 
@@ -299,7 +301,9 @@ def main():
             "attn_mixed": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 1),
                            "frac_bf16_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
             "sampler_step": {"ms": round(samp_ms, 4), "gbs": round(samp_gbs, 1),
-                             "frac_hbm_peak": round(samp_gbs / PEAK_HBM_GBS, 4)},
+                             "frac_hbm_peak": round(samp_gbs / PEAK_HBM_GBS, 4),
+                             "gbs_with_probs_write": round(samp_rw_gbs, 1),
+                             "frac_hbm_peak_with_probs_write": round(samp_rw_gbs / PEAK_HBM_GBS, 4)},
             "selfcond_embed": {"ms": round(sc_ms, 4), "gbs": round(sc_gbs, 1), "tflops": round(sc_tflops, 1),
                                "frac_hbm_peak": round(sc_gbs / PEAK_HBM_GBS, 4)},
         },

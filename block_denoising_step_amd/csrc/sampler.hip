@@ -316,7 +316,7 @@ __device__ __forceinline__ long long block_exclusive_scan_ll(long long v, long l
 // desc, position asc), exact integer prefix sum of floor(H * 2^40), budget cut, canvas
 // update and convergence bookkeeping. Every input is loaded up front.
 __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& sp, const RowOut& o) {
-  __shared__ float key[DG_MAX_CANVAS];
+  __shared__ __attribute__((aligned(16))) float key[DG_MAX_CANVAS + 16];
   __shared__ long long sorted[DG_MAX_CANVAS];
   __shared__ long long wred[kWaves];
   __shared__ int ired[kWaves];
@@ -324,6 +324,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
   const int tid = threadIdx.x;
   const int n = reqs.num_rows[r], step = reqs.step[r], row0 = reqs.row_start[r];
   const uint64_t seed = reqs.seed[r];
+  const int prev_stable = o.stable_count[r];  // loaded early: the bookkeeping at the end needs it
   float c[kPerThread];
   long long fx[kPerThread];
   int am[kPerThread], cand[kPerThread], old[kPerThread];
@@ -347,21 +348,37 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
       key[j] = c[q];
     }
   }
+  // pad to a multiple of 16 with -inf: a finite confidence never ranks below it
+  if (tid < 16) key[n + tid] = kNegInf;
   __syncthreads();
   int rank[kPerThread];
 #pragma unroll
+  for (int q = 0; q < kPerThread; ++q) rank[q] = 0;
+  // rank = #{i : key_i > c_j or (key_i == c_j and i < j)}; 16 keys per iteration,
+  // read as float4 so the loads pipeline
+  for (int i0 = 0; i0 < n; i0 += 16) {
+    float4 k4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k4[u] = *reinterpret_cast<const float4*>(&key[i0 + 4 * u]);
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      const int j = tid + kThreads * q;
+      if (kThreads * q >= n) break;  // no thread has a position here (uniform)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float kv[4] = {k4[u].x, k4[u].y, k4[u].z, k4[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 4 * u + e;
+          rank[q] += (kv[e] > c[q]) || (kv[e] == c[q] && i < j);
+        }
+      }
+    }
+  }
+#pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int j = tid + kThreads * q;
-    rank[q] = 0;
-    if (j < n) {
-      int rk = 0;
-      for (int i = 0; i < n; ++i) {
-        const float ki = key[i];
-        rk += (ki > c[q]) || (ki == c[q] && i < j);
-      }
-      rank[q] = rk;
-      sorted[rk] = fx[q];
-    }
+    if (j < n) sorted[rank[q]] = fx[q];
   }
   __syncthreads();
   // inclusive scan of sorted[0, n): each thread owns kPerThread consecutive ranks
@@ -390,11 +407,30 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
     acc[q] = j < n && (sorted[rank[q]] <= limit || rank[q] < sp.min_accept);
     cnt += acc[q];
   }
-  const long long total = block_sum_ll(sum, wred);
-  const int count = (int)block_sum_ll(cnt, wred);
-  const int all_same = -block_max_int(-same, ired);  // min over threads
+  // one reduction for the entropy total, the accepted count and "argmax unchanged"
+  long long tsum = sum;
+  int tcnt = cnt, tsame = same;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    tsum += __shfl_xor(tsum, off, 64);
+    tcnt += __shfl_xor(tcnt, off, 64);
+    tsame &= __shfl_xor(tsame, off, 64);
+  }
+  if ((tid & 63) == 0) {
+    wred[tid >> 6] = tsum;
+    ired[tid >> 6] = tcnt | (tsame << 30);
+  }
+  __syncthreads();
+  long long total = 0;
+  int count = 0, all_same = 1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    total += wred[w];
+    count += ired[w] & ((1 << 30) - 1);
+    all_same &= ired[w] >> 30;
+  }
   if (tid == 0) {
-    const int stable = (step > 0 && all_same) ? o.stable_count[r] + 1 : 0;
+    const int stable = (step > 0 && all_same) ? prev_stable + 1 : 0;
     const long long thr = (long long)ceil((double)sp.tau * (double)n * 0x1p40);
     const bool low = total < thr;
     const bool done = step + 1 >= sp.step_limit;
