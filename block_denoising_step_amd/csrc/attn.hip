@@ -563,6 +563,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
     dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
     dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
   };
+  // one of the 8 DMA instructions of stage j (0..3: K pairs, 4..7: V pairs), in the
+  // same order as issue()
+  auto issue_one = [&](int j, int i) {
+    lds_char* st = lds0 + (j & 3) * kAttStage;
+    const bool isk = i < 4;
+    const int t = i & 3;
+    const int kbase = key0 + kSub * (isk ? min(j + 1, nsub - 1) : j);
+    const char* src = (isk ? kb : vb) + (int64_t)kbase * rs;
+    lds_char* dst = isk ? st + (4 * wave + t) * kKPitch : st + kKRegion + (4 * wave + t) * kVPitch;
+    const uint32_t off = kbase + kSub <= nkeys ? vo[t]
+                                               : min(2 * (4 * wave + t) + (lane & 1), nkeys - 1 - kbase) * rs + (lane >> 1) * 16;
+    __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
 
   // ---- LDS read addresses: per-lane base + immediates
   const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
@@ -572,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);  // + 32 b
   const uint32_t v_lane = kKRegion + (vrow >> 1) * kVPitch + 16 * (vrow & 1) + 32 * (vcol >> 3) + 2 * (vcol & 7);
 
-  // mask S(j) where some row's bounds cut sub-tile j; returns the row max (scaled)
-  auto front = [&](f32x16_t& sv, int kbase) {
+  // mask S(j) where some row's bounds cut sub-tile j
+  auto mask = [&](f32x16_t& sv, int kbase) {
     if (!(lo_last <= kbase && kbase + kSub - 1 <= hi_first)) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -581,6 +594,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
         if (key < lo || key > hi) sv[e] = kNegInf;
       }
     }
+  };
+  // ... and its row max (scaled)
+  auto front = [&](f32x16_t& sv, int kbase) {
+    mask(sv, kbase);
     float t = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     t = fmaxf(t, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
     return half_max(t) * a.scale_log2;
@@ -629,19 +646,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       else if (left == 1) DG_ATT_WAIT_VM(8);
       else DG_ATT_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
-      if (sub + 3 < nsub) issue(sub + 3);
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t ka = lbase + (sub & 3) * kAttStage + k_lane;
       const uint32_t va = lbase + (sub & 3) * kAttStage + v_lane;
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
+      const bool refill = sub + 3 < nsub;   // uniform
+      const bool has_next = sub + 1 < nsub;  // uniform
 
       uint4 kf[KS];
       uint2 v0[DB][2], v1[DB][2];
       StaticFor<0, 8>::run([&](auto ks) { kf[ks] = att_b128<64 * decltype(ks)::value>(ka); });
       DG_ATT_WAIT_LGKM0();
-      __builtin_amdgcn_sched_barrier(0);
 
-      // S(sub+1) k-steps 0..7, K reads 8..15, V^T reads of keys 0..15, P(sub)
+      // S(sub+1) k-steps 0..7 with K reads 8..15, the V^T reads of keys 0..15 and the
+      // probabilities P(sub) of keys 0..15
       f32x16_t snxt;
 #pragma unroll
       for (int e = 0; e < 16; ++e) snxt[e] = 0.f;
@@ -653,19 +671,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
         kf[ks + 8] = att_b128<64 * (ks + 8)>(ka);
         v0[ks][0] = att_tr16<128 * ks>(va);
         v0[ks][1] = att_tr16<128 * ks + 4 * kVPitch>(va);
-        p[2 * ks] = fast_exp2(fmaf(scur[2 * ks], a.scale_log2, -mu));
-        p[2 * ks + 1] = fast_exp2(fmaf(scur[2 * ks + 1], a.scale_log2, -mu));
-        l_run += p[2 * ks] + p[2 * ks + 1];
+        p[ks] = fast_exp2(fmaf(scur[ks], a.scale_log2, -mu));
+        l_run += p[ks];
         __builtin_amdgcn_sched_barrier(0);
       });
       uint4 pf[2];
       pf[0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
-      pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
-                         pack_bf16(p[14], p[15]));
       DG_ATT_WAIT_LGKM0();
-      __builtin_amdgcn_sched_barrier(0);
 
-      // O^T += V^T(keys 0..15) . P^T, S(sub+1) k-steps 8..15, V^T reads of keys 16..31
+      // O^T += V^T(keys 0..15) . P^T and S(sub+1) k-steps 8..15, with the V^T reads of
+      // keys 16..31, P(sub) of keys 16..31, and the refill of the ring slot of sub-1
       StaticFor<0, DB>::run([&](auto ic) {
         constexpr int b = decltype(ic)::value;
         o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -675,26 +690,35 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
                                                        __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
         v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
         v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
+        if (refill) issue_one(sub + 3, b);
+        p[8 + b] = fast_exp2(fmaf(scur[8 + b], a.scale_log2, -mu));
+        l_run += p[8 + b];
         __builtin_amdgcn_sched_barrier(0);
       });
+      pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
+                         pack_bf16(p[14], p[15]));
       DG_ATT_WAIT_LGKM0();
-      __builtin_amdgcn_sched_barrier(0);
+
+      // O^T += V^T(keys 16..31) . P^T, with the next sub-tile's mask, row max and
+      // reference (S(sub+1) is complete) between the MFMAs
+      if (has_next) mask(snxt, key0 + kSub * (sub + 1));
+      float t4[4], tmax = kNegInf;
       StaticFor<0, DB>::run([&](auto ic) {
         constexpr int b = decltype(ic)::value;
         o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, make_uint4(v1[b][0].x, v1[b][0].y, v1[b][1].x, v1[b][1].y)),
             __builtin_bit_cast(bf16x8_t, pf[1]), o[b], 0, 0, 0);
+        if (b < 4) t4[b] = fmaxf(fmaxf(snxt[4 * b], snxt[4 * b + 1]), fmaxf(snxt[4 * b + 2], snxt[4 * b + 3]));
+        if (b == 4) tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        if (b == 5) tmax = half_max(tmax) * a.scale_log2;
+        if (b == 6 && has_next) {
+          m_seen = fmaxf(m_seen, tmax);
+          if (m_ref == kNegInf) m_ref = tmax;
+          overflow |= tmax > m_ref + kOverflow;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       });
-      __builtin_amdgcn_sched_barrier(0);
-
-      // next sub-tile: mask, max, reference of rows seeing their first finite score
-      if (sub + 1 < nsub) {
-        scur = snxt;
-        const float tmax = front(scur, key0 + kSub * (sub + 1));
-        m_seen = fmaxf(m_seen, tmax);
-        if (m_ref == kNegInf) m_ref = tmax;
-        overflow |= tmax > m_ref + kOverflow;
-      }
+      scur = snxt;
     }
     // the loop ends with the ring drained; a rare overflow anywhere redoes the chunk
     if (__any(overflow) && lane == 0) redo_flag[0] = 1;
