@@ -16,8 +16,9 @@
 //   O^T += V^T . P^T (MFMA 32x32; P^T taken straight from the S^T accumulators,
 //   V transposed into LDS with the key order permuted to match them), so the
 //   softmax rescale of O is a per-lane multiply.
-// A request whose keys were split into several chunks writes fp32 partials
-// (unnormalised O, running max and sum); attn_merge combines them in chunk order.
+// A request whose keys were split into several chunks writes partials: O of the
+// chunk normalised by its own sum, in the input dtype, plus the chunk's (max, sum)
+// in fp32; attn_merge combines them in chunk order.
 #include "dg_common.cuh"
 #include "dg_internal.h"
 
@@ -34,7 +35,7 @@ struct AttnArgs {
   const void* v;
   void* out;
   float* lse;
-  float* part_o;
+  void* part_o;  // [part][kRows][D], input dtype
   float* part_ml;
   int hq, hkv, group, window, tokens_per_tile, num_seqs;
   float scale_log2;  // scale * log2(e)
@@ -302,12 +303,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
     }
   }
 
-  // epilogue: o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]
+  // epilogue: o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]; a row
+  // with no key in this chunk (l = 0) stores zeros
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!valid) return;
-  if (sp.num_chunks == 1) {
-    const float inv = 1.f / l_tot;
-    char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz;
+  {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int part = sp.part_begin + local;
+    char* orow = sp.num_chunks == 1
+                     ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz
+                     : reinterpret_cast<char*>(a.part_o) + ((int64_t)part * kRows + row) * D * esz;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -318,34 +323,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
         if (kBf16) *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
         else *reinterpret_cast<float4*>(orow + d * 4) = make_float4(x0, x1, x2, x3);
       }
-    if (a.lse && hh == 0) a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = m_run * kLn2 + __builtin_amdgcn_logf(l_tot) * kLn2;
-  } else {
-    const int part = sp.part_begin + local;
-    float* po = a.part_o + ((int64_t)part * kRows + row) * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<float4*>(po + 32 * b + 8 * e4 + 4 * hh) =
-            make_float4(o[b][4 * e4], o[b][4 * e4 + 1], o[b][4 * e4 + 2], o[b][4 * e4 + 3]);
-    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_run, l_tot);
+    if (hh == 0) {
+      if (sp.num_chunks > 1)
+        *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_run, l_tot);
+      else if (a.lse)
+        a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = m_run * kLn2 + __builtin_amdgcn_logf(l_tot) * kLn2;
+    }
   }
 }
 
 // Combine the chunk partials of one (request, KV head, q tile) in chunk order:
-// O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j.
-// Merge of a request's key-chunk partials: one thread per 4 output columns of a row,
-// so that one (q tile, kv head) unit spreads over D/8 work groups and every load is
-// an independent, coalesced float4.
-template <int D>
-constexpr int merge_groups_per_unit() { return kRows * (D / 4) / kThreads; }
+// with w_j = 2^(m_j - M) l_j (M a running max over the chunks), O = sum_j w_j O_j / sum_j w_j,
+// where O_j is chunk j's output normalised by its own sum l_j.
+// One thread per 16 bytes of partial row (8 bf16 or 4 fp32 columns), so that one
+// (q tile, kv head) unit spreads over several work groups and every load is an
+// independent, coalesced 16-byte load.
+template <bool kBf16>
+constexpr int merge_cols() { return kBf16 ? 8 : 4; }
+template <bool kBf16, int D>
+constexpr int merge_groups_per_unit() { return kRows * (D / merge_cols<kBf16>()) / kThreads; }
 
 template <bool kBf16, int D>
 __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
   constexpr int esz = kBf16 ? 2 : 4;
-  constexpr int kTpr = D / 4;             // threads per row
+  constexpr int kC = merge_cols<kBf16>();
+  constexpr int kTpr = D / kC;            // threads per row
   constexpr int kRpw = kThreads / kTpr;   // rows per work group
-  constexpr int kGpu = merge_groups_per_unit<D>();
+  constexpr int kGpu = merge_groups_per_unit<kBf16, D>();
   const int w = blockIdx.x / kGpu;
   const int s = find_seq(a, w, true);
   const AttnSeqPlan sp = a.seqs[s];
@@ -362,33 +366,63 @@ __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
   const int part0 = sp.part_begin + (g * nqt + qt) * sp.num_chunks;
 
   const int row = (blockIdx.x % kGpu) * kRpw + threadIdx.x / kTpr;
-  const int c = (threadIdx.x % kTpr) * 4;
+  const int c = (threadIdx.x % kTpr) * kC;
   const int tok = i0 + row / a.group;
   const int head = g * a.group + row % a.group;
   if (tok >= sp.num_q) return;
-  float mmax = kNegInf;
-#pragma unroll 4
-  for (int j = 0; j < nonempty; ++j) mmax = fmaxf(mmax, a.part_ml[((int64_t)(part0 + j) * kRows + row) * 2]);
-  float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int j = 0; j < nonempty; ++j) {
-    const int64_t pr = (int64_t)(part0 + j) * kRows + row;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
-    const float4 x = *reinterpret_cast<const float4*>(a.part_o + pr * D + c);
-    const float f = ml.x == kNegInf ? 0.f : fast_exp2(ml.x - mmax);
-    wsum = fmaf(f, ml.y, wsum);
-    acc.x = fmaf(f, x.x, acc.x);
-    acc.y = fmaf(f, x.y, acc.y);
-    acc.z = fmaf(f, x.z, acc.z);
-    acc.w = fmaf(f, x.w, acc.w);
+  // batches of up to 8 chunks, all loads of a batch issued before first use; the
+  // running reference mmax moves up between batches (acc and wsum are rescaled)
+  constexpr int kB = 8;
+  float mmax = kNegInf, wsum = 0.f;
+  float acc[kC];
+#pragma unroll
+  for (int i = 0; i < kC; ++i) acc[i] = 0.f;
+  const char* pbase = reinterpret_cast<const char*>(a.part_o);
+  for (int j0 = 0; j0 < nonempty; j0 += kB) {
+    float2 ml[kB];
+    uint4 x[kB];
+#pragma unroll
+    for (int t = 0; t < kB; ++t) {
+      const int64_t pr = (int64_t)(part0 + min(j0 + t, nonempty - 1)) * kRows + row;
+      ml[t] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+      x[t] = *reinterpret_cast<const uint4*>(pbase + (pr * D + c) * esz);
+    }
+    float bmax = mmax;
+#pragma unroll
+    for (int t = 0; t < kB; ++t)
+      if (j0 + t < nonempty) bmax = fmaxf(bmax, ml[t].x);
+    if (bmax != mmax) {  // mmax = -inf only before the first finite chunk (acc and wsum are 0)
+      const float r = mmax == kNegInf ? 0.f : fast_exp2(mmax - bmax);
+      wsum *= r;
+#pragma unroll
+      for (int i = 0; i < kC; ++i) acc[i] *= r;
+      mmax = bmax;
+    }
+#pragma unroll
+    for (int t = 0; t < kB; ++t) {
+      const float f = (j0 + t >= nonempty || ml[t].x == kNegInf) ? 0.f : fast_exp2(ml[t].x - mmax) * ml[t].y;
+      wsum += f;
+      const uint32_t xw[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kBf16) {
+          acc[2 * i] = fmaf(f, __uint_as_float(xw[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(f, __uint_as_float(xw[i] & 0xffff0000u), acc[2 * i + 1]);
+        } else {
+          acc[i] = fmaf(f, __uint_as_float(xw[i]), acc[i]);
+        }
+      }
+    }
   }
   const float inv = 1.f / wsum;
   char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz + c * esz;
-  if (kBf16)
-    *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
-  else
-    *reinterpret_cast<float4*>(orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  uint32_t ow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kBf16) ow[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    else ow[i] = __float_as_uint(acc[i] * inv);
+  }
+  *reinterpret_cast<uint4*>(orow) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   if (a.lse && c == 0) a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (mmax + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
@@ -732,9 +766,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   // ---- epilogue: o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]
   const float l_tot = half_sum(l_run);
   if (!valid) return;
-  if (sp.num_chunks == 1) {
-    const float inv = 1.f / l_tot;
-    char* orow = reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2;
+  {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int part = sp.part_begin + (g * nqt + qt) * sp.num_chunks + chunk;
+    char* orow = sp.num_chunks == 1
+                     ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2
+                     : reinterpret_cast<char*>(a.part_o) + ((int64_t)part * kRows + row) * D * 2;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -743,18 +780,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
         *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(pack_bf16(o[b][4 * e4] * inv, o[b][4 * e4 + 1] * inv),
                                                              pack_bf16(o[b][4 * e4 + 2] * inv, o[b][4 * e4 + 3] * inv));
       }
-    if (a.lse && hh == 0)
-      a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  } else {
-    const int part = sp.part_begin + (g * nqt + qt) * sp.num_chunks + chunk;
-    float* po = a.part_o + ((int64_t)part * kRows + row) * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<float4*>(po + 32 * b + 8 * e4 + 4 * hh) =
-            make_float4(o[b][4 * e4], o[b][4 * e4 + 1], o[b][4 * e4 + 2], o[b][4 * e4 + 3]);
-    if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_ref, l_tot);
+    if (hh == 0) {
+      if (sp.num_chunks > 1)
+        *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_ref, l_tot);
+      else if (a.lse)
+        a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -765,7 +796,7 @@ int launch_typed(const AttnArgs& args, const AttnPlan& plan, hipStream_t s) {
   else
     hipLaunchKernelGGL((attn_fwd<kBf16, D>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
   if (plan.num_merge > 0)
-    hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge * merge_groups_per_unit<D>()), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge * merge_groups_per_unit<kBf16, D>()), dim3(kThreads), 0, s,
                        args);
   return (int)hipGetLastError();
 }
@@ -781,7 +812,7 @@ int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream) {
   args.out = a->out;
   args.lse = a->lse;
   char* ws = reinterpret_cast<char*>(a->workspace);
-  args.part_o = plan.num_parts ? reinterpret_cast<float*>(ws + plan.part_o_offset) : nullptr;
+  args.part_o = plan.num_parts ? reinterpret_cast<void*>(ws + plan.part_o_offset) : nullptr;
   args.part_ml = plan.num_parts ? reinterpret_cast<float*>(ws + plan.part_ml_offset) : nullptr;
   args.hq = a->num_q_heads;
   args.hkv = a->num_kv_heads;

@@ -139,7 +139,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   plan->num_merge = (int)num_merge;
   plan->num_parts = (int)num_parts;
   plan->part_o_offset = 0;
-  const size_t o_bytes = (size_t)num_parts * kTileRows * a->head_dim * sizeof(float);
+  const size_t o_bytes = (size_t)num_parts * kTileRows * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);
   plan->part_ml_offset = align_up(o_bytes, 256);
   const size_t ml_bytes = (size_t)num_parts * kTileRows * 2 * sizeof(float);
   plan->bytes = num_parts ? align_up(plan->part_ml_offset + ml_bytes, 256) : 0;

@@ -38,7 +38,7 @@ struct AttnPlan {
   int num_merge;        // work groups of the merge kernel
   int num_parts;        // partial slots
   int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB: LDS-DMA kernel
-  size_t part_o_offset;   // workspace: [num_parts][kAttnTileRows][D] fp32 partial outputs
+  size_t part_o_offset;   // workspace: [num_parts][kAttnTileRows][D] partial outputs, input dtype
   size_t part_ml_offset;  // workspace: [num_parts][kAttnTileRows][2] fp32 (max, sum) in log2 units
   size_t bytes;
   AttnSeqPlan seqs[DG_MAX_SEQS];

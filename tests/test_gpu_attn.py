@@ -100,7 +100,7 @@ def test_shapes_ragged_and_split(D, bf16, hq, hkv):
     q = normal(seed, (tq, hq, D), bf16=bf16)
     k = normal(seed + 1, (tk, hkv, D), bf16=bf16)
     v = normal(seed + 2, (tk, hkv, D), bf16=bf16)
-    for window, chunk in ((-1, 0), (-1, 64), (17, 0), (0, 0), (40, 128)):
+    for window, chunk in ((-1, 0), (-1, 64), (17, 0), (0, 0), (40, 128), (9, 64)):
         _compare(seqs, window, q, k, v, hq, hkv, bf16, kv_chunk=chunk,
                  label=f"D={D} bf16={bf16} G={hq // hkv}")
 
