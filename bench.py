@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "denoise steps/s (256-tok canvas) + attn MFMA util, sampler HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
 
 # workload sizes
 CANVAS, PREFIX, HQ, HKV, D = 256, 4096, 16, 8, 256
@@ -132,12 +133,161 @@ def _cpu_model():
     return platform.processor()
 
 
+def key_range(mode, prefix, num_q, window, i):
+    """Allowed keys [lo, hi] of query i of a request (causal: up to itself; bidirectional:
+    the whole canvas; a window W keeps keys within W positions, one-sided for causal)."""
+    p = prefix + i
+    hi = p if mode == 0 else prefix + num_q - 1
+    lo = 0
+    if window >= 0:
+        lo = max(0, p - window)
+        hi = min(hi, p + window)
+    return lo, hi
+
+
+def attn_work(seqs, window, hq, hkv, d, esz):
+    """Algorithmic FLOPs and bytes of one attention call: allowed (query, key) pairs,
+    Q and O once, each touched K/V row once per KV head."""
+    pairs, touched, nq = 0, 0, 0
+    for s in seqs:
+        if s.num_q == 0:
+            continue
+        los, his = zip(*(key_range(s.mode, s.prefix_len, s.num_q, window, i) for i in range(s.num_q)))
+        pairs += sum(h - l + 1 for l, h in zip(los, his))
+        touched += max(his) - min(los) + 1  # key ranges of consecutive queries overlap or touch
+        nq += s.num_q
+    return 4 * d * hq * pairs, esz * (2 * nq * hq * d + 2 * touched * hkv * d)
+
+
+def per_config(path, reps=20, warm=5):
+    """Median event time of every call of the five workloads, with each call's
+    algorithmic rate and its fraction of the binding roof; written to `path` as JSON."""
+    import torch
+    import block_denoising_step_amd as dg
+    from workloads import attn_case, sampler_case, seed_for, TID_Z, TID_SIGMA, TID_E, CAUSAL
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dg.load()
+    stream = torch.cuda.current_stream()
+    ridge_bf16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge_f32 = PEAK_F32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+    def med_us(call):
+        for _ in range(warm):
+            call(stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            call(stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return t[len(t) // 2] * 1e3
+
+    def entry(us, flop, nbytes, fp32):
+        peak_t = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+        ridge = ridge_f32 if fp32 else ridge_bf16
+        tflops = flop / us / 1e6 if flop else 0.0
+        gbs = nbytes / us / 1e3
+        mfma = flop > 0 and flop / nbytes > ridge
+        e = {"us": round(us, 2), "flop": flop, "bytes": nbytes, "tflops": round(tflops, 1), "gbs": round(gbs, 1),
+             "bound": ("mfma_f32" if fp32 else "mfma_bf16") if mfma else "hbm"}
+        e["frac"] = round(tflops / peak_t if mfma else gbs / PEAK_HBM_GBS, 4)
+        return e
+
+    def gen(seed, shape, std=1.0, dtype=torch.bfloat16):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        return (torch.randn(shape, device=dev, generator=g) * std).to(dtype)
+
+    def gen_logits(cfg, rows, vocab, dtype):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed_for(cfg, TID_SIGMA))
+        sig = torch.exp(torch.empty(rows, 1, device=dev).uniform_(np.log(0.1), np.log(10.0), generator=g))
+        return (gen(seed_for(cfg, TID_Z), (rows, vocab), dtype=torch.float32) * sig).to(dtype)
+
+    out = {"device": torch.cuda.get_device_name(0), "reps": reps, "warmup": warm, "configs": {}}
+
+    def attn_calls(case, variants):
+        dt = torch.bfloat16 if case.bf16 else torch.float32
+        esz = 2 if case.bf16 else 4
+        q = gen(seed_for(case.cfg, 1), (case.total_q, case.num_q_heads, case.head_dim), dtype=dt)
+        k = gen(seed_for(case.cfg, 2), (case.total_kv, case.num_kv_heads, case.head_dim), dtype=dt)
+        v = gen(seed_for(case.cfg, 3), (case.total_kv, case.num_kv_heads, case.head_dim), dtype=dt)
+        o = torch.empty_like(q)
+        res = {}
+        for name, seqs, window in variants:
+            c = dg.prepare_attn(q, k, v, o, seqs, window, case.num_q_heads, case.num_kv_heads)
+            flop, nbytes = attn_work(seqs, window, case.num_q_heads, case.num_kv_heads, case.head_dim, esz)
+            res[name] = entry(med_us(c), flop, nbytes, not case.bf16)
+            print(f"[per-config] cfg{case.cfg} {name}: {res[name]}", file=sys.stderr, flush=True)
+        del q, k, v, o
+        return res
+
+    def sampler_and_selfcond(cfg, with_selfcond):
+        sc = sampler_case(cfg)
+        dt = torch.bfloat16 if sc.bf16 else torch.float32
+        esz = 2 if sc.bf16 else 4
+        M, V = sc.total_rows, sc.vocab
+        lg = gen_logits(cfg, M, V, dt)
+        reqs, r0 = [], 0
+        for i, n in enumerate(sc.canvases):
+            reqs.append((r0, n, 1000 + i, 0))
+            r0 += n
+        res = {}
+        bufs = dg.SamplerBuffers(M, len(reqs), dev, vocab=V if with_selfcond else 0,
+                                 probs_dtype=dt if with_selfcond else None)
+        c = dg.prepare_sampler(lg, reqs, V, bufs, sc.budget)
+        nbytes = esz * M * V + 32 * M + (esz * M * V if with_selfcond else 0)
+        res["sampler" + ("_with_probs" if with_selfcond else "")] = entry(med_us(c), 0, nbytes, False)
+        if with_selfcond:
+            E = gen(seed_for(cfg, TID_E), (V, sc.embed_dim), std=0.02, dtype=dt)
+            so = torch.empty(M, sc.embed_dim, device=dev, dtype=dt)
+            cs = dg.prepare_selfcond(bufs.probs, E, so, p_scale=bufs.probs_scale)
+            flop = 2 * M * V * sc.embed_dim
+            nbytes = esz * (V * sc.embed_dim + M * V + M * sc.embed_dim)
+            res["selfcond"] = entry(med_us(cs), flop, nbytes, not sc.bf16)
+            del E, so
+        for k_, v_ in res.items():
+            print(f"[per-config] cfg{cfg} {k_}: {v_}", file=sys.stderr, flush=True)
+        del lg, bufs
+        return res
+
+    c1 = attn_case(1)
+    r = attn_calls(c1, [("attn_bidir_w32", c1.seqs, 32), ("attn_causal_w32", c1.with_mode(CAUSAL).seqs, 32)])
+    r.update(sampler_and_selfcond(1, True))
+    out["configs"]["1"] = r
+    c2 = attn_case(2)
+    r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)])
+    r.update(sampler_and_selfcond(2, True))
+    out["configs"]["2"] = r
+    c3 = attn_case(3)
+    out["configs"]["3"] = attn_calls(c3, [("attn_bidir_w512", c3.seqs, 512),
+                                          ("attn_causal_w512", c3.with_mode(CAUSAL).seqs, 512)])
+    c4 = attn_case(4)
+    r = attn_calls(c4, [("attn_global_layer", c4.seqs, -1), ("attn_w512_layer", c4.seqs, 512)])
+    r.update(sampler_and_selfcond(4, False))
+    out["configs"]["4"] = r
+    torch.cuda.empty_cache()
+    c5 = attn_case(5)
+    r = attn_calls(c5, [("attn_bidir_global", c5.seqs, -1)])
+    torch.cuda.empty_cache()
+    r.update(sampler_and_selfcond(5, True))
+    out["configs"]["5"] = r
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"[per-config] wrote {path}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--per-config", metavar="PATH",
+                    help="instead of the step loop, time every call of the five workloads and write JSON to PATH")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -145,6 +295,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.per_config:
+        per_config(args.per_config)
+        return
 
     import torch
     import block_denoising_step_amd as dg

@@ -35,9 +35,10 @@ struct AttnArgs {
   const void* v;
   void* out;
   float* lse;
-  void* part_o;  // [part][kRows][D], input dtype
+  void* part_o;  // [partial rows][D], input dtype
   float* part_ml;
-  int hq, hkv, group, window, tokens_per_tile, num_seqs;
+  int hq, hkv, group, window, num_seqs;
+  int work_offset;  // work index of this launch's block 0
   float scale_log2;  // scale * log2(e)
   AttnSeqPlan seqs[DG_MAX_SEQS];
 };
@@ -52,11 +53,13 @@ __device__ __forceinline__ void key_bounds(int mode, int prefix, int num_q, int 
 // The request owning a global work (or merge) index: the last one whose first index
 // is <= w. Requests without work share their first index with the next request, so
 // the last of a tie is the one that has work.
+// The request whose work (or merge) range holds index w.
 __device__ __forceinline__ int find_seq(const AttnArgs& a, int w, bool merge) {
   int s = 0;
-  for (int i = 1; i < a.num_seqs; ++i) {
+  for (int i = 0; i < a.num_seqs; ++i) {
     const int b = merge ? a.seqs[i].merge_begin : a.seqs[i].work_begin;
-    if (b <= w) s = i;
+    const int n = merge ? a.seqs[i].merge_count : a.seqs[i].work_count;
+    if (b <= w && w < b + n) s = i;
   }
   return s;
 }
@@ -186,17 +189,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lk[L::k_bytes];
   __shared__ __attribute__((aligned(16))) char lv[L::v_bytes];
 
-  const int w = blockIdx.x;
+  const int w = a.work_offset + blockIdx.x;
   const int s = find_seq(a, w, false);
   const AttnSeqPlan sp = a.seqs[s];
-  const int nqt = (sp.num_q + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
   const int chunk = local % sp.num_chunks;
   const int rest = local / sp.num_chunks;
   const int qt = rest % nqt;
   const int g = rest / nqt;
-  const int i0 = qt * a.tokens_per_tile;
-  const int nq = min(a.tokens_per_tile, sp.num_q - i0);
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
   const int nkeys = sp.prefix_len + sp.num_q;
 
   int lo_first, hi_first, lo_last, hi_last;
@@ -309,10 +312,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   if (!valid) return;
   {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int part = sp.part_begin + local;
+    const int64_t prow = sp.part_begin + (int64_t)local * kRows + row;
     char* orow = sp.num_chunks == 1
                      ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz
-                     : reinterpret_cast<char*>(a.part_o) + ((int64_t)part * kRows + row) * D * esz;
+                     : reinterpret_cast<char*>(a.part_o) + prow * D * esz;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
       }
     if (hh == 0) {
       if (sp.num_chunks > 1)
-        *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_run, l_tot);
+        *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_run, l_tot);
       else if (a.lse)
         a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = m_run * kLn2 + __builtin_amdgcn_logf(l_tot) * kLn2;
     }
@@ -341,31 +344,32 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 template <bool kBf16>
 constexpr int merge_cols() { return kBf16 ? 8 : 4; }
 template <bool kBf16, int D>
-constexpr int merge_groups_per_unit() { return kRows * (D / merge_cols<kBf16>()) / kThreads; }
+constexpr int merge_rows_per_group() { return kThreads / (D / merge_cols<kBf16>()); }
 
 template <bool kBf16, int D>
 __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
   constexpr int esz = kBf16 ? 2 : 4;
   constexpr int kC = merge_cols<kBf16>();
   constexpr int kTpr = D / kC;            // threads per row
-  constexpr int kRpw = kThreads / kTpr;   // rows per work group
-  constexpr int kGpu = merge_groups_per_unit<kBf16, D>();
-  const int w = blockIdx.x / kGpu;
-  const int s = find_seq(a, w, true);
+  constexpr int kRpw = merge_rows_per_group<kBf16, D>();  // rows per work group
+  static_assert(kRpw == attn_merge_rows_per_group(kBf16, D), "merge geometry");
+  const int s = find_seq(a, blockIdx.x, true);
   const AttnSeqPlan sp = a.seqs[s];
-  const int nqt = (sp.num_q + a.tokens_per_tile - 1) / a.tokens_per_tile;
-  const int local = w - sp.merge_begin;
-  const int qt = local % nqt, g = local / nqt;
-  const int i0 = qt * a.tokens_per_tile;
-  const int nq = min(a.tokens_per_tile, sp.num_q - i0);
+  const int gpu = sp.tile_rows / kRpw;  // work groups per (q tile, kv head) unit
+  const int lg = blockIdx.x - sp.merge_begin;
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
+  const int unit = lg / gpu;
+  const int qt = unit % nqt, g = unit / nqt;
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
   int lo_first, hi_first, lo_last, hi_last;
   key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
   key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0 + nq - 1, lo_last, hi_last);
   const int kt_lo = lo_first / kKT, kt_hi = hi_last / kKT;
   const int nonempty = min(sp.num_chunks, (kt_hi - kt_lo) / sp.chunk_tiles + 1);
-  const int part0 = sp.part_begin + (g * nqt + qt) * sp.num_chunks;
+  const int64_t prow0 = sp.part_begin + (int64_t)(g * nqt + qt) * sp.num_chunks * sp.tile_rows;
 
-  const int row = (blockIdx.x % kGpu) * kRpw + threadIdx.x / kTpr;
+  const int row = (lg % gpu) * kRpw + threadIdx.x / kTpr;
   const int c = (threadIdx.x % kTpr) * kC;
   const int tok = i0 + row / a.group;
   const int head = g * a.group + row % a.group;
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge(AttnArgs a) {
     uint4 x[kB];
 #pragma unroll
     for (int t = 0; t < kB; ++t) {
-      const int64_t pr = (int64_t)(part0 + min(j0 + t, nonempty - 1)) * kRows + row;
+      const int64_t pr = prow0 + (int64_t)min(j0 + t, nonempty - 1) * sp.tile_rows + row;
       ml[t] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
       x[t] = *reinterpret_cast<const uint4*>(pbase + (pr * D + c) * esz);
     }
@@ -520,17 +524,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kAttStage];
   __shared__ int redo_flag[1];  // set by a wave that saw a score past the reference
 
-  const int w = xcd_order(blockIdx.x, gridDim.x);
+  const int w = a.work_offset + xcd_order(blockIdx.x, gridDim.x);
   const int s_ = find_seq(a, w, false);
   const AttnSeqPlan sp = a.seqs[s_];
-  const int nqt = (sp.num_q + a.tokens_per_tile - 1) / a.tokens_per_tile;
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
   const int qt = local % nqt;  // q tiles of one (kv head, chunk) are consecutive
   const int rest = local / nqt;
   const int chunk = rest % sp.num_chunks;
   const int g = rest / sp.num_chunks;
-  const int i0 = qt * a.tokens_per_tile;
-  const int nq = min(a.tokens_per_tile, sp.num_q - i0);
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
   const int nkeys = sp.prefix_len + sp.num_q;
   int lo_first, hi_first, lo_last, hi_last;
   key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
@@ -768,10 +772,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   if (!valid) return;
   {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int part = sp.part_begin + (g * nqt + qt) * sp.num_chunks + chunk;
+    const int64_t prow = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kRows + row;
     char* orow = sp.num_chunks == 1
                      ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2
-                     : reinterpret_cast<char*>(a.part_o) + ((int64_t)part * kRows + row) * D * 2;
+                     : reinterpret_cast<char*>(a.part_o) + prow * D * 2;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -782,22 +786,399 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       }
     if (hh == 0) {
       if (sp.num_chunks > 1)
-        *reinterpret_cast<float2*>(a.part_ml + ((int64_t)part * kRows + row) * 2) = make_float2(m_ref, l_tot);
+        *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
       else if (a.lse)
         a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
 }
 
+// ---- bf16, head_dim 256, 64 query rows per wave ---------------------------------
+//
+// The ring, LDS layout and copies of attn_fwd_bf16_d256, with each wave owning 64
+// query rows (two 32-row halves), so that every K and V^T fragment read from LDS feeds
+// two MFMAs; a work group covers 256 rows. Per 32-key sub-tile j a wave computes
+// S(j+1) = K(j+1) . Q^T for both halves (32 MFMAs, K fragments streamed from LDS four
+// ahead, the ring refill interleaved), then O^T += V(j)^T . P(j)^T (32 MFMAs, V^T
+// fragments two ahead) while the vector units turn S(j+1) into P(j+1). O (2 x 128
+// accumulators) fills the AGPRs; Q^T (128), S (32) and the two P buffers (32) stay in
+// VGPRs. Softmax, reference and overflow handling are those of attn_fwd_bf16_d256,
+// per row half.
+
+// S^T MFMA in its VGPR form (accumulator in VGPRs): O fills the AGPRs, so S must not
+// go there. As inline asm, its hazards are handled here: a chain starts from the inline
+// zero (no vector write feeds it), each step accumulates into exactly the registers its
+// previous step wrote, and the last step (mfma_v_last2) carries the wait states the
+// vector units need before they read the result.
+__device__ __forceinline__ void mfma_v(f32x16_t& c, const uint4& a, const uint4& b, bool first) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t av = __builtin_bit_cast(u32x4_t, a), bv = __builtin_bit_cast(u32x4_t, b);
+  if (first) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+}
+// The last step of two chains, with the wait states in the same statement so that no
+// read of the results can be placed before them.
+__device__ __forceinline__ void mfma_v_last2(f32x16_t& c0, f32x16_t& c1, const uint4& a, const uint4& b0,
+                                             const uint4& b1) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t av = __builtin_bit_cast(u32x4_t, a), b0v = __builtin_bit_cast(u32x4_t, b0),
+                b1v = __builtin_bit_cast(u32x4_t, b1);
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1\n\t"
+      "s_nop 15\n\ts_nop 15\n\ts_nop 7"
+      : "+v"(c0), "+v"(c1)
+      : "v"(av), "v"(b0v), "v"(b1v));
+}
+
+#define DG_ATT_WAIT_LGKM(n)                                                   \
+  do {                                                                        \
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | ((n) << 8) | (3 << 14));       \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+  } while (0)
+
+__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
+  constexpr int D = 256, KS = 16, DB = 8, kTile = 256;
+  __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kAttStage];
+  __shared__ int redo_flag[1];
+  // Q^T fragments of the second row half, k-steps kQL..15, kept in LDS (per wave, lane order)
+  // instead of VGPRs: with O filling the AGPRs, the registers are short by about that much
+  constexpr int kQL = 11;
+  __shared__ __attribute__((aligned(16))) char qlds[4 * (KS - kQL) * 1024];
+
+  const int w = a.work_offset + xcd_order(blockIdx.x, gridDim.x);
+  const int s_ = find_seq(a, w, false);
+  const AttnSeqPlan sp = a.seqs[s_];
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
+  const int local = w - sp.work_begin;
+  const int qt = local % nqt;
+  const int rest = local / nqt;
+  const int chunk = rest % sp.num_chunks;
+  const int g = rest / sp.num_chunks;
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
+  const int nkeys = sp.prefix_len + sp.num_q;
+  int lo_first, hi_first, lo_last, hi_last;
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0 + nq - 1, lo_last, hi_last);
+  const int kt_lo = lo_first / kKT, kt_hi = hi_last / kKT;
+  const int t_begin = kt_lo + chunk * sp.chunk_tiles;
+  const int t_end = min(kt_hi + 1, t_begin + sp.chunk_tiles);
+  if (t_begin > kt_hi) return;
+  const int key0 = t_begin * kKT;
+  const int kend = min(t_end * kKT, hi_last + 1);
+  const int nsub = (kend - key0 + kSub - 1) / kSub;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  // row (h) = wave*64 + 32h + l32 holds token i0 + row/G, head g*G + row%G
+  auto row_of = [&](int h) { return wave * 64 + 32 * h + l32; };
+  int lo[2], hi[2];
+  uint4 qf[2][KS];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tok = i0 + row_of(h) / a.group, head = g * a.group + row_of(h) % a.group;
+    lo[h] = 0;
+    hi[h] = -1;
+    if (tok < sp.num_q) key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, tok, lo[h], hi[h]);
+    // rows past the request read its last token (their outputs are never stored)
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)(sp.q_start + min(tok, sp.num_q - 1)) * a.hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[h][ks] = *reinterpret_cast<const uint4*>(qrow + (16 * ks + 8 * hh) * 2);
+  }
+
+  {
+    const uint32_t qa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)qlds + wave * (KS - kQL) * 1024 + lane * 16;
+#pragma unroll
+    for (int ks = kQL; ks < KS; ++ks) {
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t x = {qf[1][ks].x, qf[1][ks].y, qf[1][ks].z, qf[1][ks].w};
+      asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(qa), "v"(x), "i"((ks - kQL) * 1024) : "memory");
+    }
+  }
+  const uint32_t q_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)qlds + wave * (KS - kQL) * 1024 + lane * 16;
+  const int rs = a.hkv * D * 2;
+  const int64_t head_off = ((int64_t)sp.kv_start * a.hkv + g) * D * 2;
+  const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
+  // lane offset of DMA pair t (recomputed at each use: it is cheap, and registers are not)
+  auto vo = [&](int t) { return (uint32_t)((2 * (4 * wave + t) + (lane & 1)) * rs + (lane >> 1) * 16); };
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* lds0 = (lds_char*)lds;
+  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase) {
+    const char* src = base + (int64_t)kbase * rs;
+    if (kbase + kSub <= nkeys) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds((const void*)(src + vo(t)),
+                                         (__attribute__((address_space(3))) void*)(dst + (4 * wave + t) * pitch), 16, 0, 0);
+    } else {
+      const int last = nkeys - 1 - kbase;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t r = min(2 * (4 * wave + t) + (lane & 1), last);
+        __builtin_amdgcn_global_load_lds((const void*)(src + (r * rs + (lane >> 1) * 16)),
+                                         (__attribute__((address_space(3))) void*)(dst + (4 * wave + t) * pitch), 16, 0, 0);
+      }
+    }
+  };
+  auto issue = [&](int j) {
+    lds_char* st = lds0 + (j & 3) * kAttStage;
+    dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
+    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
+  };
+  auto issue_one = [&](int j, int i) {
+    lds_char* st = lds0 + (j & 3) * kAttStage;
+    const bool isk = i < 4;
+    const int t = i & 3;
+    const int kbase = key0 + kSub * (isk ? min(j + 1, nsub - 1) : j);
+    const char* src = (isk ? kb : vb) + (int64_t)kbase * rs;
+    lds_char* dst = isk ? st + (4 * wave + t) * kKPitch : st + kKRegion + (4 * wave + t) * kVPitch;
+    const uint32_t off = kbase + kSub <= nkeys ? vo(t)
+                                               : min(2 * (4 * wave + t) + (lane & 1), nkeys - 1 - kbase) * rs + (lane >> 1) * 16;
+    __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
+  const uint32_t k_lane = (l32 >> 1) * kKPitch + 16 * (l32 & 1) + 32 * hh;
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int vrow = 4 * (grp >> 1) + (s16 >> 2);
+  const int vcol = 16 * (grp & 1) + 4 * (s16 & 3);
+  const uint32_t v_lane = kKRegion + (vrow >> 1) * kVPitch + 16 * (vrow & 1) + 32 * (vcol >> 3) + 2 * (vcol & 7);
+
+  auto mask = [&](f32x16_t& sv, int kbase, int h) {
+    if (!(lo_last <= kbase && kbase + kSub - 1 <= hi_first)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (key < lo[h] || key > hi[h]) sv[e] = kNegInf;
+      }
+    }
+  };
+  auto max16 = [](const f32x16_t& sv) {
+    float t = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    return fmaxf(t, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+  };
+
+  // S = K(slot) . Q^T for both halves: K fragments four ahead in a 5-slot ring, the
+  // half-1 Q fragments kQL..15 from LDS with them; dma(i) runs after step i
+  f32x16_t sc[2];
+  auto compute_s = [&](uint32_t ka, auto&& dma) {
+    uint4 kf[5], ql[5];
+    auto kread = [&](auto jc) {  // read j: K fragment j, and Q fragment j of half 1 when j >= kQL
+      constexpr int j = decltype(jc)::value;
+      kf[j % 5] = att_b128<64 * j>(ka);
+      if constexpr (j >= kQL) ql[j % 5] = att_b128<1024 * (j - kQL)>(q_lds);
+    };
+    StaticFor<0, 4>::run(kread);
+    StaticFor<0, KS>::run([&](auto ic) {
+      constexpr int ks = decltype(ic)::value;
+      constexpr int last = ks + 3 < KS - 1 ? ks + 3 : KS - 1;  // last read issued so far
+      constexpr int ops_last = last + 1 + (last >= kQL ? last - kQL + 1 : 0);
+      constexpr int ops_ks = ks + 1 + (ks >= kQL ? ks - kQL + 1 : 0);
+      DG_ATT_WAIT_LGKM(ops_last - ops_ks);
+      if constexpr (ks < KS - 1) {
+        mfma_v(sc[0], kf[ks % 5], qf[0][ks], ks == 0);
+        mfma_v(sc[1], kf[ks % 5], ks < kQL ? qf[1][ks] : ql[ks % 5], ks == 0);
+      } else {
+        mfma_v_last2(sc[0], sc[1], kf[ks % 5], qf[0][ks], ql[ks % 5]);
+      }
+      if constexpr (ks + 4 < KS) kread(std::integral_constant<int, ks + 4>{});
+      if constexpr (ks < 8) dma(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  f32x16_t o[2][DB];
+  float l_run[2];
+  float m_ref[2] = {kNegInf, kNegInf};
+  for (;;) {
+    if (tid == 0) redo_flag[0] = 0;
+    dma_rows(kb, lds0 + 3 * kAttStage, kKPitch, key0);
+    issue(0);
+    if (nsub > 1) issue(1);
+    if (nsub > 2) issue(2);
+    if (nsub > 2) DG_ATT_WAIT_VM(24);
+    else if (nsub > 1) DG_ATT_WAIT_VM(16);
+    else DG_ATT_WAIT_VM(8);
+    DG_ATT_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    compute_s(lbase + 3 * kAttStage + k_lane, [](int) {});
+    float m_seen[2] = {kNegInf, kNegInf};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      l_run[h] = 0.f;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[h][b][e] = 0.f;
+    }
+
+    bool overflow = false;
+    for (int sub = 0; sub < nsub; ++sub) {
+      const int left = nsub - 1 - sub;
+      if (left >= 2) DG_ATT_WAIT_VM(16);
+      else if (left == 1) DG_ATT_WAIT_VM(8);
+      else DG_ATT_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t ka = lbase + (sub & 3) * kAttStage + k_lane;
+      const uint32_t va = lbase + (sub & 3) * kAttStage + v_lane;
+      if (sub + 3 < nsub) issue(sub + 3);  // into the slot of sub-1, free since the barrier
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- softmax of S(sub), keys 0..15 (elements 0..7). Once every row has its
+      // reference, the row max (for the overflow test) waits until the MFMAs run.
+      uint2 vf[3][2];
+      auto vread = [&](auto fc) {  // fragment f = 8 kh + b: d block b, key half kh
+        constexpr int f = decltype(fc)::value;
+        constexpr int b = f & 7, kh = f >> 3;
+        vf[f % 3][0] = att_tr16<128 * b + 8 * kh * kVPitch>(va);
+        vf[f % 3][1] = att_tr16<128 * b + (8 * kh + 4) * kVPitch>(va);
+      };
+      vread(std::integral_constant<int, 0>{});
+      vread(std::integral_constant<int, 1>{});
+      mask(sc[0], key0 + kSub * sub, 0);
+      mask(sc[1], key0 + kSub * sub, 1);
+      auto row_max = [&](int h) {
+        const float t = half_max(max16(sc[h])) * a.scale_log2;
+        m_seen[h] = fmaxf(m_seen[h], t);
+        if (m_ref[h] == kNegInf) m_ref[h] = t;  // on a retry m_ref already covers this sub-tile
+        overflow |= t > m_ref[h] + kOverflow;
+      };
+      const bool late_max = !__any(m_ref[0] == kNegInf || m_ref[1] == kNegInf);  // uniform
+      if (!late_max) {
+        row_max(0);
+        row_max(1);
+      }
+      float mu[2];
+      uint4 pc[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mu[h] = m_ref[h] == kNegInf ? 0.f : m_ref[h];
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(sc[h][e], a.scale_log2, -mu[h]));
+          l_run[h] += p[e];
+        }
+        asm volatile("" : "+v"(l_run[h]));  // keep the sums here
+        pc[h][0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- O^T += V(sub)^T . P(sub)^T: 16 fragments (two V^T reads each, two ahead), each
+      // feeding both halves; P of keys 16..31 during the first eight, the late row max next
+      float pv[2][8];
+      StaticFor<0, 2 * DB>::run([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        constexpr int b = f & 7, kh = f >> 3;
+        DG_ATT_WAIT_LGKM(f < 2 * DB - 1 ? 2 : 0);
+        const bf16x8_t va8 = __builtin_bit_cast(
+            bf16x8_t, make_uint4(vf[f % 3][0].x, vf[f % 3][0].y, vf[f % 3][1].x, vf[f % 3][1].y));
+        o[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va8, __builtin_bit_cast(bf16x8_t, pc[0][kh]), o[0][b], 0, 0, 0);
+        o[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va8, __builtin_bit_cast(bf16x8_t, pc[1][kh]), o[1][b], 0, 0, 0);
+        if constexpr (f + 2 < 2 * DB) vread(std::integral_constant<int, f + 2>{});
+        if constexpr (f < 8) {
+          constexpr int h = f >> 2, e0 = 8 + 2 * (f & 3);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            pv[h][e0 - 8 + i] = fast_exp2(fmaf(sc[h][e0 + i], a.scale_log2, -mu[h]));
+            l_run[h] += pv[h][e0 - 8 + i];
+          }
+          asm volatile("" : "+v"(l_run[h]));
+          if constexpr ((f & 3) == 3)
+            pc[h][1] = make_uint4(pack_bf16(pv[h][0], pv[h][1]), pack_bf16(pv[h][2], pv[h][3]),
+                                  pack_bf16(pv[h][4], pv[h][5]), pack_bf16(pv[h][6], pv[h][7]));
+        }
+        if constexpr (f == 8 || f == 9) {
+          if (late_max) row_max(f - 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+
+      // ---- S(sub+1) = K(sub+1) . Q^T, with the refill of the ring slot of sub-1 (free
+      // since the barrier) spread over its first steps
+      if (sub + 1 < nsub) {
+        compute_s(ka, [](int) {});
+      }
+    }
+    if (__any(overflow) && lane == 0) redo_flag[0] = 1;
+    __syncthreads();
+    const int redo = redo_flag[0];
+    if (!redo) break;
+    __syncthreads();
+    m_ref[0] = fmaxf(m_ref[0], m_seen[0]);
+    m_ref[1] = fmaxf(m_ref[1], m_seen[1]);
+  }
+
+  // ---- epilogue: O (normalised, bf16) goes through LDS, the ring being free after the
+  // loop's final barrier, so that the global stores are whole rows: each wave stages
+  // its 64 rows at a 528-byte pitch, then writes 2 rows (1 KB) per store.
+  // o[h][b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][row h].
+  constexpr int kOPitch = 528;
+  char* ost = lds + wave * 64 * kOPitch;
+  float ltot[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ltot[h] = half_sum(l_run[h]);
+    const float inv = ltot[h] > 0.f ? 1.f / ltot[h] : 0.f;
+    char* orow = ost + (32 * h + l32) * kOPitch;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<uint2*>(orow + (32 * b + 8 * e4 + 4 * hh) * 2) =
+            make_uint2(pack_bf16(o[h][b][4 * e4] * inv, o[h][b][4 * e4 + 1] * inv),
+                       pack_bf16(o[h][b][4 * e4 + 2] * inv, o[h][b][4 * e4 + 3] * inv));
+  }
+  const int64_t prow0 = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kTile;
+  if (hh == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = row_of(h), tok = i0 + row / a.group, head = g * a.group + row % a.group;
+      if (tok >= sp.num_q) continue;
+      if (sp.num_chunks > 1)
+        *reinterpret_cast<float2*>(a.part_ml + (prow0 + row) * 2) = make_float2(m_ref[h], ltot[h]);
+      else if (a.lse)
+        a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref[h] + __builtin_amdgcn_logf(ltot[h])) * kLn2;
+    }
+  }
+  DG_ATT_WAIT_LGKM0();  // this wave's rows are in LDS (each wave reads only its own)
+  // store r covers rows 2r, 2r+1 of this wave: lane i takes 16 bytes i%32 of row 2r + i/32
+#pragma unroll 4
+  for (int r = 0; r < 32; ++r) {
+    const int lr = 2 * r + (lane >> 5);  // local row 0..63
+    const int row = wave * 64 + lr, tok = i0 + row / a.group, head = g * a.group + row % a.group;
+    const uint4 x = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + l32 * 16);
+    if (tok >= sp.num_q) continue;
+    char* dst = sp.num_chunks == 1
+                    ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2
+                    : reinterpret_cast<char*>(a.part_o) + (prow0 + row) * D * 2;
+    *reinterpret_cast<uint4*>(dst + l32 * 16) = x;
+  }
+}
+
 template <bool kBf16, int D>
-int launch_typed(const AttnArgs& args, const AttnPlan& plan, hipStream_t s) {
-  if (kBf16 && D == 256 && plan.dma)
-    hipLaunchKernelGGL(attn_fwd_bf16_d256, dim3(plan.num_work), dim3(kThreads), 0, s, args);
-  else
-    hipLaunchKernelGGL((attn_fwd<kBf16, D>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
-  if (plan.num_merge > 0)
-    hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge * merge_groups_per_unit<kBf16, D>()), dim3(kThreads), 0, s,
-                       args);
+int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
+  // work [0, num_wide): 64-rows-per-wave kernel; [num_wide, num_work): 128-row kernels
+  if constexpr (kBf16 && D == 256) {
+    if (plan.num_wide > 0) {
+      args.work_offset = 0;
+      hipLaunchKernelGGL(attn_fwd_bf16_d256_w64, dim3(plan.num_wide), dim3(kThreads), 0, s, args);
+    }
+  }
+  if (plan.num_work > plan.num_wide) {
+    args.work_offset = plan.num_wide;
+    const dim3 grid(plan.num_work - plan.num_wide);
+    if (kBf16 && D == 256 && plan.dma)
+      hipLaunchKernelGGL(attn_fwd_bf16_d256, grid, dim3(kThreads), 0, s, args);
+    else
+      hipLaunchKernelGGL((attn_fwd<kBf16, D>), grid, dim3(kThreads), 0, s, args);
+  }
+  if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
   return (int)hipGetLastError();
 }
 
@@ -812,13 +1193,13 @@ int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream) {
   args.out = a->out;
   args.lse = a->lse;
   char* ws = reinterpret_cast<char*>(a->workspace);
-  args.part_o = plan.num_parts ? reinterpret_cast<void*>(ws + plan.part_o_offset) : nullptr;
-  args.part_ml = plan.num_parts ? reinterpret_cast<float*>(ws + plan.part_ml_offset) : nullptr;
+  args.part_o = plan.part_rows ? reinterpret_cast<void*>(ws + plan.part_o_offset) : nullptr;
+  args.part_ml = plan.part_rows ? reinterpret_cast<float*>(ws + plan.part_ml_offset) : nullptr;
   args.hq = a->num_q_heads;
   args.hkv = a->num_kv_heads;
   args.group = plan.group;
   args.window = a->window;
-  args.tokens_per_tile = plan.tokens_per_tile;
+  args.work_offset = 0;
   args.num_seqs = plan.num_seqs;
   const float scale = a->scale > 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   args.scale_log2 = scale * kLog2e;

@@ -48,9 +48,9 @@ void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int*
 // kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write and read.
 
 static constexpr int kKeyTile = kAttnKeyTile;
-static constexpr int kTileRows = kAttnTileRows;
 static constexpr int kTargetGroups = 256;
 static constexpr int kMinChunkTiles = 4;
+static constexpr int kWideMinSub = 16;
 
 dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
@@ -91,18 +91,22 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   for (size_t i = 1; i < qranges.size(); ++i)
     if (qranges[i].first < qranges[i - 1].second) return bad(DG_ERR_INVALID_ARG, "seq query ranges overlap");
 
-  // tiles and chunks; the split of a request depends on that request alone, so its
-  // result is the same whatever else is in the batch
-  const int tok_per_tile = kTileRows / G;
-  int64_t num_work = 0, num_merge = 0, num_parts = 0;
-  plan->num_seqs = a->num_seqs;
+  // tiles and chunks; the split of a request, and the kernel that runs it, depend on
+  // that request alone, so its result is the same whatever else is in the batch.
+  // The LDS-DMA kernels (bf16, head_dim 256) take 32-bit byte offsets within a request's K/V.
   plan->dma = a->dtype == DG_BF16 && a->head_dim == 256;
   for (int s = 0; s < a->num_seqs; ++s) {
     const dg_seq& q = a->seqs[s];
-    const int64_t ntiles_q = ceil_div(q.num_q, tok_per_tile);
+    if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
+  }
+  // q tiles and key chunks of request q at a given tile height
+  struct Split { int64_t ntiles_q, nch, chunk_tiles, sub_tiles; };
+  auto split = [&](const dg_seq& q, int tile_rows) {
+    const int tok = tile_rows / G;
+    Split r{ceil_div(q.num_q, tok), 0, 0, 0};
     int64_t max_tiles = 0, units = 0;
-    for (int t = 0; t < ntiles_q; ++t) {
-      const int i0 = t * tok_per_tile, i1 = std::min<int>(q.num_q, i0 + tok_per_tile) - 1;
+    for (int t = 0; t < r.ntiles_q; ++t) {
+      const int i0 = t * tok, i1 = std::min<int>(q.num_q, i0 + tok) - 1;
       int lo0, hi0, lo1, hi1;
       key_range(q.mode, q.prefix_len, q.num_q, a->window, i0, &lo0, &hi0);
       key_range(q.mode, q.prefix_len, q.num_q, a->window, i1, &lo1, &hi1);
@@ -110,39 +114,73 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
       max_tiles = std::max(max_tiles, nt);
       units += nt * a->num_kv_heads;
     }
-    int64_t chunk_tiles;
-    if (a->kv_chunk > 0) chunk_tiles = a->kv_chunk / kKeyTile;
-    else chunk_tiles = std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
-    const int64_t nch = max_tiles > 0 ? ceil_div(max_tiles, chunk_tiles) : 0;
-    if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
-    AttnSeqPlan& sp = plan->seqs[s];
-    sp.q_start = q.q_start;
-    sp.num_q = q.num_q;
-    sp.kv_start = q.kv_start;
-    sp.prefix_len = q.prefix_len;
-    sp.mode = q.mode;
-    sp.num_chunks = (int32_t)nch;
-    sp.chunk_tiles = (int32_t)std::min<int64_t>(chunk_tiles, INT32_MAX);
-    sp.work_begin = (int32_t)num_work;
-    sp.merge_begin = (int32_t)num_merge;
-    sp.part_begin = (int32_t)num_parts;
-    num_work += a->num_kv_heads * ntiles_q * nch;
-    if (nch > 1) {
-      num_merge += a->num_kv_heads * ntiles_q;
-      num_parts += a->num_kv_heads * ntiles_q * nch;
+    if (a->kv_chunk > 0) r.chunk_tiles = a->kv_chunk / kKeyTile;
+    else r.chunk_tiles = std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
+    r.nch = max_tiles > 0 ? ceil_div(max_tiles, r.chunk_tiles) : 0;
+    r.sub_tiles = units * (kKeyTile / 32);  // 32-key sub-tiles over all (q tile, kv head) units
+    return r;
+  };
+  // The 64-rows-per-wave kernel has the faster loop but the larger fixed cost (prologue,
+  // epilogue, twice the rows per work group): it takes a request whose work groups
+  // average at least kWideMinSub sub-tiles.
+  bool wide[DG_MAX_SEQS];
+  Split sq[DG_MAX_SEQS];
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const dg_seq& q = a->seqs[s];
+    wide[s] = false;
+    if (plan->dma && q.num_q > 0) {
+      const Split w = split(q, kAttnWideTileRows);
+      const int64_t groups = w.ntiles_q * w.nch * a->num_kv_heads;
+      wide[s] = groups > 0 && w.sub_tiles >= kWideMinSub * groups;
+      if (wide[s]) sq[s] = w;
     }
-    if (num_work > INT32_MAX / 2 || num_parts > INT32_MAX / 2) return bad(DG_ERR_UNSUPPORTED, "too much work for one call");
+    if (!wide[s]) sq[s] = split(q, kAttnTileRows);
   }
+  const int mrpg = attn_merge_rows_per_group(a->dtype == DG_BF16, a->head_dim);
+  int64_t num_work = 0, num_merge = 0, part_rows = 0, num_wide = 0;
+  plan->num_seqs = a->num_seqs;
+  for (int pass = 0; pass < 2; ++pass)  // wide requests' work first
+    for (int s = 0; s < a->num_seqs; ++s) {
+      if (wide[s] != (pass == 0)) continue;
+      const dg_seq& q = a->seqs[s];
+      const Split& r = sq[s];
+      const int tile_rows = wide[s] ? kAttnWideTileRows : kAttnTileRows;
+      AttnSeqPlan& sp = plan->seqs[s];
+      sp.q_start = q.q_start;
+      sp.num_q = q.num_q;
+      sp.kv_start = q.kv_start;
+      sp.prefix_len = q.prefix_len;
+      sp.mode = q.mode;
+      sp.tile_rows = tile_rows;
+      sp.tokens_per_tile = tile_rows / G;
+      sp.num_chunks = (int32_t)r.nch;
+      sp.chunk_tiles = (int32_t)std::min<int64_t>(r.chunk_tiles, INT32_MAX);
+      const int64_t units = a->num_kv_heads * r.ntiles_q;
+      sp.work_begin = (int32_t)num_work;
+      sp.work_count = (int32_t)std::min<int64_t>(units * r.nch, INT32_MAX);
+      sp.merge_begin = (int32_t)num_merge;
+      sp.merge_count = 0;
+      sp.part_begin = (int32_t)std::min<int64_t>(part_rows, INT32_MAX);
+      num_work += units * r.nch;
+      if (wide[s]) num_wide += units * r.nch;
+      if (r.nch > 1) {
+        sp.merge_count = (int32_t)std::min<int64_t>(units * (tile_rows / mrpg), INT32_MAX);
+        num_merge += units * (tile_rows / mrpg);
+        part_rows += units * r.nch * tile_rows;
+      }
+      if (num_work > INT32_MAX / 2 || num_merge > INT32_MAX / 2 || part_rows > INT32_MAX / 2)
+        return bad(DG_ERR_UNSUPPORTED, "too much work for one call");
+    }
   plan->group = G;
-  plan->tokens_per_tile = tok_per_tile;
+  plan->num_wide = (int)num_wide;
   plan->num_work = (int)num_work;
   plan->num_merge = (int)num_merge;
-  plan->num_parts = (int)num_parts;
+  plan->part_rows = part_rows;
   plan->part_o_offset = 0;
-  const size_t o_bytes = (size_t)num_parts * kTileRows * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);
+  const size_t o_bytes = (size_t)part_rows * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);
   plan->part_ml_offset = align_up(o_bytes, 256);
-  const size_t ml_bytes = (size_t)num_parts * kTileRows * 2 * sizeof(float);
-  plan->bytes = num_parts ? align_up(plan->part_ml_offset + ml_bytes, 256) : 0;
+  const size_t ml_bytes = (size_t)part_rows * 2 * sizeof(float);
+  plan->bytes = part_rows ? align_up(plan->part_ml_offset + ml_bytes, 256) : 0;
   return DG_OK;
 }
 

@@ -12,34 +12,41 @@ namespace dg {
 
 // ---- attention ---------------------------------------------------------------
 //
-// Work is laid out per request as [kv head][q tile][key chunk]. A q tile holds
-// kTileRows query rows (tokens x grouped heads); a key chunk is a run of 64-key
+// Work is laid out per request as [kv head][key chunk][q tile]. A q tile holds
+// tile_rows query rows (tokens x grouped heads); a key chunk is a run of 64-key
 // tiles. Every q tile of a request gets the same number of chunks (a chunk past a
 // tile's keys is empty and exits at once). The kernel finds its (request, head,
 // tile, chunk) from this table, so no work list has to be copied to the device.
 
 constexpr int kAttnKeyTile = 64;
-constexpr int kAttnTileRows = 128;
+constexpr int kAttnTileRows = 128;      // q tile of the general kernel
+constexpr int kAttnWideTileRows = 256;  // q tile of the bf16 head_dim-256 kernel (64 rows per wave)
+// Rows of one merge work group (256 threads, one per 16 bytes of a partial row).
+constexpr int attn_merge_rows_per_group(bool bf16, int head_dim) { return 256 / (head_dim / (bf16 ? 8 : 4)); }
 
 struct AttnSeqPlan {
   int32_t q_start, num_q, kv_start, prefix_len, mode;
-  int32_t num_chunks;   // key chunks per q tile
-  int32_t chunk_tiles;  // 64-key tiles per chunk (depends on this request only)
-  int32_t work_begin;   // first work-group index of this request
-  int32_t merge_begin;  // first merge index (requests with num_chunks > 1)
-  int32_t part_begin;   // first partial slot (requests with num_chunks > 1)
+  int32_t tile_rows;        // query rows per q tile: kAttnWideTileRows or kAttnTileRows
+  int32_t tokens_per_tile;  // tile_rows / G
+  int32_t num_chunks;       // key chunks per q tile
+  int32_t chunk_tiles;      // 64-key tiles per chunk (depends on this request only)
+  int32_t work_begin;       // first work-group index of this request
+  int32_t work_count;       // its work groups
+  int32_t merge_begin;      // first merge work group (requests with num_chunks > 1)
+  int32_t merge_count;      // its merge work groups
+  int32_t part_begin;       // first partial row (requests with num_chunks > 1)
 };
 
 struct AttnPlan {
   int num_seqs;
   int group;            // G = Hq / Hkv
-  int tokens_per_tile;  // kAttnTileRows / G
-  int num_work;         // work groups of the attention kernel
+  int num_wide;         // work groups of the 64-rows-per-wave kernel: work [0, num_wide)
+  int num_work;         // all attention work groups; [num_wide, num_work) run the 128-row kernels
   int num_merge;        // work groups of the merge kernel
-  int num_parts;        // partial slots
+  int64_t part_rows;    // partial rows (each D wide)
   int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB: LDS-DMA kernel
-  size_t part_o_offset;   // workspace: [num_parts][kAttnTileRows][D] partial outputs, input dtype
-  size_t part_ml_offset;  // workspace: [num_parts][kAttnTileRows][2] fp32 (max, sum) in log2 units
+  size_t part_o_offset;   // workspace: [part_rows][D] partial outputs, input dtype
+  size_t part_ml_offset;  // workspace: [part_rows][2] fp32 (max, sum) in log2 units
   size_t bytes;
   AttnSeqPlan seqs[DG_MAX_SEQS];
 };
