@@ -767,29 +767,43 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
     m_ref = fmaxf(m_ref, m_seen);
   }
 
-  // ---- epilogue: o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]
+  // ---- epilogue: O (normalised, bf16) goes through LDS, the ring being free after the
+  // loop's final barrier, so that the global stores are whole rows: each wave stages its
+  // 32 rows at a 528-byte pitch, then writes 2 rows (1 KB) per store.
+  // o[b][e] = O^T[d = 32b + 8(e/4) + 4hh + e%4][this lane's row]
+  constexpr int kOPitch = 528;
+  char* ost = lds + wave * 32 * kOPitch;
   const float l_tot = half_sum(l_run);
-  if (!valid) return;
   {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t prow = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kRows + row;
-    char* orow = sp.num_chunks == 1
-                     ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2
-                     : reinterpret_cast<char*>(a.part_o) + prow * D * 2;
+    char* orow = ost + l32 * kOPitch;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int d = 32 * b + 8 * e4 + 4 * hh;
-        *reinterpret_cast<uint2*>(orow + d * 2) = make_uint2(pack_bf16(o[b][4 * e4] * inv, o[b][4 * e4 + 1] * inv),
-                                                             pack_bf16(o[b][4 * e4 + 2] * inv, o[b][4 * e4 + 3] * inv));
-      }
-    if (hh == 0) {
-      if (sp.num_chunks > 1)
-        *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m_ref, l_tot);
-      else if (a.lse)
-        a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    }
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<uint2*>(orow + (32 * b + 8 * e4 + 4 * hh) * 2) =
+            make_uint2(pack_bf16(o[b][4 * e4] * inv, o[b][4 * e4 + 1] * inv),
+                       pack_bf16(o[b][4 * e4 + 2] * inv, o[b][4 * e4 + 3] * inv));
+  }
+  const int64_t prow0 = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kRows;
+  if (valid && hh == 0) {
+    if (sp.num_chunks > 1)
+      *reinterpret_cast<float2*>(a.part_ml + (prow0 + row) * 2) = make_float2(m_ref, l_tot);
+    else if (a.lse)
+      a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+  DG_ATT_WAIT_LGKM0();  // this wave's rows are in LDS (each wave reads only its own)
+  // store r covers rows 2r, 2r+1 of this wave: lane i takes 16 bytes i%32 of row 2r + i/32
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const int lr = 2 * r + hh;  // local row 0..31
+    const int srow = wave * 32 + lr, stok = i0 + srow / a.group, shead = g * a.group + srow % a.group;
+    const uint4 x = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + l32 * 16);
+    if (stok >= sp.num_q) continue;
+    char* dst = sp.num_chunks == 1
+                    ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + stok) * a.hq + shead) * D * 2
+                    : reinterpret_cast<char*>(a.part_o) + (prow0 + srow) * D * 2;
+    *reinterpret_cast<uint4*>(dst + l32 * 16) = x;
   }
 }
 
