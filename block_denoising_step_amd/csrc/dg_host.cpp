@@ -42,7 +42,8 @@ void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int*
 // ---- attention plan ----------------------------------------------------------
 //
 // A request with a single chunk per q tile writes its output directly; one with
-// several writes fp32 partials that the merge kernel combines in chunk order.
+// several writes partials (each chunk's output normalised by that chunk's sum, in the
+// input dtype, plus its (max, sum) in fp32) that the merge kernel combines in chunk order.
 // A request's chunk length gives it about kTargetGroups work groups (one per compute
 // unit: a work group of the bf16 head_dim-256 kernel fills a CU), but never under
 // kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write and read.
