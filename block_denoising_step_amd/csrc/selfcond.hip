@@ -405,7 +405,7 @@ __device__ __forceinline__ uint32_t a_off(int r, int c) { return r * 64 + ((c ^ 
 // BM x BN tile: 256 x 256 (5-stage ring), or 128 x 512 (4-stage ring) whose stages
 // hold 8 KB of P and 32 KB of E, so more of E - the stream from HBM - is in flight.
 constexpr int kDmaThreads = 512;
-constexpr int kDmaWaves = kDmaThreads / 64;
+constexpr int kDmaIssuers = 4;  // waves that refill the ring (one per SIMD)
 
 template <int BN>
 struct DmaTile {
@@ -416,8 +416,10 @@ struct DmaTile {
   static constexpr int kStageB = kDmaBK * kRowB;
   static constexpr int kStageBytes = kStageA + kStageB;
   static constexpr int kStages = 163840 / kStageBytes;  // 5 or 4
-  static constexpr int kSegA = kStageA / 1024 / kDmaWaves;  // 1 KB DMA segments per wave
-  static constexpr int kSegB = kStageB / 1024 / kDmaWaves;
+  // The ring is refilled by the first kDmaIssuers waves (one per SIMD): while one wave
+  // of a SIMD issues its copies, the other keeps the matrix core busy.
+  static constexpr int kSegA = kStageA / 1024 / kDmaIssuers;  // 1 KB DMA segments per issuing wave
+  static constexpr int kSegB = kStageB / 1024 / kDmaIssuers;
   static constexpr int kRowsPerSegB = 1024 / kRowB;    // k rows per B segment (2 or 1)
 };
 
@@ -434,17 +436,19 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   const int h = lane >> 5, l32 = lane & 31;
   const int wm = (wave / T::kWN) * 64, wn = (wave % T::kWN) * 128;
 
-  // Per-lane DMA sources. Wave w fills A segments kSegA*w .. and B segments kSegB*w ..
-  // (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the lane fetches the
-  // chunk that the swizzle puts in its slot. Rows past M and columns past d are
-  // clamped to valid memory; their results are never stored.
+  // Per-lane DMA sources. Issuing wave w fills A segments kSegA*w .. and B segments
+  // kSegB*w .. (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the lane
+  // fetches the chunk that the swizzle puts in its slot. Rows past M and columns past d
+  // are clamped to valid memory; their results are never stored. The other waves
+  // compute the same pointers as wave w % kDmaIssuers and never use them.
+  const int dw = wave % kDmaIssuers;
   const char* psrc[kSegA];
   const char* esrc[kSegB];
   const char* pb = reinterpret_cast<const char*>(g.p);
   const char* eb = reinterpret_cast<const char*>(g.e);
 #pragma unroll
   for (int t = 0; t < kSegA; ++t) {
-    const int seg = kSegA * wave + t;
+    const int seg = kSegA * dw + t;
     const int r = seg * 16 + (lane >> 2);         // A row within the tile
     const int ca = (lane & 3) ^ swa(r);           // logical chunk stored in this slot
     const int grow = min(ti.m0 + r, g.M - 1);
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   }
 #pragma unroll
   for (int t = 0; t < kSegB; ++t) {
-    const int seg = kSegB * wave + t;
+    const int seg = kSegB * dw + t;
     const int kk = seg * T::kRowsPerSegB + (T::kRowsPerSegB == 2 ? (lane >> 5) : 0);  // B k row
     const int cb = (T::kRowsPerSegB == 2 ? (lane & 31) : lane) ^ swb(kk);
     const int gcol = min(ti.n0 + cb * 8, g.d - 8);
@@ -464,19 +468,20 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
 
   auto issue = [&](int s) {
+    if (wave >= kDmaIssuers) return;  // uniform
     __attribute__((address_space(3))) char* st = lds0 + (s % kStages) * kStageBytes;
 #pragma unroll
     for (int t = 0; t < kSegA; ++t)
       __builtin_amdgcn_global_load_lds((const void*)(psrc[t] + s * pstep),
-                                       (__attribute__((address_space(3))) void*)(st + (kSegA * wave + t) * 1024), 16, 0,
+                                       (__attribute__((address_space(3))) void*)(st + (kSegA * dw + t) * 1024), 16, 0,
                                        0);
 #pragma unroll
     for (int t = 0; t < kSegB; ++t)
       __builtin_amdgcn_global_load_lds((const void*)(esrc[t] + s * estep),
-                                       (__attribute__((address_space(3))) void*)(st + kStageA + (kSegB * wave + t) * 1024),
+                                       (__attribute__((address_space(3))) void*)(st + kStageA + (kSegB * dw + t) * 1024),
                                        16, 0, 0);
   };
-  constexpr int kGroup = kSegA + kSegB;  // DMA instructions per stage per wave
+  constexpr int kGroup = kSegA + kSegB;  // DMA instructions per stage per issuing wave (0 for the others)
 
   f32x16_t acc[2][4];
 #pragma unroll
