@@ -261,8 +261,10 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   plan->tile_k = plan->dma ? 32 : (a->dtype == DG_BF16 ? 64 : 32);
   plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
   plan->n_tiles = (int)ceil_div(a->d, plan->tile_n);
-  // split-K: about one work group per CU, in slices of at least kMinSteps K steps
-  constexpr int64_t kCUs = 256, kMinSteps = 8;
+  // split-K: about one work group per CU, in slices of at least kMinSteps K steps (one
+  // for fp32, whose MFMA rate makes a single 256 x 256 tile's slice compute-bound)
+  constexpr int64_t kCUs = 256;
+  const int64_t kMinSteps = a->dtype == DG_F32 ? 1 : 8;
   const int64_t base = (int64_t)plan->m_tiles * plan->n_tiles;
   const int64_t target = std::max<int64_t>(1, ceil_div(kCUs, base));
   int64_t k_per_split;

@@ -600,8 +600,22 @@ __global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict_
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
   if (i >= per_split) return;
+  // slices added in order; loads in batches of 8, all issued before the adds
   float4 s = part[i];
-  for (int k = 1; k < splits; ++k) {
+  int k = 1;
+  for (; k + 8 <= splits; k += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = part[(int64_t)(k + t) * per_split + i];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      s.x += v[t].x;
+      s.y += v[t].y;
+      s.z += v[t].z;
+      s.w += v[t].w;
+    }
+  }
+  for (; k < splits; ++k) {
     const float4 v = part[(int64_t)k * per_split + i];
     s.x += v.x;
     s.y += v.y;
