@@ -45,8 +45,9 @@ void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int*
 // several writes partials (each chunk's output normalised by that chunk's sum, in the
 // input dtype, plus its (max, sum) in fp32) that the merge kernel combines in chunk order.
 // A request's chunk length gives it about kTargetGroups work groups (one per compute
-// unit: a work group of the bf16 head_dim-256 kernel fills a CU), but never under
-// kMinChunkTiles tiles, since every partial costs a [128 x D] fp32 write and read.
+// unit: a work group of the bf16 head_dim-256 kernels fills a CU), but never under
+// kMinChunkTiles tiles, since every partial costs a [tile rows x D] write and read,
+// unless the request is too small to reach kTargetGroups work groups at all.
 
 static constexpr int kKeyTile = kAttnKeyTile;
 static constexpr int kTargetGroups = 256;
@@ -116,7 +117,8 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
       units += nt * a->num_kv_heads;
     }
     if (a->kv_chunk > 0) r.chunk_tiles = a->kv_chunk / kKeyTile;
-    else r.chunk_tiles = std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
+    // a request too small to fill the GPU even at one tile per chunk takes one-tile chunks
+    else r.chunk_tiles = units < kTargetGroups ? 1 : std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
     r.nch = max_tiles > 0 ? ceil_div(max_tiles, r.chunk_tiles) : 0;
     r.sub_tiles = units * (kKeyTile / 32);  // 32-key sub-tiles over all (q tile, kv head) units
     return r;

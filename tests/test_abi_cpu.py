@@ -111,8 +111,13 @@ def test_attn_fp32_head_dim_256_unsupported_and_workspace():
 
 
 def test_attn_workspace_single_chunk_is_zero():
+    # a chunk covering all 96 keys leaves one chunk per q tile: no partials
     a = _attn()
+    a.kv_chunk = 128
     assert dg.attn_workspace_size(a) == 0
+    # left to the planner, a request this small is split into one-tile chunks
+    a.kv_chunk = 0
+    assert dg.attn_workspace_size(a) > 0
 
 
 def _sampler(**over):
