@@ -13,7 +13,7 @@ What is computed, and where the pages state it:
     bidirectional one sees W on each side, 2W+1 in all - [P1] section
     "대칭 슬라이딩 윈도우 어텐션", [P3] (the +-W windows of decoder mode).
 
-Readings taken where the pages leave a step open (each listed in the design doc):
+Readings taken where the pages leave a step open:
   * the one-sided window holds the W preceding tokens plus the token itself (W+1 keys);
   * window bounds are absolute positions over [cache || new tokens], clipped to the
     request's own keys; requests never see each other;

@@ -17,7 +17,7 @@ What is computed, and where the pages state it:
     "샘플링 루프와 엔트로피 경계 디노이징"; [P2] Sudoku showcase (48-step limit,
     adaptive stopping).
 
-Readings taken where the pages leave a step open (each listed in the design doc):
+Readings taken where the pages leave a step open:
   * confidence c = -H (entropy in nats); order by c descending, then position
     ascending; a max-probability confidence is available as an option;
   * the accepted set is the longest confidence-ordered prefix whose entropy total is

@@ -46,45 +46,45 @@ def _compare(seqs, window, q, k, v, hq, hkv, bf16, rows=None, kv_chunk=0, label=
 
 @pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
 @pytest.mark.parametrize("window", [32, -1])
-def test_config1_fp32(mode, window):
+def test_fp32_canvas256_prefix256_heads4_d64(mode, window):
     c = attn_case(1).with_mode(mode).with_window(window)
     q, k, v = c.tensors()
-    err, _ = _compare(c.seqs, window, q, k, v, c.num_q_heads, c.num_kv_heads, False, label=f"config 1 mode={mode}")
+    err, _ = _compare(c.seqs, window, q, k, v, c.num_q_heads, c.num_kv_heads, False, label=f"fp32 canvas 256 prefix 256 mode={mode}")
     assert err < 1e-4
 
 
-def test_config2_bf16_all_rows():
+def test_bf16_canvas256_prefix4096_all_rows():
     c = attn_case(2)
     q, k, v = c.tensors()
-    _compare(c.seqs, -1, q, k, v, 16, 8, True, label="config 2 bidir global P=4096")
+    _compare(c.seqs, -1, q, k, v, 16, 8, True, label="bf16 bidir global canvas 256 prefix 4096")
 
 
 @pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
-def test_config3_window_512_sampled(mode):
+def test_bf16_window512_prefix32768_sampled(mode):
     c = attn_case(3).with_mode(mode)
     q, k, v = c.tensors()
     rows = [0, 1, 63, 64, 100, 191, 192, 200, 254, 255]
-    _compare(c.seqs, 512, q, k, v, 16, 8, True, rows=rows, label=f"config 3 W=512 mode={mode}")
+    _compare(c.seqs, 512, q, k, v, 16, 8, True, rows=rows, label=f"bf16 W=512 prefix 32768 mode={mode}")
 
 
 @pytest.mark.parametrize("window", [-1, 512])
-def test_config4_mixed_batch_sampled(window):
+def test_bf16_mixed_four_request_batch_sampled(window):
     c = attn_case(4)
     q, k, v = c.tensors()
     rows = []
     for s in c.seqs:
         rows += [s.q_start, s.q_start + 1, s.q_start + s.num_q // 2, s.q_start + s.num_q - 1]
     rows += [700, 1500, 2047]
-    _compare(c.seqs, window, q, k, v, 16, 8, True, rows=sorted(set(rows)), label=f"config 4 mixed W={window}")
+    _compare(c.seqs, window, q, k, v, 16, 8, True, rows=sorted(set(rows)), label=f"bf16 mixed 4-request batch W={window}")
 
 
-def test_config5_long_context_sampled():
+def test_bf16_prefixes_to_262144_sampled():
     c = attn_case(5)
     q, k, v = c.tensors()
     rows = []
     for s in c.seqs:
         rows += [s.q_start, s.q_start + 129, s.q_start + s.num_q - 1]
-    _compare(c.seqs, -1, q, k, v, 16, 8, True, rows=rows, label="config 5 long context")
+    _compare(c.seqs, -1, q, k, v, 16, 8, True, rows=rows, label="bf16 prefixes 262144/131072/65536/4096")
 
 
 @pytest.mark.parametrize("D,bf16", [(64, True), (128, True), (256, True), (64, False), (128, False)])

@@ -113,23 +113,23 @@ def _run(logits_np, bf16, reqs, V, budget, min_accept=1, conf_mode=CONF_NEG_ENTR
     return b2, ref2
 
 
-def test_config1_fp32():
+def test_fp32_256x4096():
     c = sampler_case(1)
     l = synth_logits(1, c.total_rows, c.vocab, bf16=False)
-    _run(l, False, [(0, 256, request_seeds(1, 1)[0], 0)], c.vocab, c.budget, label="config 1 fp32 256x4096")
+    _run(l, False, [(0, 256, request_seeds(1, 1)[0], 0)], c.vocab, c.budget, label="fp32 256x4096")
 
 
-def test_config2_bf16_full_size():
+def test_bf16_256x262144():
     c = sampler_case(2)
     l = synth_logits(2, c.total_rows, c.vocab, bf16=True)
-    _run(l, True, [(0, 256, request_seeds(2, 1)[0], 0)], c.vocab, c.budget, label="config 2 bf16 256x262144")
+    _run(l, True, [(0, 256, request_seeds(2, 1)[0], 0)], c.vocab, c.budget, label="bf16 256x262144")
 
 
-def test_config4_two_denoise_requests_bf16():
+def test_bf16_two_denoise_requests_512x262144():
     c = sampler_case(4)
     l = synth_logits(4, c.total_rows, c.vocab, bf16=True)
     s = request_seeds(4, 2)
-    _run(l, True, [(0, 256, s[0], 3), (256, 256, s[1], 5)], c.vocab, c.budget, label="config 4 bf16 512x262144")
+    _run(l, True, [(0, 256, s[0], 3), (256, 256, s[1], 5)], c.vocab, c.budget, label="bf16 two requests 512x262144")
 
 
 @pytest.mark.parametrize("bf16", [False, True])

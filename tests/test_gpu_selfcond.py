@@ -23,7 +23,7 @@ def _stats_dev(l_np):
     return dev(st["max"].astype(np.float32)), dev(st["sum"].astype(np.float32))
 
 
-def test_config1_fp32_probs_and_fused():
+def test_fp32_256x4096x256_probs_and_fused():
     E = embed_table(1, 4096, 256, bf16=False)
     l = synth_logits(1, 256, 4096, bf16=False)
     want = selfcond_embed(E, logits=l)
@@ -38,12 +38,12 @@ def test_config1_fp32_probs_and_fused():
     dg.dg_selfcond_embed(lt, Et, out2, row_max=rm, row_sum=rs)
     torch.cuda.synchronize()
     e2 = max_rel_rows(host(out2), want)
-    say(f"[selfcond] config 1 fp32: probs max-rel {e1:.3e}, fused max-rel {e2:.3e}")
+    say(f"[selfcond] fp32 256x4096x256: probs max-rel {e1:.3e}, fused max-rel {e2:.3e}")
     assert e1 <= TOL and e2 <= TOL
     assert e1 < 1e-4 and e2 < 1e-4  # fp32 path is far inside the bar
 
 
-def test_config2_bf16_full_size_sampled_rows():
+def test_bf16_256x262144x2048_sampled_rows():
     V, d, M = 262144, 2048, 256
     E = embed_table(2, V, d, bf16=True)
     l = synth_logits(2, M, V, bf16=True)
@@ -55,7 +55,7 @@ def test_config2_bf16_full_size_sampled_rows():
     rows = [0, 1, 17, 63, 128, 200, 254, 255]
     want = selfcond_embed(E, logits=l[rows])
     err = max_rel_rows(host(out)[rows], want)
-    say(f"[selfcond] config 2 bf16 fused, rows {rows}: max-rel {err:.3e}")
+    say(f"[selfcond] bf16 256x262144x2048 fused, rows {rows}: max-rel {err:.3e}")
     assert err <= TOL
     # materialised-probability mode on the same rows
     p = dev(softmax_rows(l).astype(np.float32), True)
@@ -64,7 +64,7 @@ def test_config2_bf16_full_size_sampled_rows():
     torch.cuda.synchronize()
     want2 = selfcond_embed(E, probs=round_to_bf16(softmax_rows(l[rows]).astype(np.float32)))
     err2 = max_rel_rows(host(out2)[rows], want2)
-    say(f"[selfcond] config 2 bf16 probs: max-rel {err2:.3e}")
+    say(f"[selfcond] bf16 256x262144x2048 probs: max-rel {err2:.3e}")
     assert err2 <= TOL
 
 

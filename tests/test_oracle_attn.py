@@ -105,7 +105,7 @@ def _key_sets_via_onehot(mode, P, N, W):
     return out[:, 0, :], lse[:, 0]
 
 
-def test_window_cover_bidir_config1_shape():
+def test_window_cover_bidir_canvas256_prefix256():
     """P-A3: a bidirectional query sees 2W+1 keys where the window fits (the canvas
     of 256 tokens on a 256-token prefix with W = 32), and the clipped count at the end."""
     P, N, W = 256, 256, 32

@@ -164,17 +164,17 @@ def pack_seqs(spec: List[Tuple[int, int, int]]) -> List[Seq]:
 
 def attn_case(cfg: int) -> AttnCase:
     if cfg == 1:
-        return AttnCase("cfg1-bidir-w32", pack_seqs([(256, 256, BIDIR)]), 32, 4, 4, 64, False, 1)
+        return AttnCase("fp32 canvas 256 prefix 256 W=32", pack_seqs([(256, 256, BIDIR)]), 32, 4, 4, 64, False, 1)
     if cfg == 2:
-        return AttnCase("cfg2-bidir-global", pack_seqs([(4096, 256, BIDIR)]), -1, 16, 8, 256, True, 2)
+        return AttnCase("bf16 canvas 256 prefix 4096 global", pack_seqs([(4096, 256, BIDIR)]), -1, 16, 8, 256, True, 2)
     if cfg == 3:
-        return AttnCase("cfg3-bidir-w512", pack_seqs([(32768, 256, BIDIR)]), 512, 16, 8, 256, True, 3)
+        return AttnCase("bf16 canvas 256 prefix 32768 W=512", pack_seqs([(32768, 256, BIDIR)]), 512, 16, 8, 256, True, 3)
     if cfg == 4:
-        return AttnCase("cfg4-mixed-global",
+        return AttnCase("bf16 mixed 4-request batch",
                         pack_seqs([(0, 2048, CAUSAL), (8192, 256, CAUSAL), (1024, 256, BIDIR), (16384, 256, BIDIR)]),
                         -1, 16, 8, 256, True, 4)
     if cfg == 5:
-        return AttnCase("cfg5-long-bidir-global",
+        return AttnCase("bf16 prefixes 262144/131072/65536/4096",
                         pack_seqs([(262144, 256, BIDIR), (131072, 256, BIDIR), (65536, 256, BIDIR), (4096, 256, BIDIR)]),
                         -1, 16, 8, 256, True, 5)
     raise ValueError(cfg)
