@@ -143,3 +143,44 @@ def test_score_jump_far_past_first_tile(D, bf16):
     seqs = pack_seqs([(P, N, BIDIR)])
     for chunk in (0, 64):
         _compare(seqs, -1, q, k, v, H, H, bf16, kv_chunk=chunk, scale=1.0, label=f"score jump D={D}")
+
+
+# Requests long enough, with chunks long enough, that the planner runs them on the
+# 64-rows-per-wave kernel (work groups averaging at least 16 sub-tiles): masks, windows,
+# group sizes, ragged q tiles, 256-row partials and the merge over them.
+WIDE_CASES = [
+    # mode, window, G, N, kv_chunk
+    (BIDIR, -1, 2, 200, 1024),
+    (CAUSAL, -1, 2, 200, 1024),
+    (BIDIR, 300, 2, 200, 1024),
+    (CAUSAL, 1000, 4, 130, 4096),
+    (BIDIR, 700, 1, 64, 2048),
+    (BIDIR, -1, 8, 100, 1024),
+]
+
+
+@pytest.mark.parametrize("mode,window,G,N,chunk", WIDE_CASES)
+def test_wide_kernel_cases(mode, window, G, N, chunk):
+    P, hkv, D = 2048, 2, 256
+    hq = G * hkv
+    seed = 5000 + 7 * G + N
+    q = normal(seed, (N, hq, D), bf16=True)
+    k = normal(seed + 1, (P + N, hkv, D), bf16=True)
+    v = normal(seed + 2, (P + N, hkv, D), bf16=True)
+    seqs = pack_seqs([(P, N, mode)])
+    _compare(seqs, window, q, k, v, hq, hkv, True, kv_chunk=chunk, label=f"wide mode={mode} G={G} N={N}")
+
+
+def test_wide_kernel_score_jump():
+    """The reference-overflow recomputation on the 64-rows-per-wave kernel: keys after
+    the first 32 score far above the first ones."""
+    P, N, H, D = 2048, 64, 2, 256
+    rng = np.random.default_rng(91)
+    q = 0.5 + 0.05 * rng.standard_normal((N, H, D))
+    k = 0.25 + 0.05 * rng.standard_normal((P + N, H, D))
+    k[:32] *= -1.0
+    v = rng.standard_normal((P + N, H, D))
+    q, k, v = (round_to_bf16(x.astype(np.float32)) for x in (q, k, v))
+    seqs = pack_seqs([(P, N, BIDIR)])
+    for chunk in (4096, 1024):
+        _compare(seqs, -1, q, k, v, H, H, True, kv_chunk=chunk, scale=1.0, label=f"wide score jump chunk={chunk}")
