@@ -23,7 +23,7 @@ DG_F32, DG_BF16 = 0, 1
 DG_CAUSAL, DG_BIDIR = 0, 1
 DG_CONF_NEG_ENTROPY, DG_CONF_MAX_PROB = 0, 1
 DG_CONV_AND, DG_CONV_OR = 0, 1
-DG_ENTROPY_IN, DG_INIT_CANVAS = 1, 2
+DG_ENTROPY_IN, DG_INIT_CANVAS, DG_SKIP_SELECT, DG_SELECT_ONLY = 1, 2, 4, 8
 DG_MAX_SEQS = DG_MAX_REQS = 64
 DG_MAX_CANVAS = 1024
 DG_PROB_BLOCK = 8192

@@ -197,7 +197,8 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   if (a->num_rows < 1) return bad(DG_ERR_INVALID_ARG, "num_rows must be >= 1");
   if (a->vocab < 1) return bad(DG_ERR_INVALID_ARG, "vocab must be >= 1");
   if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
-  if (a->ld < a->vocab || a->ld % 8) return bad(DG_ERR_INVALID_ARG, "ld must be >= vocab and a multiple of 8");
+  const bool reads_logits = !(a->flags & (DG_INIT_CANVAS | DG_SELECT_ONLY));
+  if (reads_logits && (a->ld < a->vocab || a->ld % 8)) return bad(DG_ERR_INVALID_ARG, "ld must be >= vocab and a multiple of 8");
   if (!std::isfinite(a->budget) || a->budget < 0.f) return bad(DG_ERR_INVALID_ARG, "budget must be finite and >= 0");
   if (!std::isfinite(a->tau) || a->tau < 0.f) return bad(DG_ERR_INVALID_ARG, "tau must be finite and >= 0");
   if (a->min_accept < 0) return bad(DG_ERR_INVALID_ARG, "min_accept must be >= 0");
@@ -205,9 +206,14 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   if (a->combine != DG_CONV_AND && a->combine != DG_CONV_OR) return bad(DG_ERR_INVALID_ARG, "bad combine");
   if (a->renoise != 0 && a->renoise != 1) return bad(DG_ERR_INVALID_ARG, "renoise must be 0 or 1");
   if (a->stable_k < 1 || a->step_limit < 1) return bad(DG_ERR_INVALID_ARG, "stable_k and step_limit must be >= 1");
-  if (a->flags & ~(DG_ENTROPY_IN | DG_INIT_CANVAS)) return bad(DG_ERR_INVALID_ARG, "unknown flag bits");
+  if (a->flags & ~(DG_ENTROPY_IN | DG_INIT_CANVAS | DG_SKIP_SELECT | DG_SELECT_ONLY))
+    return bad(DG_ERR_INVALID_ARG, "unknown flag bits");
   const bool init = a->flags & DG_INIT_CANVAS;
-  if (!init && !a->logits) return bad(DG_ERR_INVALID_ARG, "logits is NULL");
+  const bool select_only = a->flags & DG_SELECT_ONLY;
+  if ((a->flags & DG_SKIP_SELECT) && (select_only || init))
+    return bad(DG_ERR_INVALID_ARG, "DG_SKIP_SELECT excludes DG_SELECT_ONLY and DG_INIT_CANVAS");
+  if (select_only && init) return bad(DG_ERR_INVALID_ARG, "DG_SELECT_ONLY excludes DG_INIT_CANVAS");
+  if (!init && !select_only && !a->logits) return bad(DG_ERR_INVALID_ARG, "logits is NULL");
   if (a->logits && !aligned16(a->logits)) return bad(DG_ERR_INVALID_ARG, "logits must be 16-byte aligned");
   const void* ptrs[] = {a->entropy, a->conf, a->row_max, a->row_sum, a->argmax, a->cand, a->canvas,
                         a->prev_argmax, a->stable_count, a->num_accepted, a->converged, a->mean_entropy};
@@ -233,7 +239,7 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   plan->num_chunks = (int)ceil_div(a->vocab, plan->chunk);
   if (plan->num_chunks > 1024) return bad(DG_ERR_UNSUPPORTED, "vocab too large (more than 1024 row-pass chunks)");
   plan->sub_offset = align_up((size_t)a->num_rows * plan->num_chunks * 16, 256);
-  plan->bytes = init ? 0 : plan->sub_offset + align_up((size_t)a->num_rows * plan->num_chunks * 32 * sizeof(float), 256);
+  plan->bytes = init || select_only ? 0 : plan->sub_offset + align_up((size_t)a->num_rows * plan->num_chunks * 32 * sizeof(float), 256);
   return DG_OK;
 }
 

@@ -654,6 +654,10 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
   }
   SelectParams sp{a->vocab, a->min_accept, a->conf_mode, a->renoise, a->stable_k, a->step_limit, a->combine,
                   a->budget, a->tau, a->flags};
+  if (a->flags & DG_SELECT_ONLY) {
+    hipLaunchKernelGGL(sampler_select, dim3(a->num_reqs), dim3(kThreads), 0, s, t, sp, o);
+    return (int)hipGetLastError();
+  }
   const int nfull = a->vocab / plan.chunk;
   const bool tail = nfull < plan.num_chunks;
   const dim3 gfull((unsigned)nfull * a->num_rows), gtail(a->num_rows), blk(kThreads);
@@ -679,7 +683,7 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
                        plan.num_chunks, a->num_rows, stats, sub, t, sp, o);
   }
 #undef DG_ROWPASS
-  hipLaunchKernelGGL(sampler_select, dim3(a->num_reqs), blk, 0, s, t, sp, o);
+  if (!(a->flags & DG_SKIP_SELECT)) hipLaunchKernelGGL(sampler_select, dim3(a->num_reqs), blk, 0, s, t, sp, o);
   return (int)hipGetLastError();
 }
 

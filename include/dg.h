@@ -150,6 +150,13 @@ size_t dg_attn_workspace_size(const dg_attn_args* args);
  * With DG_INIT_CANVAS the call only starts a block: canvas = Philox token from
  * counter (step, j, 2, 0), prev_argmax = -1, stable_count = 0, converged = 0,
  * num_accepted = 0; logits are not read.
+ * The step splits in two calls with the same arguments, for a caller that overlaps
+ * the selection with work that needs only the row outputs (self-conditioning reads the
+ * probabilities): DG_SKIP_SELECT computes the row statistics, candidates and
+ * probabilities and leaves accept, canvas, prev_argmax and the per-request state
+ * untouched; DG_SELECT_ONLY then runs the selection alone on the entropy, conf, argmax
+ * and cand that call wrote (logits and the workspace are not used). The pair gives
+ * exactly the results of one call without either flag.
  * Precondition: every logits row has at least one finite value (-inf means p = 0).
  * ------------------------------------------------------------------------------ */
 #define DG_CONF_NEG_ENTROPY 0
@@ -158,6 +165,8 @@ size_t dg_attn_workspace_size(const dg_attn_args* args);
 #define DG_CONV_OR 1
 #define DG_ENTROPY_IN 1u
 #define DG_INIT_CANVAS 2u
+#define DG_SKIP_SELECT 4u
+#define DG_SELECT_ONLY 8u
 
 typedef struct {
   int32_t row_start, num_rows; /* rows of this request's canvas; 1..DG_MAX_CANVAS rows */
@@ -182,7 +191,7 @@ typedef struct {
   float tau;                   /* mean-entropy threshold, finite, >= 0 */
   int32_t step_limit;          /* >= 1 */
   int32_t combine;             /* DG_CONV_* */
-  uint32_t flags;              /* DG_ENTROPY_IN | DG_INIT_CANVAS */
+  uint32_t flags;              /* DG_ENTROPY_IN | DG_INIT_CANVAS | DG_SKIP_SELECT | DG_SELECT_ONLY */
   float* entropy;              /* device [M] (input with DG_ENTROPY_IN) */
   float* conf;                 /* device [M] (input with DG_ENTROPY_IN and DG_CONF_MAX_PROB) */
   float* row_max;              /* device [M] */

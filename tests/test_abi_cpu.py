@@ -137,7 +137,8 @@ def _sampler(**over):
     dict(num_reqs=0), dict(reqs=[(0, 1025, 1, 0)]), dict(reqs=[(200, 100, 1, 0)]),
     dict(reqs=[(0, 128, 1, 0), (100, 100, 2, 0)]), dict(reqs=[(0, 256, 1, -1)]), dict(vocab=0), dict(ld=4095),
     dict(ld=4100), dict(budget=float("inf")), dict(budget=-1.0), dict(tau=float("nan")), dict(min_accept=-1),
-    dict(conf_mode=2), dict(combine=3), dict(renoise=2), dict(stable_k=0), dict(step_limit=0), dict(flags=4),
+    dict(conf_mode=2), dict(combine=3), dict(renoise=2), dict(stable_k=0), dict(step_limit=0), dict(flags=16),
+    dict(flags=4 | 8), dict(flags=4 | 2), dict(flags=8 | 2),
     dict(logits=None), dict(entropy=None), dict(accept=None), dict(canvas=FAKE + 2), dict(dtype=3),
     dict(probs=FAKE, ldq=4096), dict(probs_scale=FAKE), dict(probs=FAKE, probs_scale=FAKE, ldq=4000),
     dict(probs=FAKE + 8, probs_scale=FAKE, ldq=4096),
@@ -156,6 +157,11 @@ def test_sampler_workspace():
     assert dg.load().dg_sampler_step(ctypes.byref(a), None) == dg.DG_ERR_WORKSPACE
     init = _sampler(flags=dg.DG_INIT_CANVAS, logits=None)
     assert dg.sampler_workspace_size(init) == 0
+    # the selection alone reads neither logits nor the workspace
+    sel = _sampler(flags=dg.DG_SELECT_ONLY, logits=None)
+    assert dg.sampler_workspace_size(sel) == 0
+    stats = _sampler(flags=dg.DG_SKIP_SELECT)
+    assert dg.sampler_workspace_size(stats) == need
 
 
 def _selfcond(**over):

@@ -212,6 +212,32 @@ def test_repeat_is_bit_identical():
         assert np.array_equal(a, bb)
 
 
+def test_split_call_equals_one_call():
+    """DG_SKIP_SELECT then DG_SELECT_ONLY (same arguments) give exactly the results of one
+    call, over three steps of two requests with their state carried."""
+    c = sampler_case(4)
+    V, M = 40000, 512
+    l = dev(synth_logits(4, M, V, bf16=True), True)
+    reqs0 = [(0, 256, 11, 0), (256, 256, 12, 0)]
+    names = ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
+             "stable_count", "num_accepted", "converged", "mean_entropy", "probs", "probs_scale")
+    bufs = []
+    for _ in range(2):
+        b = dg.SamplerBuffers(M, 2, DEV, vocab=V, probs_dtype=torch.bfloat16)
+        dg.dg_sampler_step(None, reqs0, V, b, c.budget, flags=dg.DG_INIT_CANVAS, num_rows=M)
+        bufs.append(b)
+    for step in range(3):
+        reqs = [(r0, n, seed, step) for r0, n, seed, _ in reqs0]
+        dg.dg_sampler_step(l, reqs, V, bufs[0], c.budget)
+        dg.dg_sampler_step(l, reqs, V, bufs[1], c.budget, flags=dg.DG_SKIP_SELECT)
+        dg.dg_sampler_step(None, reqs, V, bufs[1], c.budget, flags=dg.DG_SELECT_ONLY, num_rows=M)
+        torch.cuda.synchronize()
+        for n in names:
+            a, b = host(getattr(bufs[0], n)), host(getattr(bufs[1], n))
+            assert np.array_equal(a, b, equal_nan=True), (step, n)
+    say("[sampler] split call == one call over 3 steps")
+
+
 @pytest.mark.parametrize("bf16,V", [(True, 262144), (False, 4096), (True, 40000), (False, 12)])
 def test_block_scaled_probabilities(bf16, V):
     """w * scale per DG_PROB_BLOCK reproduces the softmax: within the rounding of w to the
