@@ -289,8 +289,9 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   plan->k_per_split = (int)k_per_split;
   plan->part_offset = 0;
   // partials in whole tiles (MFMA register layout)
+  // partials: bf16 for bf16 products, fp32 for fp32 ones
   size_t bytes = plan->splits > 1 ? align_up((size_t)plan->splits * plan->m_tiles * plan->n_tiles *
-                                             plan->tile_m * plan->tile_n * sizeof(float), 256) : 0;
+                                             plan->tile_m * plan->tile_n * (a->dtype == DG_BF16 ? 2 : 4), 256) : 0;
   plan->p_offset = bytes;
   if (plan->dma && fused) bytes += align_up((size_t)a->M * a->V * 2, 256);
   plan->bytes = bytes;

@@ -72,7 +72,7 @@ struct SelfcondPlan {
   int m_tiles, n_tiles;
   int splits;                  // split-K slices over V
   int k_per_split;             // vocabulary rows per slice (multiple of tile_k)
-  size_t part_offset;          // workspace: fp32 partials [splits][M][d] (splits > 1)
+  size_t part_offset;          // workspace: partials per split and output tile (bf16 for bf16, else fp32; splits > 1)
   size_t p_offset;             // workspace: rebuilt bf16 probabilities [M][V] (logits mode, DMA kernel)
   size_t bytes;
 };

@@ -84,16 +84,14 @@ template <> __device__ __forceinline__ uint4 to_prob<false>(uint4 v, float c) {
   return r;
 }
 
-// Epilogue shared by both kernels: acc[i][j][e] = C[wm + 32i + 8(e/4) + 4h + e%4][wn + 32j + l32].
-// Split-K partials keep the MFMA register layout: per 256 x 256 tile, float4 q =
-// [wave][i][j][e/4][lane] holds acc[i][j][e/4*4 .. +3], so every store is a coalesced
-// 1 KB wave write; selfcond_reduce maps them back to rows and columns.
-// Epilogue of a BM x BN tile held as NI x 4 blocks of 32x32 per wave: the wave's rows
-// start at 32-row block `rb0`, its columns at 128-column group `ch`.
-// Split-K partials are stored in the accumulators' native order (so stores and the
-// reduce's reads are whole 16-byte vectors), with kCh = BN / 128:
-//   float4 index = (((rb * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane, holding rows
-//   32 rb + 8 e4 + 4 (lane / 32) + 0..3 of column 128 ch + 32 j + lane % 32.
+// Epilogue shared by both kernels: acc[i][j][e] = C[wm + 32i + 8(e/4) + 4h + e%4][wn + 32j + l32],
+// for a BM x BN tile held as NI x 4 blocks of 32x32 per wave: the wave's rows start at
+// 32-row block `rb0`, its columns at 128-column group `ch`.
+// Split-K partials are stored in the accumulators' native order (every store a coalesced
+// wave write; selfcond_reduce maps them back to rows and columns), with kCh = BN / 128:
+//   group index = (((rb * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane, holding rows
+//   32 rb + 8 e4 + 4 (lane / 32) + 0..3 of column 128 ch + 32 j + lane % 32;
+// a group is a float4, or 4 bf16 in 8 bytes for bf16 products.
 template <int BM, int BN, int NI>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI][4], int split, int k_lo, int mt,
                                            int nt, int rb0, int ch, int lane, bool bf16) {
@@ -103,8 +101,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI
   const int blk = k_lo / DG_PROB_BLOCK;
   auto scale = [&](int r) { return g.p_scale ? g.p_scale[(int64_t)min(r, g.M - 1) * g.nblocks + blk] : 1.f; };
   if (g.part) {
-    float4* tile = reinterpret_cast<float4*>(g.part) +
-                   (((int64_t)split * g.m_tiles + mt) * g.n_tiles + nt) * (BM * BN / 4);
+    // partials in the output's precision class: bf16 for bf16 products (one rounding of
+    // each slice sum), fp32 for fp32 ones; 4 values (rows r .. r+3 of a column) per lane
+    const int64_t t0 = (((int64_t)split * g.m_tiles + mt) * g.n_tiles + nt) * (BM * BN / 4);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -112,10 +111,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI
         const int r = m0 + 32 * (rb0 + i) + 8 * e4 + 4 * h;  // rows r .. r+3
         const float s0 = scale(r), s1 = scale(r + 1), s2 = scale(r + 2), s3 = scale(r + 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tile[((((rb0 + i) * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane] =
-              make_float4(acc[i][j][4 * e4] * s0, acc[i][j][4 * e4 + 1] * s1, acc[i][j][4 * e4 + 2] * s2,
-                          acc[i][j][4 * e4 + 3] * s3);
+        for (int j = 0; j < 4; ++j) {
+          const int64_t q = t0 + ((((rb0 + i) * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane;
+          const float v0 = acc[i][j][4 * e4] * s0, v1 = acc[i][j][4 * e4 + 1] * s1;
+          const float v2 = acc[i][j][4 * e4 + 2] * s2, v3 = acc[i][j][4 * e4 + 3] * s3;
+          if (bf16) reinterpret_cast<uint2*>(g.part)[q] = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+          else reinterpret_cast<float4*>(g.part)[q] = make_float4(v0, v1, v2, v3);
+        }
       }
     return;
   }
@@ -591,22 +593,32 @@ __global__ __launch_bounds__(256) void selfcond_normalize(const uint16_t* __rest
 }
 
 // Sum split-K partials in slice order (deterministic) and store in the output dtype.
-// Thread = one float4 of the MFMA-layout tile (4 consecutive rows of one column).
+// Thread = one 4-value group of the MFMA-layout tile (4 consecutive rows of one column).
 template <bool kBf16>
-__global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict__ part, int splits, int m_tiles,
+__global__ __launch_bounds__(256) void selfcond_reduce(const void* __restrict__ part_v, int splits, int m_tiles,
                                                        int n_tiles, int tile_m, int tile_n, int M, int d,
                                                        void* __restrict__ out, int64_t ldo) {
   constexpr int kTile4 = 65536 / 4;  // every tile shape holds 64K values
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
   if (i >= per_split) return;
-  // slices added in order; loads in batches of 8, all issued before the adds
-  float4 s = part[i];
+  // slices added in order; loads in batches of 8, all issued before the adds.
+  // Partials are bf16 (4 values in 8 bytes) for bf16 products, else fp32.
+  auto load = [&](int64_t idx) {
+    if constexpr (kBf16) {
+      const uint2 u = reinterpret_cast<const uint2*>(part_v)[idx];
+      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                         __uint_as_float(u.y & 0xffff0000u));
+    } else {
+      return reinterpret_cast<const float4*>(part_v)[idx];
+    }
+  };
+  float4 s = load(i);
   int k = 1;
   for (; k + 8 <= splits; k += 8) {
     float4 v[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[t] = part[(int64_t)(k + t) * per_split + i];
+    for (int t = 0; t < 8; ++t) v[t] = load((int64_t)(k + t) * per_split + i);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       s.x += v[t].x;
@@ -616,7 +628,7 @@ __global__ __launch_bounds__(256) void selfcond_reduce(const float4* __restrict_
     }
   }
   for (; k < splits; ++k) {
-    const float4 v = part[(int64_t)k * per_split + i];
+    const float4 v = load((int64_t)k * per_split + i);
     s.x += v.x;
     s.y += v.y;
     s.z += v.z;
@@ -688,7 +700,7 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
   if (plan.splits > 1) {
     const int64_t n4 = (int64_t)plan.m_tiles * plan.n_tiles * (plan.tile_m * plan.tile_n / 4);
     const dim3 rg((unsigned)((n4 + 255) / 256));
-    const float4* part = reinterpret_cast<const float4*>(g.part);
+    const void* part = g.part;
     if (a->dtype == DG_BF16)
       hipLaunchKernelGGL(selfcond_reduce<true>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles, plan.n_tiles,
                          plan.tile_m, plan.tile_n, a->M, a->d, a->out, a->ldo);
