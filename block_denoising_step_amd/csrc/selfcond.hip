@@ -85,16 +85,17 @@ template <> __device__ __forceinline__ uint4 to_prob<false>(uint4 v, float c) {
 }
 
 // Epilogue shared by both kernels: acc[i][j][e] = C[wm + 32i + 8(e/4) + 4h + e%4][wn + 32j + l32],
-// for a BM x BN tile held as NI x 4 blocks of 32x32 per wave: the wave's rows start at
-// 32-row block `rb0`, its columns at 128-column group `ch`.
+// for a BM x BN tile held as NI x NJ blocks of 32x32 per wave: the wave's rows start at
+// 32-row block `rb0`, its columns at 32-column block `cb0`.
 // Split-K partials are stored in the accumulators' native order (every store a coalesced
 // wave write; selfcond_reduce maps them back to rows and columns), with kCh = BN / 128:
 //   group index = (((rb * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane, holding rows
 //   32 rb + 8 e4 + 4 (lane / 32) + 0..3 of column 128 ch + 32 j + lane % 32;
 // a group is a float4, or 4 bf16 in 8 bytes for bf16 products.
-template <int BM, int BN, int NI>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI][4], int split, int k_lo, int mt,
-                                           int nt, int rb0, int ch, int lane, bool bf16) {
+template <int BM, int BN, int NI, int NJ>
+__device__ __forceinline__ void store_blocks(const GemmArgs& g, f32x16_t (&acc)[NI][NJ], int split, int k_lo, int mt,
+                                             int nt, int rb0, int cb0, int lane, bool bf16) {
+  // acc[i][j] is the 32x32 block at 32-row block rb0 + i, 32-column block cb0 + j
   constexpr int kCh = BN / 128;
   const int h = lane >> 5, l32 = lane & 31;
   const int m0 = mt * BM, n0 = nt * BN;
@@ -111,8 +112,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI
         const int r = m0 + 32 * (rb0 + i) + 8 * e4 + 4 * h;  // rows r .. r+3
         const float s0 = scale(r), s1 = scale(r + 1), s2 = scale(r + 2), s3 = scale(r + 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t q = t0 + ((((rb0 + i) * kCh + ch) * 4 + j) * 4 + e4) * 64 + lane;
+        for (int j = 0; j < NJ; ++j) {
+          const int cb = cb0 + j, ch = cb >> 2, jj = cb & 3;
+          const int64_t q = t0 + ((((rb0 + i) * kCh + ch) * 4 + jj) * 4 + e4) * 64 + lane;
           const float v0 = acc[i][j][4 * e4] * s0, v1 = acc[i][j][4 * e4 + 1] * s1;
           const float v2 = acc[i][j][4 * e4 + 2] * s2, v3 = acc[i][j][4 * e4 + 3] * s3;
           if (bf16) reinterpret_cast<uint2*>(g.part)[q] = make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
@@ -129,8 +131,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16_t (&acc)[NI
       if (r >= g.M) continue;
       const float sr = scale(r);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = n0 + 128 * ch + 32 * j + l32;
+      for (int j = 0; j < NJ; ++j) {
+        const int c = n0 + 32 * (cb0 + j) + l32;
         if (c >= g.d) continue;
         const float v = acc[i][j][e] * sr;
         if (bf16) reinterpret_cast<__bf16*>(g.out)[(int64_t)r * g.ldo + c] = (__bf16)v;
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     }
   }
 
-  store_tile<kBM, kBN, 4>(g, acc, ti.split, k_lo, ti.mt, ti.nt, (wave >> 1) * 4, wave & 1, lane, kBf16);
+  store_blocks<kBM, kBN, 4, 4>(g, acc, ti.split, k_lo, ti.mt, ti.nt, (wave >> 1) * 4, (wave & 1) * 4, lane, kBf16);
 }
 
 
@@ -436,7 +438,14 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int wm = (wave / T::kWN) * 64, wn = (wave % T::kWN) * 128;
+  // Wave placement. BN = 512: SIMD s (waves s and s + 4) owns rows 64 (s / 2) .. +63 and
+  // columns 256 (s % 2) .. +255; the wave that refills the ring (s) takes the first 96
+  // columns and the other the next 160, so the copies the first issues are balanced by
+  // the second's extra MFMAs. BN = 256: every wave a 64 x 128 tile.
+  constexpr bool kSplit = BN == 512;
+  const int s4 = wave % kDmaIssuers;
+  const int wm = kSplit ? (s4 >> 1) * 64 : (wave / T::kWN) * 64;
+  const int wn = kSplit ? (s4 & 1) * 256 + (wave < kDmaIssuers ? 0 : 96) : (wave % T::kWN) * 128;
 
   // Per-lane DMA sources. Issuing wave w fills A segments kSegA*w .. and B segments
   // kSegB*w .. (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the lane
@@ -485,13 +494,6 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   };
   constexpr int kGroup = kSegA + kSegB;  // DMA instructions per stage per issuing wave (0 for the others)
 
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // B operand addresses (tr16): lane group grp = lane/16 covers k rows 8*(grp/2) + 4q
   // + (lane%16)/4 and columns 16*(grp%2) + 4*(lane%4) of each 32-column block.
@@ -499,82 +501,99 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   const int brow = 8 * (grp >> 1) + (s16 >> 2);
   const int bcol = 16 * (grp & 1) + 4 * (s16 & 3);  // + wn + 32j
 
-  // One half step = 16 k: A fragments of 2 row blocks, B fragments of 4 column blocks
-  // (two transposing reads of 4 k rows each). The 10 LDS reads of the next half step
-  // are interleaved with the 8 MFMAs of the current one (sched_barrier pins the order).
+  // One half step = 16 k: A fragments of 2 row blocks, B fragments of NJ column blocks
+  // (two transposing reads of 4 k rows each). The 2 NJ + 2 LDS reads of the next half
+  // step are interleaved with the 2 NJ MFMAs of the current one (sched_barrier pins the
+  // order). The loop is instantiated per NJ, so each wave keeps only its own registers.
   auto a_addr = [&](uint32_t st, int ks, int i) { return st + a_off(wm + 32 * i + l32, 2 * ks + h); };
   auto b_addr = [&](uint32_t st, int ks, int j, int q) {
     const int col = wn + 32 * j + bcol;
     const int kk = 16 * ks + brow + 4 * q;
     return st + kStageA + kk * T::kRowB + (((col >> 3) ^ swb(kk)) << 4) + ((col & 7) << 1);
   };
-  uint4 fa[2][2], fb[2][4];
-  auto read_half = [&](uint32_t st, int ks, int buf) {
+  auto run = [&](auto njc) {
+    constexpr int NJ = decltype(njc)::value;
+    f32x16_t acc[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) fa[buf][i] = lds_read_b128(a_addr(st, ks, i));
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 lo = lds_read_tr16(b_addr(st, ks, j, 0)), hi = lds_read_tr16(b_addr(st, ks, j, 1));
-      fb[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
-  };
-  auto mma_half = [&](int buf, uint32_t next_st, int next_ks) {
-    const int nb = buf ^ 1;
-    uint2 lo[4], hi[4];
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = t >> 2, j = t & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[buf][i]),
-                                                          __builtin_bit_cast(bf16x8_t, fb[buf][j]), acc[i][j], 0, 0, 0);
-      if (next_st != ~0u) {
-        if (t & 1) hi[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 1));
-        else lo[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 0));
-        if (t == 3) fa[nb][0] = lds_read_b128(a_addr(next_st, next_ks, 0));
-        if (t == 7) fa[nb][1] = lds_read_b128(a_addr(next_st, next_ks, 1));
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    uint4 fa[2][2], fb[2][NJ];
+    auto read_half = [&](uint32_t st, int ks, int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[buf][i] = lds_read_b128(a_addr(st, ks, i));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint2 lo = lds_read_tr16(b_addr(st, ks, j, 0)), hi = lds_read_tr16(b_addr(st, ks, j, 1));
+        fb[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (next_st != ~0u) {
+    };
+    auto mma_half = [&](int buf, uint32_t next_st, int next_ks) {
+      const int nb = buf ^ 1;
+      uint2 lo[NJ], hi[NJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[nb][j] = make_uint4(lo[j].x, lo[j].y, hi[j].x, hi[j].y);
-    }
-  };
+      for (int t = 0; t < 2 * NJ; ++t) {
+        const int i = t / NJ, j = t % NJ;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[buf][i]),
+                                                            __builtin_bit_cast(bf16x8_t, fb[buf][j]), acc[i][j], 0, 0, 0);
+        if (next_st != ~0u) {
+          if (t & 1) hi[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 1));
+          else lo[t >> 1] = lds_read_tr16(b_addr(next_st, next_ks, t >> 1, 0));
+          if (t == NJ - 1) fa[nb][0] = lds_read_b128(a_addr(next_st, next_ks, 0));
+          if (t == 2 * NJ - 1) fa[nb][1] = lds_read_b128(a_addr(next_st, next_ks, 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (next_st != ~0u) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[nb][j] = make_uint4(lo[j].x, lo[j].y, hi[j].x, hi[j].y);
+      }
+    };
 
-  // Pipeline: step s's fragments are all in registers once the reads issued during
-  // its first half have landed, so its ring slot is refilled (with step s+kStages)
-  // right after the barrier that follows; the same barrier publishes step s+1.
-  // kStages-1 steps stay in flight while one is consumed.
-  const int pro = min(nsteps, kStages);
-  for (int t = 0; t < pro; ++t) issue(t);
-  if (nsteps > 0) {
-    // step 0 has landed once at most the pro-1 groups issued after it remain
-    if (pro == 5) DG_WAIT_VM(kGroup * 4);
-    else if (pro == 4) DG_WAIT_VM(kGroup * 3);
-    else if (pro == 3) DG_WAIT_VM(kGroup * 2);
-    else if (pro == 2) DG_WAIT_VM(kGroup * 1);
-    else DG_WAIT_VM(0);
-    __builtin_amdgcn_s_barrier();
-    read_half(lbase, 0, 0);
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    const uint32_t st = lbase + (s % kStages) * kStageBytes;
-    DG_WAIT_LGKM0();       // fragments of (s, 0) in buffer 0
-    mma_half(0, st, 1);    // ... with the reads of (s, 1) into buffer 1
-    DG_WAIT_LGKM0();       // fragments of (s, 1) in buffer 1: this wave is done with slot s
-    if (s + 1 < nsteps) {
-      // step s+1 has landed once at most the groups issued after it (steps s+2 ..
-      // min(s+kStages-1, nsteps-1)) remain
-      const int after = min(kStages - 2, nsteps - 2 - s);
-      if (after >= 3) DG_WAIT_VM(kGroup * 3);
-      else if (after == 2) DG_WAIT_VM(kGroup * 2);
-      else if (after == 1) DG_WAIT_VM(kGroup * 1);
+    // Pipeline: step s's fragments are all in registers once the reads issued during
+    // its first half have landed, so its ring slot is refilled (with step s+kStages)
+    // right after the barrier that follows; the same barrier publishes step s+1.
+    // kStages-1 steps stay in flight while one is consumed.
+    const int pro = min(nsteps, kStages);
+    for (int t = 0; t < pro; ++t) issue(t);
+    if (nsteps > 0) {
+      // step 0 has landed once at most the pro-1 groups issued after it remain
+      if (pro == 5) DG_WAIT_VM(kGroup * 4);
+      else if (pro == 4) DG_WAIT_VM(kGroup * 3);
+      else if (pro == 3) DG_WAIT_VM(kGroup * 2);
+      else if (pro == 2) DG_WAIT_VM(kGroup * 1);
       else DG_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();
-      if (s + kStages < nsteps) issue(s + kStages);  // into slot s
+      read_half(lbase, 0, 0);
     }
-    mma_half(1, s + 1 < nsteps ? lbase + ((s + 1) % kStages) * kStageBytes : ~0u, 0);
+    for (int s = 0; s < nsteps; ++s) {
+      const uint32_t st = lbase + (s % kStages) * kStageBytes;
+      DG_WAIT_LGKM0();       // fragments of (s, 0) in buffer 0
+      mma_half(0, st, 1);    // ... with the reads of (s, 1) into buffer 1
+      DG_WAIT_LGKM0();       // fragments of (s, 1) in buffer 1: this wave is done with slot s
+      if (s + 1 < nsteps) {
+        // step s+1 has landed once at most the groups issued after it (steps s+2 ..
+        // min(s+kStages-1, nsteps-1)) remain
+        const int after = min(kStages - 2, nsteps - 2 - s);
+        if (after >= 3) DG_WAIT_VM(kGroup * 3);
+        else if (after == 2) DG_WAIT_VM(kGroup * 2);
+        else if (after == 1) DG_WAIT_VM(kGroup * 1);
+        else DG_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        if (s + kStages < nsteps) issue(s + kStages);  // into slot s
+      }
+      mma_half(1, s + 1 < nsteps ? lbase + ((s + 1) % kStages) * kStageBytes : ~0u, 0);
+    }
+    store_blocks<BM, BN, 2, NJ>(g, acc, ti.split, ti.k_lo, ti.mt, ti.nt, wm >> 5, wn >> 5, lane, true);
+  };
+  if constexpr (kSplit) {
+    if (wave < kDmaIssuers) run(std::integral_constant<int, 3>{});
+    else run(std::integral_constant<int, 5>{});
+  } else {
+    run(std::integral_constant<int, 4>{});
   }
-  store_tile<BM, BN, 2>(g, acc, ti.split, ti.k_lo, ti.mt, ti.nt, (wave / T::kWN) * 2, wave % T::kWN, lane, true);
 }
 
 // bf16 logits + row statistics -> probabilities p = 2^(l*log2e + c); 8 per thread.
