@@ -50,10 +50,8 @@ __device__ __forceinline__ void key_bounds(int mode, int prefix, int num_q, int 
   hi = mode == DG_CAUSAL ? p : (window < 0 ? last : min(last, p + window));
 }
 
-// The request owning a global work (or merge) index: the last one whose first index
-// is <= w. Requests without work share their first index with the next request, so
-// the last of a tie is the one that has work.
-// The request whose work (or merge) range holds index w.
+// The request whose work (or merge) range holds index w (the ranges are disjoint, in
+// any order).
 __device__ __forceinline__ int find_seq(const AttnArgs& a, int w, bool merge) {
   int s = 0;
   for (int i = 0; i < a.num_seqs; ++i) {
@@ -512,11 +510,16 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work groups are dealt round-robin to the 8 XCDs; renumber them so that consecutive
-// indices share an XCD (and its L2): the q tiles of one key chunk read the same K/V.
+// Work groups are dealt round-robin to the 8 XCDs. Renumber them so that each XCD takes
+// runs of kXcdRun consecutive work items (the q tiles of one key chunk read the same K/V,
+// which its L2 then serves once), while all XCDs walk the work list together from its
+// start: long and short requests spread evenly over the XCDs. Blocks of the last partial
+// round keep their launch order.
+constexpr int kXcdRun = 4;
 __device__ __forceinline__ int xcd_order(int b, int n) {
-  const int q = n >> 3, r = n & 7, x = b & 7;
-  return x * q + min(x, r) + (b >> 3);
+  constexpr int kRound = 8 * kXcdRun;
+  if (b >= n / kRound * kRound) return b;
+  return b / kRound * kRound + (b & 7) * kXcdRun + (b >> 3) % kXcdRun;
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {

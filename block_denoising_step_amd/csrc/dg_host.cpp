@@ -142,8 +142,20 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   const int mrpg = attn_merge_rows_per_group(a->dtype == DG_BF16, a->head_dim);
   int64_t num_work = 0, num_merge = 0, part_rows = 0, num_wide = 0;
   plan->num_seqs = a->num_seqs;
-  for (int pass = 0; pass < 2; ++pass)  // wide requests' work first
-    for (int s = 0; s < a->num_seqs; ++s) {
+  // Work list: the wide kernel's requests, then the others (two launches); within each,
+  // requests with the longest work groups first, so that the short ones fill the tail.
+  // The order changes no result: every work group computes the same thing wherever it runs.
+  int order[DG_MAX_SEQS];
+  double per_group[DG_MAX_SEQS];
+  for (int s = 0; s < a->num_seqs; ++s) {
+    order[s] = s;
+    const int64_t groups = a->num_kv_heads * sq[s].ntiles_q * sq[s].nch;
+    per_group[s] = groups > 0 ? (double)sq[s].sub_tiles / (double)groups : 0.0;
+  }
+  std::stable_sort(order, order + a->num_seqs, [&](int x, int y) { return per_group[x] > per_group[y]; });
+  for (int pass = 0; pass < 2; ++pass)
+    for (int oi = 0; oi < a->num_seqs; ++oi) {
+      const int s = order[oi];
       if (wide[s] != (pass == 0)) continue;
       const dg_seq& q = a->seqs[s];
       const Split& r = sq[s];
