@@ -42,7 +42,19 @@ class DgAttnArgs(ctypes.Structure):
                 ("num_q_heads", _c_int32), ("num_kv_heads", _c_int32), ("head_dim", _c_int32),
                 ("scale", ctypes.c_float), ("dtype", _c_int32), ("total_q", _c_int64), ("total_kv", _c_int64),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp), ("lse", _vp), ("kv_chunk", _c_int32),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("block_size", _c_int32), ("block_table", _vp), ("block_table_len", _c_int64)]
+
+
+class DgKvSeq(ctypes.Structure):
+    _fields_ = [("src_start", _c_int32), ("num", _c_int32), ("table_start", _c_int32), ("pos", _c_int32)]
+
+
+class DgKvWriteArgs(ctypes.Structure):
+    _fields_ = [("num_seqs", _c_int32), ("seqs", ctypes.POINTER(DgKvSeq)), ("num_kv_heads", _c_int32),
+                ("head_dim", _c_int32), ("dtype", _c_int32), ("block_size", _c_int32), ("block_table", _vp),
+                ("block_table_len", _c_int64), ("total_new", _c_int64), ("pool_rows", _c_int64),
+                ("k_new", _vp), ("v_new", _vp), ("k_pool", _vp), ("v_pool", _vp)]
 
 
 class DgSreq(ctypes.Structure):
@@ -71,7 +83,7 @@ class DgSelfcondArgs(ctypes.Structure):
 
 
 EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sampler_workspace_size",
-           "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_status_string", "dg_last_error",
+           "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_status_string", "dg_last_error",
            "dg_abi_version"]
 
 _lib = None
@@ -103,6 +115,8 @@ def load() -> ctypes.CDLL:
     lib.dg_selfcond_embed.restype = ctypes.c_int
     lib.dg_selfcond_workspace_size.argtypes = [ctypes.POINTER(DgSelfcondArgs)]
     lib.dg_selfcond_workspace_size.restype = ctypes.c_size_t
+    lib.dg_kv_write.argtypes = [ctypes.POINTER(DgKvWriteArgs), _vp]
+    lib.dg_kv_write.restype = ctypes.c_int
     lib.dg_status_string.argtypes = [ctypes.c_int]
     lib.dg_status_string.restype = ctypes.c_char_p
     lib.dg_last_error.argtypes = []
@@ -157,7 +171,10 @@ def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor
 # ---- dg_attn_mixed ---------------------------------------------------------------
 
 def make_attn_args(q, k, v, out, seqs: Sequence, window: int, num_q_heads: int, num_kv_heads: int,
-                   lse=None, scale: float = 0.0, kv_chunk: int = 0, workspace=None):
+                   lse=None, scale: float = 0.0, kv_chunk: int = 0, workspace=None, block_table=None,
+                   block_size: int = 0):
+    """block_size > 0: k/v are paged pools and block_table an int32 device tensor; each
+    request's kv_start is then the index of its first table entry."""
     seq_arr = (DgSeq * max(1, len(seqs)))()
     for i, s in enumerate(seqs):
         f = (s.q_start, s.num_q, s.kv_start, s.prefix_len, s.mode) if hasattr(s, "q_start") else tuple(s)
@@ -173,6 +190,11 @@ def make_attn_args(q, k, v, out, seqs: Sequence, window: int, num_q_heads: int, 
     a.total_q, a.total_kv = q.shape[0], k.shape[0]
     a.q, a.k, a.v, a.out, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
     a.kv_chunk = kv_chunk
+    a.block_size = block_size
+    if block_size:
+        if block_table is None or block_table.dtype != torch.int32:
+            raise TypeError("paged attention needs an int32 block_table tensor")
+        a.block_table, a.block_table_len = _ptr(block_table), block_table.numel()
     a._keep = seq_arr  # keep the host array alive with the struct
     return a
 
@@ -184,15 +206,51 @@ def attn_workspace_size(args: DgAttnArgs) -> int:
 def dg_attn_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, seqs: Sequence,
                   window: int, num_q_heads: int, num_kv_heads: int, lse: Optional[torch.Tensor] = None,
                   scale: float = 0.0, kv_chunk: int = 0, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> Optional[torch.Tensor]:
+                  stream=None, block_table: Optional[torch.Tensor] = None, block_size: int = 0) -> Optional[torch.Tensor]:
     """Mixed-mode attention (see include/dg.h). q [T, Hq, D], k/v [S, Hkv, D], out like q,
-    lse [T, Hq] fp32 or None. Returns the workspace tensor used (reusable)."""
-    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk)
+    lse [T, Hq] fp32 or None; with block_size > 0, k/v are paged pools read through
+    block_table. Returns the workspace tensor used (reusable)."""
+    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk,
+                       block_table=block_table, block_size=block_size)
     ws = _workspace(attn_workspace_size(a), q, workspace)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().dg_attn_mixed(ctypes.byref(a), _stream(stream)))
     return ws
+
+
+# ---- dg_kv_write -----------------------------------------------------------------
+
+def make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs: Sequence, block_table, block_size: int):
+    """seqs: (src_start, num, table_start, pos) per request."""
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be an int32 tensor")
+    arr = (DgKvSeq * max(1, len(seqs)))()
+    for i, s in enumerate(seqs):
+        arr[i] = DgKvSeq(*tuple(s))
+    a = DgKvWriteArgs()
+    a.num_seqs = len(seqs)
+    a.seqs = ctypes.cast(arr, ctypes.POINTER(DgKvSeq))
+    a.num_kv_heads, a.head_dim = k_new.shape[1], k_new.shape[2]
+    a.dtype = _dtype(k_new)
+    a.block_size = block_size
+    a.block_table, a.block_table_len = _ptr(block_table), block_table.numel()
+    a.total_new, a.pool_rows = k_new.shape[0], k_pool.shape[0]
+    a.k_new, a.v_new, a.k_pool, a.v_pool = _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool)
+    a._keep = arr
+    return a
+
+
+def dg_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                seqs: Sequence, block_table: torch.Tensor, block_size: int, stream=None) -> None:
+    """Scatter new K/V rows [T, Hkv, D] into paged pools [rows, Hkv, D] (see include/dg.h)."""
+    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size)
+    _check(load().dg_kv_write(ctypes.byref(a), _stream(stream)))
+
+
+def prepare_kv_write(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size):
+    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size)
+    return Prepared(load().dg_kv_write, a, ())
 
 
 # ---- dg_sampler_step -------------------------------------------------------------
@@ -322,8 +380,10 @@ class Prepared:
         _check(self._fn(ctypes.byref(self.args), _stream(stream)))
 
 
-def prepare_attn(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse=None, scale=0.0, kv_chunk=0):
-    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk)
+def prepare_attn(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse=None, scale=0.0, kv_chunk=0,
+                 block_table=None, block_size=0):
+    a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk,
+                       block_table=block_table, block_size=block_size)
     ws = _workspace(attn_workspace_size(a), q, None)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel()

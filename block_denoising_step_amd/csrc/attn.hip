@@ -40,8 +40,28 @@ struct AttnArgs {
   int hq, hkv, group, window, num_seqs;
   int work_offset;  // work index of this launch's block 0
   float scale_log2;  // scale * log2(e)
+  const int32_t* block_table;  // paged K/V: a request's table starts at its kv_start
+  int64_t pool_blocks;         // blocks in the K and V pools
+  int block_shift;             // log2(block_size)
   AttnSeqPlan seqs[DG_MAX_SEQS];
 };
+
+// Pool row of key `key` of request sp. Contiguous: kv_start + key. Paged: through the
+// request's block table, read with a scalar load (the table is uniform and read-only).
+// Blocks hold a power of two >= 64 rows and key tiles start at multiples of 32, so the
+// rows of one 32-key sub-tile or 64-key tile are consecutive in the pool. An entry
+// outside the pool is clamped to its last block, so no read leaves the pools.
+template <bool kPaged>
+__device__ __forceinline__ int64_t key_row(const AttnArgs& a, const AttnSeqPlan& sp, int key) {
+  if constexpr (!kPaged) {
+    return (int64_t)sp.kv_start + key;
+  } else {
+    typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+    const uint32_t e = (uint32_t)((const_i32p)a.block_table)[sp.kv_start + (key >> a.block_shift)];
+    const int64_t blk = min((int64_t)e, a.pool_blocks - 1);
+    return (blk << a.block_shift) + (key & ((1 << a.block_shift) - 1));
+  }
+}
 
 __device__ __forceinline__ void key_bounds(int mode, int prefix, int num_q, int window, int i, int& lo, int& hi) {
   const int p = prefix + i;
@@ -116,7 +136,7 @@ struct Lds {
 // or past `nkeys` (request-local) are zero.
 template <bool kBf16, int D>
 __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, const char* vg, int64_t row_stride,
-                                           int k0, int nkeys) {
+                                           int nvalid) {
   using L = Lds<kBf16, D>;
   constexpr int esz = L::esz;
   constexpr int cpr = D * esz / 16;  // 16-byte chunks per key row
@@ -126,7 +146,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   for (int q = tid; q < kKT * cpr; q += kThreads) {
     const int key = q / cpr, col = q % cpr;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (k0 + key < nkeys) val = *reinterpret_cast<const uint4*>(kg + (int64_t)(k0 + key) * row_stride + col * 16);
+    if (key < nvalid) val = *reinterpret_cast<const uint4*>(kg + (int64_t)key * row_stride + col * 16);
     *reinterpret_cast<uint4*>(lk + key * L::k_pitch + col * 16) = val;
   }
   // V^T: within each 16-key group, key w sits at position w with bits 2 and 3 swapped
@@ -141,7 +161,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
       for (int j = 0; j < 8; ++j) {
         const int key = 16 * a16 + 4 * c + (j & 3) + ((j >> 2) << 3);
         r[j] = make_uint4(0, 0, 0, 0);
-        if (k0 + key < nkeys) r[j] = *reinterpret_cast<const uint4*>(vg + (int64_t)(k0 + key) * row_stride + dgp * 16);
+        if (key < nvalid) r[j] = *reinterpret_cast<const uint4*>(vg + (int64_t)key * row_stride + dgp * 16);
       }
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -167,7 +187,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         r[j] = make_float4(0, 0, 0, 0);
-        if (k0 + key0 + j < nkeys) r[j] = *reinterpret_cast<const float4*>(vg + (int64_t)(k0 + key0 + j) * row_stride + dgp * 16);
+        if (key0 + j < nvalid) r[j] = *reinterpret_cast<const float4*>(vg + (int64_t)(key0 + j) * row_stride + dgp * 16);
       }
       *reinterpret_cast<float4*>(lv + (dgp * 4 + 0) * L::v_pitch + pos0 * 4) = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
       *reinterpret_cast<float4*>(lv + (dgp * 4 + 1) * L::v_pitch + pos0 * 4) = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
@@ -177,7 +197,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   }
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   using OP = Op<kBf16>;
   using L = Lds<kBf16, D>;
@@ -234,13 +254,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   float l_run = 0.f;      // this lane's share of the running sum
 
   const int64_t row_stride = (int64_t)a.hkv * D * esz;
-  const char* kg = reinterpret_cast<const char*>(a.k) + ((int64_t)sp.kv_start * a.hkv + g) * D * esz;
-  const char* vg = reinterpret_cast<const char*>(a.v) + ((int64_t)sp.kv_start * a.hkv + g) * D * esz;
+  const char* kg = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * esz;
+  const char* vg = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * esz;
 
   for (int kt = t_begin; kt < t_end; ++kt) {
     const int k0 = kt * kKT;
+    const int64_t r0 = key_row<kPaged>(a, sp, k0) * row_stride;  // the tile's 64 rows are consecutive
     __syncthreads();  // previous tile fully consumed
-    stage_tile<kBf16, D>(lk, lv, kg, vg, row_stride, k0, nkeys);
+    stage_tile<kBf16, D>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
     __syncthreads();
 
     // S^T blocks: sblk[kb][i] = score of key k0 + 32kb + 8(i/4) + 4hh + i%4 for this lane's row
@@ -522,6 +543,7 @@ __device__ __forceinline__ int xcd_order(int b, int n) {
   return b / kRound * kRound + (b & 7) * kXcdRun + (b >> 3) % kXcdRun;
 }
 
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   constexpr int D = 256, KS = 16, DB = 8;
   __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kAttStage];
@@ -571,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   // ---- DMA: wave w fills pairs 4w..4w+3 of the K and V regions; lane i loads
   // chunk i/2 of key row 2*pair + i%2 (per-request byte offsets fit in 32 bits).
   const int rs = a.hkv * D * 2;  // bytes between consecutive keys
-  const int64_t head_off = ((int64_t)sp.kv_start * a.hkv + g) * D * 2;
+  const int64_t head_off = (int64_t)g * D * 2;
   const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
   const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
   uint32_t vo[4];
@@ -582,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   // rows kbase .. kbase+31 into the K or V region at `dst` (uniform base + per-lane
   // 32-bit offset); rows past the request's last key repeat that key (they are masked)
   auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase) {
-    const char* src = base + (int64_t)kbase * rs;
+    const char* src = base + key_row<kPaged>(a, sp, kbase) * rs;
     if (kbase + kSub <= nkeys) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -605,13 +627,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
     dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
   };
   // one of the 8 DMA instructions of stage j (0..3: K pairs, 4..7: V pairs), in the
-  // same order as issue()
-  auto issue_one = [&](int j, int i) {
+  // same order as issue(); krow / vrow are the pool rows of the stage's first K and V key
+  auto issue_one = [&](int j, int i, int64_t krow, int64_t vrow) {
     lds_char* st = lds0 + (j & 3) * kAttStage;
     const bool isk = i < 4;
     const int t = i & 3;
     const int kbase = key0 + kSub * (isk ? min(j + 1, nsub - 1) : j);
-    const char* src = (isk ? kb : vb) + (int64_t)kbase * rs;
+    const char* src = (isk ? kb + krow * rs : vb + vrow * rs);
     lds_char* dst = isk ? st + (4 * wave + t) * kKPitch : st + kKRegion + (4 * wave + t) * kVPitch;
     const uint32_t off = kbase + kSub <= nkeys ? vo[t]
                                                : min(2 * (4 * wave + t) + (lane & 1), nkeys - 1 - kbase) * rs + (lane >> 1) * 16;
@@ -693,6 +715,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
       const bool refill = sub + 3 < nsub;   // uniform
       const bool has_next = sub + 1 < nsub;  // uniform
+      // pool rows of the stage refilled below (the K reads' wait also covers a table load)
+      const int64_t krow = key_row<kPaged>(a, sp, key0 + kSub * min(sub + 4, nsub - 1));
+      const int64_t vrow = key_row<kPaged>(a, sp, key0 + kSub * min(sub + 3, nsub - 1));
 
       uint4 kf[KS];
       uint2 v0[DB][2], v1[DB][2];
@@ -731,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
                                                        __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
         v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
         v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
-        if (refill) issue_one(sub + 3, b);
+        if (refill) issue_one(sub + 3, b, krow, vrow);
         p[8 + b] = fast_exp2(fmaf(scur[8 + b], a.scale_log2, -mu));
         l_run += p[8 + b];
         __builtin_amdgcn_sched_barrier(0);
@@ -749,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
         o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, make_uint4(v1[b][0].x, v1[b][0].y, v1[b][1].x, v1[b][1].y)),
             __builtin_bit_cast(bf16x8_t, pf[1]), o[b], 0, 0, 0);
-        if (b < 4) t4[b] = fmaxf(fmaxf(snxt[4 * b], snxt[4 * b + 1]), fmaxf(snxt[4 * b + 2], snxt[4 * b + 3]));
+        if constexpr (b < 4) t4[b] = fmaxf(fmaxf(snxt[4 * b], snxt[4 * b + 1]), fmaxf(snxt[4 * b + 2], snxt[4 * b + 3]));
         if (b == 4) tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
         if (b == 5) tmax = half_max(tmax) * a.scale_log2;
         if (b == 6 && has_next) {
@@ -854,6 +879,7 @@ __device__ __forceinline__ void mfma_v_last2(f32x16_t& c0, f32x16_t& c1, const u
     __builtin_amdgcn_sched_barrier(0);                                        \
   } while (0)
 
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   constexpr int D = 256, KS = 16, DB = 8, kTile = 256;
   __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kAttStage];
@@ -917,15 +943,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   }
   const uint32_t q_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)qlds + wave * (KS - kQL) * 1024 + lane * 16;
   const int rs = a.hkv * D * 2;
-  const int64_t head_off = ((int64_t)sp.kv_start * a.hkv + g) * D * 2;
+  const int64_t head_off = (int64_t)g * D * 2;
   const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
   const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
   // lane offset of DMA pair t (recomputed at each use: it is cheap, and registers are not)
   auto vo = [&](int t) { return (uint32_t)((2 * (4 * wave + t) + (lane & 1)) * rs + (lane >> 1) * 16); };
   typedef __attribute__((address_space(3))) char lds_char;
   lds_char* lds0 = (lds_char*)lds;
-  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase) {
-    const char* src = base + (int64_t)kbase * rs;
+  // rows kbase .. kbase+31 from pool row `row` on (row < 0: look it up)
+  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase, int64_t row) {
+    const char* src = base + (row < 0 ? key_row<kPaged>(a, sp, kbase) : row) * rs;
     if (kbase + kSub <= nkeys) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -941,21 +968,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       }
     }
   };
-  auto issue = [&](int j) {
+  // stage j: K of sub-tile j+1 and V of sub-tile j, from pool rows krow / vrow (< 0: look up)
+  auto issue = [&](int j, int64_t krow = -1, int64_t vrow = -1) {
     lds_char* st = lds0 + (j & 3) * kAttStage;
-    dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
-    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
+    dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1), krow);
+    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j, vrow);
   };
-  auto issue_one = [&](int j, int i) {
-    lds_char* st = lds0 + (j & 3) * kAttStage;
-    const bool isk = i < 4;
-    const int t = i & 3;
-    const int kbase = key0 + kSub * (isk ? min(j + 1, nsub - 1) : j);
-    const char* src = (isk ? kb : vb) + (int64_t)kbase * rs;
-    lds_char* dst = isk ? st + (4 * wave + t) * kKPitch : st + kKRegion + (4 * wave + t) * kVPitch;
-    const uint32_t off = kbase + kSub <= nkeys ? vo(t)
-                                               : min(2 * (4 * wave + t) + (lane & 1), nkeys - 1 - kbase) * rs + (lane >> 1) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  // pool rows of stage j's K and V keys; in the loop they are looked up one sub-tile
+  // ahead, so that the softmax's LDS waits also cover the table loads
+  auto stage_rows = [&](int j, int64_t& krow, int64_t& vrow) {
+    krow = key_row<kPaged>(a, sp, key0 + kSub * min(j + 1, nsub - 1));
+    vrow = key_row<kPaged>(a, sp, key0 + kSub * min(j, nsub - 1));
   };
 
   const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
@@ -1013,7 +1036,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   float m_ref[2] = {kNegInf, kNegInf};
   for (;;) {
     if (tid == 0) redo_flag[0] = 0;
-    dma_rows(kb, lds0 + 3 * kAttStage, kKPitch, key0);
+    dma_rows(kb, lds0 + 3 * kAttStage, kKPitch, key0, -1);
     issue(0);
     if (nsub > 1) issue(1);
     if (nsub > 2) issue(2);
@@ -1034,6 +1057,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
     }
 
     bool overflow = false;
+    int64_t krow, vrow;
+    stage_rows(3, krow, vrow);
     for (int sub = 0; sub < nsub; ++sub) {
       const int left = nsub - 1 - sub;
       if (left >= 2) DG_ATT_WAIT_VM(16);
@@ -1043,7 +1068,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t ka = lbase + (sub & 3) * kAttStage + k_lane;
       const uint32_t va = lbase + (sub & 3) * kAttStage + v_lane;
-      if (sub + 3 < nsub) issue(sub + 3);  // into the slot of sub-1, free since the barrier
+      if (sub + 3 < nsub) issue(sub + 3, krow, vrow);  // into the slot of sub-1, free since the barrier
+      stage_rows(sub + 4, krow, vrow);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax of S(sub), keys 0..15 (elements 0..7). Once every row has its
@@ -1178,22 +1204,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   }
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kPaged>
 int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   // work [0, num_wide): 64-rows-per-wave kernel; [num_wide, num_work): 128-row kernels
   if constexpr (kBf16 && D == 256) {
     if (plan.num_wide > 0) {
       args.work_offset = 0;
-      hipLaunchKernelGGL(attn_fwd_bf16_d256_w64, dim3(plan.num_wide), dim3(kThreads), 0, s, args);
+      hipLaunchKernelGGL(attn_fwd_bf16_d256_w64<kPaged>, dim3(plan.num_wide), dim3(kThreads), 0, s, args);
     }
   }
   if (plan.num_work > plan.num_wide) {
     args.work_offset = plan.num_wide;
     const dim3 grid(plan.num_work - plan.num_wide);
     if (kBf16 && D == 256 && plan.dma)
-      hipLaunchKernelGGL(attn_fwd_bf16_d256, grid, dim3(kThreads), 0, s, args);
+      hipLaunchKernelGGL(attn_fwd_bf16_d256<kPaged>, grid, dim3(kThreads), 0, s, args);
     else
-      hipLaunchKernelGGL((attn_fwd<kBf16, D>), grid, dim3(kThreads), 0, s, args);
+      hipLaunchKernelGGL((attn_fwd<kBf16, D, kPaged>), grid, dim3(kThreads), 0, s, args);
   }
   if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
   return (int)hipGetLastError();
@@ -1220,18 +1246,22 @@ int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream) {
   args.num_seqs = plan.num_seqs;
   const float scale = a->scale > 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   args.scale_log2 = scale * kLog2e;
+  args.block_table = a->block_size > 0 ? a->block_table : nullptr;
+  args.pool_blocks = a->block_size > 0 ? a->total_kv / a->block_size : 0;
+  args.block_shift = plan.block_shift;
   for (int i = 0; i < plan.num_seqs; ++i) args.seqs[i] = plan.seqs[i];
   for (int i = plan.num_seqs; i < DG_MAX_SEQS; ++i) args.seqs[i] = AttnSeqPlan{};
+  const bool paged = plan.block_shift >= 0;
   if (a->dtype == DG_BF16) {
     switch (a->head_dim) {
-      case 64: return launch_typed<true, 64>(args, plan, s);
-      case 128: return launch_typed<true, 128>(args, plan, s);
-      default: return launch_typed<true, 256>(args, plan, s);
+      case 64: return paged ? launch_typed<true, 64, true>(args, plan, s) : launch_typed<true, 64, false>(args, plan, s);
+      case 128: return paged ? launch_typed<true, 128, true>(args, plan, s) : launch_typed<true, 128, false>(args, plan, s);
+      default: return paged ? launch_typed<true, 256, true>(args, plan, s) : launch_typed<true, 256, false>(args, plan, s);
     }
   }
   switch (a->head_dim) {
-    case 64: return launch_typed<false, 64>(args, plan, s);
-    default: return launch_typed<false, 128>(args, plan, s);
+    case 64: return paged ? launch_typed<false, 64, true>(args, plan, s) : launch_typed<false, 64, false>(args, plan, s);
+    default: return paged ? launch_typed<false, 128, true>(args, plan, s) : launch_typed<false, 128, false>(args, plan, s);
   }
 }
 

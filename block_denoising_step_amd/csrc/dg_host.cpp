@@ -76,6 +76,20 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
     return bad(DG_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (a->lse && !aligned4(a->lse)) return bad(DG_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  // paged K/V: pools of block_size-row blocks, a block table per request
+  const bool paged = a->block_size != 0;
+  plan->block_shift = -1;
+  if (paged) {
+    if (a->block_size < kKeyTile || (a->block_size & (a->block_size - 1)))
+      return bad(DG_ERR_INVALID_ARG, "block_size must be 0 or a power of two >= 64");
+    if (a->total_kv < a->block_size || a->total_kv % a->block_size)
+      return bad(DG_ERR_INVALID_ARG, "total_kv must be a positive multiple of block_size in paged mode");
+    if (!a->block_table || !aligned4(a->block_table)) return bad(DG_ERR_INVALID_ARG, "block_table must be non-NULL and 4-byte aligned");
+    if (a->block_table_len < 1) return bad(DG_ERR_INVALID_ARG, "block_table_len must be >= 1 in paged mode");
+    int sh = 0;
+    while ((1 << sh) < a->block_size) ++sh;
+    plan->block_shift = sh;
+  }
 
   // request geometry
   std::vector<std::pair<int64_t, int64_t>> qranges;
@@ -85,7 +99,10 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     if (q.q_start < 0 || q.num_q < 0 || q.kv_start < 0 || q.prefix_len < 0)
       return bad(DG_ERR_INVALID_ARG, "seq offsets and lengths must be >= 0");
     if ((int64_t)q.q_start + q.num_q > a->total_q) return bad(DG_ERR_INVALID_ARG, "seq query rows exceed total_q");
-    if ((int64_t)q.kv_start + q.prefix_len + q.num_q > a->total_kv) return bad(DG_ERR_INVALID_ARG, "seq key rows exceed total_kv");
+    if (!paged && (int64_t)q.kv_start + q.prefix_len + q.num_q > a->total_kv)
+      return bad(DG_ERR_INVALID_ARG, "seq key rows exceed total_kv");
+    if (paged && (int64_t)q.kv_start + ceil_div((int64_t)q.prefix_len + q.num_q, a->block_size) > a->block_table_len)
+      return bad(DG_ERR_INVALID_ARG, "seq block table entries exceed block_table_len");
     if ((int64_t)q.prefix_len + q.num_q > INT32_MAX - kKeyTile) return bad(DG_ERR_INVALID_ARG, "seq too long");
     if (q.num_q > 0) qranges.push_back({q.q_start, (int64_t)q.q_start + q.num_q});
   }
@@ -96,8 +113,9 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   // tiles and chunks; the split of a request, and the kernel that runs it, depend on
   // that request alone, so its result is the same whatever else is in the batch.
   // The LDS-DMA kernels (bf16, head_dim 256) take 32-bit byte offsets within a request's K/V.
+  // Paged requests are addressed per sub-tile, so only the contiguous layout has the limit.
   plan->dma = a->dtype == DG_BF16 && a->head_dim == 256;
-  for (int s = 0; s < a->num_seqs; ++s) {
+  for (int s = 0; s < a->num_seqs && !paged; ++s) {
     const dg_seq& q = a->seqs[s];
     if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
   }
@@ -310,6 +328,44 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   return DG_OK;
 }
 
+// ---- paged K/V writes ----------------------------------------------------------
+
+dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char** msg) {
+  auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
+  if (!a) return bad(DG_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_seqs < 1 || a->num_seqs > DG_MAX_SEQS) return bad(DG_ERR_INVALID_ARG, "num_seqs must be in [1, DG_MAX_SEQS]");
+  if (!a->seqs) return bad(DG_ERR_INVALID_ARG, "seqs is NULL");
+  if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (a->num_kv_heads < 1) return bad(DG_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (a->head_dim < 8 || a->head_dim % 8) return bad(DG_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8");
+  if (a->block_size < 1 || (a->block_size & (a->block_size - 1)))
+    return bad(DG_ERR_INVALID_ARG, "block_size must be a power of two");
+  if (a->pool_rows < a->block_size || a->pool_rows % a->block_size)
+    return bad(DG_ERR_INVALID_ARG, "pool_rows must be a positive multiple of block_size");
+  if (a->total_new < 0 || a->block_table_len < 1) return bad(DG_ERR_INVALID_ARG, "total_new must be >= 0 and block_table_len >= 1");
+  if (!a->block_table || !aligned4(a->block_table)) return bad(DG_ERR_INVALID_ARG, "block_table must be non-NULL and 4-byte aligned");
+  if (!a->k_new || !a->v_new || !a->k_pool || !a->v_pool) return bad(DG_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be non-NULL");
+  if (!aligned16(a->k_new) || !aligned16(a->v_new) || !aligned16(a->k_pool) || !aligned16(a->v_pool))
+    return bad(DG_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
+  int64_t rows = 0;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const dg_kv_seq& q = a->seqs[s];
+    if (q.src_start < 0 || q.num < 0 || q.table_start < 0 || q.pos < 0)
+      return bad(DG_ERR_INVALID_ARG, "seq offsets and counts must be >= 0");
+    if ((int64_t)q.src_start + q.num > a->total_new) return bad(DG_ERR_INVALID_ARG, "seq source rows exceed total_new");
+    if ((int64_t)q.table_start + ceil_div((int64_t)q.pos + q.num, a->block_size) > a->block_table_len)
+      return bad(DG_ERR_INVALID_ARG, "seq block table entries exceed block_table_len");
+    rows += q.num;
+  }
+  plan->row_bytes = (int64_t)a->num_kv_heads * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);
+  plan->total_rows = rows;
+  int sh = 0;
+  while ((1 << sh) < a->block_size) ++sh;
+  plan->block_shift = sh;
+  if (rows * (plan->row_bytes / 16) > INT32_MAX) return bad(DG_ERR_UNSUPPORTED, "too many rows for one call");
+  return DG_OK;
+}
+
 }  // namespace dg
 
 // ---- C ABI -------------------------------------------------------------------
@@ -388,6 +444,18 @@ dg_status dg_selfcond_embed(const dg_selfcond_args* a, void* stream) {
   if (plan.bytes && (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace)))
     return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_selfcond_workspace_size");
   int e = launch_selfcond(a, plan, stream);
+  if (e) return fail(DG_ERR_HIP, hip_error_name(e));
+  g_last_error[0] = 0;
+  return DG_OK;
+}
+
+dg_status dg_kv_write(const dg_kv_write_args* a, void* stream) {
+  KvWritePlan plan;
+  const char* msg = "";
+  dg_status s = kv_write_plan(a, &plan, &msg);
+  if (s != DG_OK) return fail(s, msg);
+  if (plan.total_rows == 0) { g_last_error[0] = 0; return DG_OK; }
+  int e = launch_kv_write(a, plan, stream);
   if (e) return fail(DG_ERR_HIP, hip_error_name(e));
   g_last_error[0] = 0;
   return DG_OK;

@@ -44,7 +44,8 @@ struct AttnPlan {
   int num_work;         // all attention work groups; [num_wide, num_work) run the 128-row kernels
   int num_merge;        // work groups of the merge kernel
   int64_t part_rows;    // partial rows (each D wide)
-  int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB: LDS-DMA kernel
+  int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB (or paged): LDS-DMA kernel
+  int block_shift;      // paged K/V: log2(block_size); -1 for the contiguous layout
   size_t part_o_offset;   // workspace: [part_rows][D] partial outputs, input dtype
   size_t part_ml_offset;  // workspace: [part_rows][2] fp32 (max, sum) in log2 units
   size_t bytes;
@@ -78,11 +79,21 @@ struct SelfcondPlan {
 };
 dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const char** msg);
 
+// ---- paged K/V writes ----------------------------------------------------------
+
+struct KvWritePlan {
+  int64_t row_bytes;   // bytes of one key row (Hkv * D * element size)
+  int64_t total_rows;  // rows written over all requests
+  int block_shift;     // log2(block_size)
+};
+dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char** msg);
+
 // ---- launchers (HIP side); return 0 on success or a hipError_t value ---------
 
 int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream);
 int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stream);
 int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream);
+int launch_kv_write(const dg_kv_write_args* a, const KvWritePlan& plan, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace dg

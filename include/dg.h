@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 1
+#define DG_ABI_VERSION 2
 #define DG_MAX_SEQS 64      /* requests per dg_attn_mixed call */
 #define DG_MAX_REQS 64      /* requests per dg_sampler_step call */
 #define DG_MAX_CANVAS 1024  /* positions per sampler request */
@@ -83,6 +83,19 @@ typedef enum { DG_CAUSAL = 0, DG_BIDIR = 1 } dg_mode;
  * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped heads).
  *   out[t, h, :] = sum_j softmax_j(scale * <q[t,h], k[j,g]>) * v[j, g, :]
  *   lse[t, h]    = log sum_j exp(scale * <q[t,h], k[j,g]>)      (natural log)
+ *
+ * Paged K/V (block_size > 0). A committed block is appended to the request's cache
+ * and the canvas is redrafted every step ([P1] sections "샘플링 루프와 엔트로피 경계
+ * 디노이징" and "ModelState 인터페이스"; [P3] section "Integracija u vLLM
+ * infrastrukturu", which keeps vLLM's paged cache). In this mode k and v are pools of
+ * total_kv / block_size blocks of block_size rows, and key j of request r (cache and
+ * new tokens alike) sits at pool row
+ *     block_table[kv_start + j / block_size] * block_size + j % block_size,
+ * so kv_start is the index of the request's first table entry. The result is the one
+ * the contiguous layout gives for the same key rows, bit for bit. Table entries are
+ * device data and are not checked on the host: an entry outside [0, total_kv /
+ * block_size) gives unspecified results for that request (the kernels clamp it, so
+ * they never read outside the pools). dg_kv_write fills the pools.
  * ------------------------------------------------------------------------------ */
 typedef struct {
   int32_t q_start, num_q, kv_start, prefix_len, mode; /* mode: dg_mode */
@@ -107,6 +120,9 @@ typedef struct {
   int32_t kv_chunk;             /* keys per split-KV chunk: 0 = library's choice, else a multiple of 64 */
   void* workspace;              /* device, >= dg_attn_workspace_size(args) bytes (may be NULL if that is 0) */
   size_t workspace_bytes;
+  int32_t block_size;           /* 0: contiguous K/V; else a power of two >= 64, dividing total_kv (paged) */
+  const int32_t* block_table;   /* device [block_table_len] int32 when block_size > 0, else ignored */
+  int64_t block_table_len;      /* every request needs kv_start + ceil((prefix_len + num_q) / block_size) <= this */
 } dg_attn_args;
 
 dg_status dg_attn_mixed(const dg_attn_args* args, void* stream);
@@ -246,6 +262,45 @@ typedef struct {
 
 dg_status dg_selfcond_embed(const dg_selfcond_args* args, void* stream);
 size_t dg_selfcond_workspace_size(const dg_selfcond_args* args);
+
+/* ------------------------------------------------------------------------------
+ * dg_kv_write: write new K/V rows into paged pools (the layout dg_attn_mixed reads
+ * with block_size > 0). This is the cache side of a request's life ([P1] sections
+ * "샘플링 루프와 엔트로피 경계 디노이징" and "ModelState 인터페이스"): a prefill or a
+ * committed block appends its rows after the request's cache, and a canvas draft
+ * rewrites the same positions at every denoise step.
+ * For request r, row src_start + i of k_new/v_new (i < num) goes to the request's key
+ * position pos + i, i.e. pool row
+ *     block_table[table_start + (pos + i) / block_size] * block_size + (pos + i) % block_size.
+ * Rows of the pools that no request writes are left untouched. Target rows of
+ * different requests must not overlap (they would race). Table entries are not
+ * checked on the host; the kernel skips a row whose entry lies outside the pool.
+ * ------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t src_start;            /* first row of k_new / v_new */
+  int32_t num;                  /* rows to write, >= 0 */
+  int32_t table_start;          /* index of the request's first block_table entry */
+  int32_t pos;                  /* key position of the first row within the request, >= 0 */
+} dg_kv_seq;
+
+typedef struct {
+  int32_t num_seqs;             /* 1..DG_MAX_SEQS */
+  const dg_kv_seq* seqs;        /* host array [num_seqs] */
+  int32_t num_kv_heads;         /* Hkv >= 1 */
+  int32_t head_dim;             /* D >= 8, a multiple of 8 */
+  int32_t dtype;                /* dg_dtype of all four tensors */
+  int32_t block_size;           /* a power of two >= 1 */
+  const int32_t* block_table;   /* device [block_table_len] int32 */
+  int64_t block_table_len;      /* every request needs table_start + ceil((pos + num) / block_size) <= this */
+  int64_t total_new;            /* rows of k_new / v_new */
+  int64_t pool_rows;            /* rows of k_pool / v_pool, a multiple of block_size */
+  const void* k_new;            /* device [total_new, Hkv, D] */
+  const void* v_new;            /* device [total_new, Hkv, D] */
+  void* k_pool;                 /* device [pool_rows, Hkv, D] */
+  void* v_pool;                 /* device [pool_rows, Hkv, D] */
+} dg_kv_write_args;
+
+dg_status dg_kv_write(const dg_kv_write_args* args, void* stream);
 
 /* ------------------------------------------------------------------------------ */
 const char* dg_status_string(dg_status s); /* static string for a status */

@@ -17,6 +17,7 @@ Every function is pinned by a CPU test against something other than itself
 the pins are listed in tests/test_oracle_*.py.
 """
 from .attn import attn_mixed, key_range, CAUSAL, BIDIR  # noqa: F401
+from .kvcache import attn_mixed_paged, kv_write, gather_rows, pool_row  # noqa: F401
 from .philox import philox4x64_10, uniform24, renoise_token  # noqa: F401
 from .sampler import (row_stats, candidate, select, convergence, sampler_step,  # noqa: F401
                       CONF_NEG_ENTROPY, CONF_MAX_PROB, CONV_AND, CONV_OR, FIXED_SHIFT)

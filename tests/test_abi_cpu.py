@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dg.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dg_abi_version() == 1
+    assert lib.dg_abi_version() == 2
     for s in range(5):
         assert lib.dg_status_string(s).decode().startswith("DG_")
 
@@ -40,10 +40,16 @@ class _T:
         self.shape = shape
         self._ptr = ptr
         import torch
-        self.dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}[dtype]
 
     def data_ptr(self):
         return self._ptr
+
+    def numel(self):
+        n = 1
+        for x in self.shape:
+            n *= x
+        return n
 
     def stride(self, i):
         s = 1
@@ -118,6 +124,65 @@ def test_attn_workspace_single_chunk_is_zero():
     # left to the planner, a request this small is split into one-tile chunks
     a.kv_chunk = 0
     assert dg.attn_workspace_size(a) > 0
+
+
+@pytest.mark.parametrize("change", [
+    dict(block_size=32), dict(block_size=96), dict(block_size=-64),  # not a power of two >= 64
+    dict(block_size=64, block_table=None),
+    dict(block_size=64, block_table=FAKE + 2),
+    dict(block_size=64, block_table_len=0),
+    dict(block_size=64, block_table_len=1),  # the request needs ceil(96 / 64) = 2 entries
+    dict(block_size=64, total_kv=100),  # not a multiple of block_size
+])
+def test_attn_paged_validation(change):
+    a = _attn()
+    a.block_table, a.block_table_len = FAKE, 2
+    for key, val in change.items():
+        setattr(a, key, val)
+    assert _status(a) == dg.DG_ERR_INVALID_ARG
+    assert dg.last_error()
+
+
+def test_attn_paged_sizes_a_workspace_and_ignores_the_contiguous_span():
+    """In paged mode kv_start indexes the table: rows past total_kv are no error."""
+    a = _attn(seqs=[(0, 32, 5, 64, BIDIR)])
+    a.block_size, a.block_table, a.block_table_len, a.total_kv = 64, FAKE, 7, 64
+    assert dg.attn_workspace_size(a) != ctypes.c_size_t(-1).value
+    a.block_table_len = 6
+    assert dg.attn_workspace_size(a) == ctypes.c_size_t(-1).value
+
+
+def _kv(**over):
+    seqs = over.pop("seqs", [(0, 32, 0, 10)])
+    a = dg.make_kv_write_args(_T((32, 2, 64)), _T((32, 2, 64)), _T((256, 2, 64)), _T((256, 2, 64)), seqs,
+                              _T((4,), dtype="i32"), 64)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(num_seqs=0), dg.DG_ERR_INVALID_ARG), (dict(num_seqs=65), dg.DG_ERR_INVALID_ARG),
+    (dict(block_size=48), dg.DG_ERR_INVALID_ARG), (dict(block_size=0), dg.DG_ERR_INVALID_ARG),
+    (dict(pool_rows=200), dg.DG_ERR_INVALID_ARG), (dict(head_dim=12), dg.DG_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), dg.DG_ERR_INVALID_ARG), (dict(dtype=5), dg.DG_ERR_INVALID_ARG),
+    (dict(block_table=None), dg.DG_ERR_INVALID_ARG), (dict(k_pool=FAKE + 8), dg.DG_ERR_INVALID_ARG),
+    (dict(seqs=[(10, 32, 0, 0)]), dg.DG_ERR_INVALID_ARG),  # source rows past total_new
+    (dict(seqs=[(0, 32, 2, 100)]), dg.DG_ERR_INVALID_ARG),  # needs entries 2..4 of a 4-entry table
+    (dict(seqs=[(0, -1, 0, 0)]), dg.DG_ERR_INVALID_ARG),
+])
+def test_kv_write_validation(change, status):
+    seqs = change.pop("seqs", None)
+    a = _kv(**({"seqs": seqs} if seqs else {}))
+    for key, val in change.items():
+        setattr(a, key, val)
+    assert dg.load().dg_kv_write(ctypes.byref(a), None) == status
+    assert dg.last_error()
+
+
+def test_kv_write_nothing_to_write_is_ok():
+    a = _kv(seqs=[(0, 0, 0, 0)])
+    assert dg.load().dg_kv_write(ctypes.byref(a), None) == dg.DG_OK
 
 
 def _sampler(**over):

@@ -16,7 +16,9 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "..", "block_denoising_step_amd", "csrc", "attn.hip")
-KERNEL = "_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ENS0_8AttnArgsE"
+# both instantiations: contiguous (false) and paged (true) K/V
+KERNELS = ["_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ILb0EEEvNS0_8AttnArgsE",
+           "_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ILb1EEEvNS0_8AttnArgsE"]
 
 
 def _regs(op):
@@ -28,7 +30,7 @@ def _regs(op):
     return out
 
 
-def _asm(tmp_path):
+def _asm(tmp_path, kernel):
     hipcc = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
     if hipcc is None:
         pytest.skip("hipcc not found")
@@ -38,7 +40,7 @@ def _asm(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True)
     lines, on = [], False
     for l in out.read_text().splitlines():
-        if l.startswith(KERNEL + ":"):
+        if l.startswith(kernel + ":"):
             on = True
         if on:
             lines.append(l.strip())
@@ -61,8 +63,9 @@ def _instrs(lines):
     return res
 
 
-def test_asm_mfma_operands_not_written_just_before(tmp_path):
-    ins = _instrs(_asm(tmp_path))
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_asm_mfma_operands_not_written_just_before(tmp_path, kernel):
+    ins = _instrs(_asm(tmp_path, kernel))
     n = 0
     for i, (t, in_asm) in enumerate(ins):
         if not (in_asm and t.startswith("v_mfma")):
@@ -76,8 +79,9 @@ def test_asm_mfma_operands_not_written_just_before(tmp_path):
     assert n >= 32, n  # S^T chains of the loop and the prologue
 
 
-def test_asm_mfma_results_not_read_before_wait_states(tmp_path):
-    ins = _instrs(_asm(tmp_path))
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_asm_mfma_results_not_read_before_wait_states(tmp_path, kernel):
+    ins = _instrs(_asm(tmp_path, kernel))
     pending = set()  # registers written by asm MFMAs not yet covered by wait states
     for t, in_asm in ins:
         if t.startswith("s_nop 15"):
