@@ -209,7 +209,30 @@ def per_config(path, reps=20, warm=5):
 
     out = {"device": torch.cuda.get_device_name(0), "reps": reps, "warmup": warm, "configs": {}}
 
-    def attn_calls(case, variants):
+    def paged_pool(seqs, k, v, B, seed):
+        """Each request's rows in whole B-row blocks, the blocks scattered over the pools
+        by a seeded permutation: pools, int32 table, paged requests (kv_start = first entry)."""
+        from workloads import Seq
+        nbs = [-(-(s.prefix_len + s.num_q) // B) for s in seqs]
+        total = sum(nbs)
+        perm = torch.randperm(total, generator=torch.Generator().manual_seed(seed))
+        kp = torch.zeros((total, B) + tuple(k.shape[1:]), device=dev, dtype=k.dtype)
+        vp = torch.zeros_like(kp)
+        pseqs, b0 = [], 0
+        for s, nb in zip(seqs, nbs):
+            n = s.prefix_len + s.num_q
+            dst = perm[b0:b0 + nb].to(dev)
+            pad = nb * B - n
+            for src, pool in ((k, kp), (v, vp)):
+                rows = src[s.kv_start:s.kv_start + n]
+                if pad:
+                    rows = torch.cat([rows, torch.zeros((pad,) + tuple(k.shape[1:]), device=dev, dtype=k.dtype)])
+                pool[dst] = rows.view((nb, B) + tuple(k.shape[1:]))
+            pseqs.append(Seq(s.q_start, s.num_q, b0, s.prefix_len, s.mode))
+            b0 += nb
+        return kp.view((-1,) + tuple(k.shape[1:])), vp.view((-1,) + tuple(k.shape[1:])), perm.to(dev, torch.int32), pseqs
+
+    def attn_calls(case, variants, paged_block=0):
         dt = torch.bfloat16 if case.bf16 else torch.float32
         esz = 2 if case.bf16 else 4
         q = gen(seed_for(case.cfg, 1), (case.total_q, case.num_q_heads, case.head_dim), dtype=dt)
@@ -222,8 +245,37 @@ def per_config(path, reps=20, warm=5):
             flop, nbytes = attn_work(seqs, window, case.num_q_heads, case.num_kv_heads, case.head_dim, esz)
             res[name] = entry(med_us(c), flop, nbytes, not case.bf16)
             print(f"[per-config] cfg{case.cfg} {name}: {res[name]}", file=sys.stderr, flush=True)
+            if paged_block:
+                # the same call on a paged cache (blocks of paged_block rows in a shuffled pool)
+                kp, vp, table, pseqs = paged_pool(seqs, k, v, paged_block, seed_for(case.cfg, 9))
+                c = dg.prepare_attn(q, kp, vp, o, pseqs, window, case.num_q_heads, case.num_kv_heads,
+                                    block_table=table, block_size=paged_block)
+                pname = f"{name}_paged_block{paged_block}"
+                res[pname] = entry(med_us(c), flop, nbytes, not case.bf16)
+                print(f"[per-config] cfg{case.cfg} {pname}: {res[pname]}", file=sys.stderr, flush=True)
+                del kp, vp, table
         del q, k, v, o
         return res
+
+    def kv_write_call(name, counts, B=256, hkv=8, d=256):
+        """dg_kv_write of `counts` new rows per request (each request's rows after a
+        4096-row cache in its own table), bf16: reads and writes each K/V byte once."""
+        n = sum(counts)
+        k_new = gen(seed_for(4, 2), (n, hkv, d))
+        v_new = gen(seed_for(4, 3), (n, hkv, d))
+        per = [-(-(4096 + c) // B) for c in counts]
+        table = torch.randperm(sum(per), generator=torch.Generator().manual_seed(seed_for(4, 9))).to(dev, torch.int32)
+        kp = torch.zeros(sum(per) * B, hkv, d, device=dev, dtype=torch.bfloat16)
+        vp = torch.zeros_like(kp)
+        seqs, src, t0 = [], 0, 0
+        for c, nb in zip(counts, per):
+            seqs.append((src, c, t0, 4096))
+            src += c
+            t0 += nb
+        call = dg.prepare_kv_write(k_new, v_new, kp, vp, seqs, table, B)
+        e = entry(med_us(call), 0, 2 * 2 * n * hkv * d * 2, False)
+        print(f"[per-config] {name}: {e}", file=sys.stderr, flush=True)
+        return e
 
     def sampler_and_selfcond(cfg, with_selfcond):
         sc = sampler_case(cfg)
@@ -259,19 +311,21 @@ def per_config(path, reps=20, warm=5):
     r.update(sampler_and_selfcond(1, True))
     out["configs"]["1"] = r
     c2 = attn_case(2)
-    r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)])
+    r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)], paged_block=256)
+    r["kv_write_canvas256"] = kv_write_call("cfg2 kv_write_canvas256", [256])
     r.update(sampler_and_selfcond(2, True))
     out["configs"]["2"] = r
     c3 = attn_case(3)
     out["configs"]["3"] = attn_calls(c3, [("attn_bidir_w512", c3.seqs, 512),
                                           ("attn_causal_w512", c3.with_mode(CAUSAL).seqs, 512)])
     c4 = attn_case(4)
-    r = attn_calls(c4, [("attn_global_layer", c4.seqs, -1), ("attn_w512_layer", c4.seqs, 512)])
+    r = attn_calls(c4, [("attn_global_layer", c4.seqs, -1), ("attn_w512_layer", c4.seqs, 512)], paged_block=256)
+    r["kv_write_prefill2048_and_commit256"] = kv_write_call("cfg4 kv_write_prefill2048_and_commit256", [2048, 256])
     r.update(sampler_and_selfcond(4, False))
     out["configs"]["4"] = r
     torch.cuda.empty_cache()
     c5 = attn_case(5)
-    r = attn_calls(c5, [("attn_bidir_global", c5.seqs, -1)])
+    r = attn_calls(c5, [("attn_bidir_global", c5.seqs, -1)], paged_block=256)
     torch.cuda.empty_cache()
     r.update(sampler_and_selfcond(5, True))
     out["configs"]["5"] = r
