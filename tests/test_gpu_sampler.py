@@ -72,9 +72,13 @@ def _run(logits_np, bf16, reqs, V, budget, min_accept=1, conf_mode=CONF_NEG_ENTR
     assert err <= 1e-5
     assert np.array_equal(host(b.argmax), st["argmax"].astype(np.int32))
     assert np.array_equal(host(b.row_max).astype(np.float64), st["max"])
-    np.testing.assert_allclose(host(b.row_sum), st["sum"], rtol=2e-6)
+    # Row sums are fp32: a lane adds its 64 terms in sequence (63 roundings), a
+    # 256-thread tree adds 8 levels, and up to 16 chunk sums are merged in order with
+    # one scaling each; about 90 roundings of 2^-24 (5.4e-6) in the worst case, plus
+    # under 3e-7 from the fp32 exponent arguments of the dominant terms.
+    np.testing.assert_allclose(host(b.row_sum), st["sum"], rtol=1e-5)
     if conf_mode == CONF_MAX_PROB:
-        np.testing.assert_allclose(host(b.conf), st["max_prob"], rtol=2e-6)
+        np.testing.assert_allclose(host(b.conf), st["max_prob"], rtol=1e-5)
     else:
         assert np.array_equal(host(b.conf), -ent)
     cand = host(b.cand)
@@ -130,6 +134,15 @@ def test_bf16_two_denoise_requests_512x262144():
     l = synth_logits(4, c.total_rows, c.vocab, bf16=True)
     s = request_seeds(4, 2)
     _run(l, True, [(0, 256, s[0], 3), (256, 256, s[1], 5)], c.vocab, c.budget, label="bf16 two requests 512x262144")
+
+
+def test_bf16_four_long_context_requests_1024x262144():
+    """The long-context batch: four 256-position canvases in one call, at different steps."""
+    c = sampler_case(5)
+    l = synth_logits(5, c.total_rows, c.vocab, bf16=True)
+    s = request_seeds(5, 4)
+    _run(l, True, [(0, 256, s[0], 0), (256, 256, s[1], 7), (512, 256, s[2], 2), (768, 256, s[3], 30)], c.vocab,
+         c.budget, label="bf16 four requests 1024x262144")
 
 
 @pytest.mark.parametrize("bf16", [False, True])

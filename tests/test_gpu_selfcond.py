@@ -123,8 +123,8 @@ def test_repeat_is_bit_identical():
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("bf16,M,V,d", [(True, 256, 262144, 2048), (False, 256, 4096, 256), (True, 300, 40000, 384),
-                                        (True, 64, 8200, 128)])
+@pytest.mark.parametrize("bf16,M,V,d", [(True, 256, 262144, 2048), (True, 1024, 262144, 2048), (False, 256, 4096, 256),
+                                        (True, 300, 40000, 384), (True, 64, 8200, 128)])
 def test_block_scaled_from_sampler(bf16, M, V, d):
     """The sampler's block-scaled probabilities feed self-conditioning directly; the
     result matches the oracle's softmax-weighted average."""
