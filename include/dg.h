@@ -219,7 +219,9 @@ typedef struct {
   int32_t* prev_argmax;        /* device [M], in/out */
   int32_t* stable_count;       /* device [num_reqs], in/out */
   int32_t* num_accepted;       /* device [num_reqs] */
-  int32_t* converged;          /* device [num_reqs] (0/1) */
+  int32_t* converged;          /* device-accessible [num_reqs] (0/1), write-only: device memory, or pinned
+                                  host memory (hipHostMalloc, coherent) that the host reads once the
+                                  call's work has completed, with no copy on the stream */
   float* mean_entropy;         /* device [num_reqs] */
   void* probs;                 /* device [M, ldq] (logits dtype) or NULL: block-scaled probabilities w */
   int64_t ldq;                 /* row stride of probs in elements, >= V, multiple of 8 */

@@ -198,6 +198,32 @@ def test_stability_counting_and_convergence():
              stable_k=3, tau=5.0, combine=comb, label=f"stability comb={comb}")
 
 
+def test_converged_flag_into_pinned_host_memory():
+    """The selection writes the converged flag straight into pinned host memory (read
+    by the host after the step completes, with no copy on the stream); over several
+    steps in a row, alternating between two host slots, every flag equals the one the
+    same step writes to a device buffer."""
+    rng = np.random.default_rng(11)
+    V = 512
+    l = dev((rng.standard_normal((64, V)) * 6).astype(np.float32))
+    reqs = [(0, 40, 5, 0), (40, 24, 6, 0)]
+    host_slots = torch.zeros(2, 2, dtype=torch.int32, pin_memory=True)
+    bd, bh = dg.SamplerBuffers(64, 2, DEV), dg.SamplerBuffers(64, 2, DEV)
+    for t in range(6):
+        r = [(r0, n, sd, t) for (r0, n, sd, _) in reqs]
+        dg.dg_sampler_step(l, r, V, bd, 2.0, stable_k=2, tau=0.0, combine=CONV_OR)
+        ph = dg.prepare_sampler(l, r, V, bh, 2.0, stable_k=2, tau=0.0, combine=CONV_OR)
+        ph.args.converged = host_slots[t % 2].data_ptr()
+        ph()
+        ev = torch.cuda.Event()
+        ev.record()
+        ev.synchronize()
+        want = host(bd.converged)
+        say(f"[sampler] pinned flag step {t}: {host_slots[t % 2].tolist()} (device {want.tolist()})")
+        assert np.array_equal(host_slots[t % 2].numpy(), want)
+    assert host_slots[1].tolist() == [1, 1]  # the logits never change: stable for 2 steps by step 2
+
+
 def test_init_canvas():
     M, V = 300, 262144
     b = dg.SamplerBuffers(M, 2, DEV)
