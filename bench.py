@@ -334,6 +334,116 @@ def per_config(path, reps=20, warm=5):
     print(f"[per-config] wrote {path}", file=sys.stderr, flush=True)
 
 
+def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
+    """The block-autoregressive loop on a paged cache, at the step workload's shapes:
+    a prefill of `prompt` tokens (K/V written through the block table, one causal pass),
+    then `blocks` blocks of denoise steps (canvas draft K/V written, bidirectional
+    attention, sampler, self-conditioning) until the convergence rule fires, each
+    committed by a causal pass over its 256 tokens, the next canvas placed after it.
+    The logits follow the same synthetic settling driver as the step loop, so a block
+    takes 12 steps. Writes JSON to `path` and prints one line."""
+    import torch
+    import block_denoising_step_amd as dg
+    from workloads import Seq, embed_table, driver_pool, driver_rows, request_seeds, CAUSAL, BIDIR
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dg.load()
+    stream = torch.cuda.current_stream()
+    bf = torch.bfloat16
+
+    def gen(seed, shape, std=1.0):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        return (torch.randn(shape, device=dev, generator=g) * std).to(bf)
+
+    total = prompt + blocks * CANVAS
+    nblk = -(-total // block_size)
+    table = torch.randperm(nblk, generator=torch.Generator().manual_seed(214091)).to(dev, torch.int32)
+    kp = torch.zeros(nblk * block_size, HKV, D, device=dev, dtype=bf)
+    vp = torch.zeros_like(kp)
+    E = torch.from_numpy(embed_table(2, VOCAB, EMBED, bf16=True)).to(dev).to(bf)
+    pool = torch.from_numpy(driver_pool(VOCAB, bf16=True)).to(dev).to(bf)
+    step_logits = [pool[torch.from_numpy(driver_rows(t)).to(dev)].contiguous() for t in range(9)]
+    seed = request_seeds(2, 1)[0]
+    # the model's stand-in: prompt K/V and queries, two alternating canvas drafts, commit rows
+    pk, pv, pq = gen(214101, (prompt, HKV, D)), gen(214102, (prompt, HKV, D)), gen(214103, (prompt, HQ, D))
+    dk = [gen(214111 + i, (CANVAS, HKV, D)) for i in range(2)]
+    dv = [gen(214121 + i, (CANVAS, HKV, D)) for i in range(2)]
+    dq = [gen(214131 + i, (CANVAS, HQ, D)) for i in range(2)]
+    ck, cv, cq = gen(214141, (CANVAS, HKV, D)), gen(214142, (CANVAS, HKV, D)), gen(214143, (CANVAS, HQ, D))
+    out_p = torch.empty(prompt, HQ, D, device=dev, dtype=bf)
+    out_c = torch.empty(CANVAS, HQ, D, device=dev, dtype=bf)
+    bufs = dg.SamplerBuffers(CANVAS, 1, dev, vocab=VOCAB, probs_dtype=bf)
+    sc_out = torch.empty(CANVAS, EMBED, device=dev, dtype=bf)
+    flags = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+    samp_calls = [dg.prepare_sampler(step_logits[t], [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, stable_k=STABLE_K,
+                                     tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR) for t in range(9)]
+    init_call = dg.prepare_sampler(None, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
+                                   num_rows=CANVAS)
+    sc_call = dg.prepare_selfcond(bufs.probs, E, sc_out, p_scale=bufs.probs_scale)
+
+    def run():
+        steps = []
+        dg.prepare_kv_write(pk, pv, kp, vp, [(0, prompt, 0, 0)], table, block_size)(stream)
+        dg.prepare_attn(pq, kp, vp, out_p, [Seq(0, prompt, 0, 0, CAUSAL)], -1, HQ, HKV, block_table=table,
+                        block_size=block_size)(stream)
+        prefix, issued = prompt, 0
+        for b in range(blocks):
+            draft = [dg.prepare_kv_write(dk[i], dv[i], kp, vp, [(0, CANVAS, 0, prefix)], table, block_size)
+                     for i in range(2)]
+            attn = [dg.prepare_attn(dq[i], kp, vp, out_c, [Seq(0, CANVAS, 0, prefix, BIDIR)], -1, HQ, HKV,
+                                    block_table=table, block_size=block_size) for i in range(2)]
+            init_call.args._keep[0].seed = (seed + b) & ((1 << 64) - 1)
+            init_call(stream)
+            t, pending = 0, None
+            while True:
+                draft[t % 2](stream)
+                attn[t % 2](stream)
+                samp = samp_calls[min(t, 8)]
+                samp.args._keep[0].step = t
+                samp.args._keep[0].seed = (seed + b) & ((1 << 64) - 1)
+                slot = issued % 2
+                samp.args.converged = flags[slot:slot + 1].data_ptr()
+                samp(stream)
+                sc_call(stream)
+                ev = torch.cuda.Event()
+                ev.record(stream)
+                issued += 1
+                t += 1
+                done = False
+                if pending is not None:  # the previous step's flag, read while this step runs
+                    pending[0].synchronize()
+                    done = bool(flags[pending[1]].item())
+                pending = (ev, slot)
+                if done or t >= STEP_LIMIT:
+                    break  # the step just issued was speculative
+            ev.synchronize()
+            steps.append(t - 1 if done else t)
+            dg.prepare_kv_write(ck, cv, kp, vp, [(0, CANVAS, 0, prefix)], table, block_size)(stream)
+            dg.prepare_attn(cq, kp, vp, out_c, [Seq(0, CANVAS, 0, prefix, CAUSAL)], -1, HQ, HKV,
+                            block_table=table, block_size=block_size)(stream)
+            prefix += CANVAS
+        torch.cuda.synchronize()
+        return steps, issued
+
+    run()  # warm-up pass
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    steps, issued = run()
+    elapsed = time.perf_counter() - t0
+    res = {"workload": f"block loop on a paged cache: prompt {prompt}, {blocks} blocks of {CANVAS} tokens, "
+                       f"16 q / 8 kv heads x 256, vocab {VOCAB}, embed {EMBED}, cache blocks of {block_size} rows",
+           "committed_tokens_per_s": round(blocks * CANVAS / elapsed, 1),
+           "denoise_steps_per_s": round(issued / elapsed, 1),
+           "steps_per_block": steps, "steps_issued": issued, "seconds": round(elapsed, 5),
+           "note": "includes the prefill, one speculative step per block, the commit passes and the "
+                   "host's flag reads"}
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +452,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--per-config", metavar="PATH",
                     help="instead of the step loop, time every call of the five workloads and write JSON to PATH")
+    ap.add_argument("--block-loop", metavar="PATH",
+                    help="instead of the step loop, time the block-autoregressive loop on a paged cache; JSON to PATH")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -351,6 +463,9 @@ def main():
         sys.exit(2)
     if args.per_config:
         per_config(args.per_config)
+        return
+    if args.block_loop:
+        block_loop(args.block_loop)
         return
 
     import torch
