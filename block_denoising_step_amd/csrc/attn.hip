@@ -554,10 +554,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   const AttnSeqPlan sp = a.seqs[s_];
   const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
-  const int qt = local % nqt;  // q tiles of one (kv head, chunk) are consecutive
+  // items [key chunk][kv head][q tile]: the q tiles of one (chunk, head) are consecutive,
+  // and a run of xcd_order's deal covers one head, so an XCD keeps to few heads' Q
+  const int qt = local % nqt;
   const int rest = local / nqt;
-  const int chunk = rest % sp.num_chunks;
-  const int g = rest / sp.num_chunks;
+  const int g = rest % a.hkv;
+  const int chunk = rest / a.hkv;
   const int i0 = qt * sp.tokens_per_tile;
   const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
   const int nkeys = sp.prefix_len + sp.num_q;
@@ -894,10 +896,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   const AttnSeqPlan sp = a.seqs[s_];
   const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
-  const int qt = local % nqt;
+  const int qt = local % nqt;  // items [key chunk][kv head][q tile], as in attn_fwd_bf16_d256
   const int rest = local / nqt;
-  const int chunk = rest % sp.num_chunks;
-  const int g = rest / sp.num_chunks;
+  const int g = rest % a.hkv;
+  const int chunk = rest / a.hkv;
   const int i0 = qt * sp.tokens_per_tile;
   const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
   const int nkeys = sp.prefix_len + sp.num_q;

@@ -12,7 +12,8 @@ namespace dg {
 
 // ---- attention ---------------------------------------------------------------
 //
-// Work is laid out per request as [kv head][key chunk][q tile]. A q tile holds
+// Work is laid out per request as [key chunk][kv head][q tile] in the bf16 head_dim-256
+// kernels and [kv head][q tile][key chunk] in the general one. A q tile holds
 // tile_rows query rows (tokens x grouped heads); a key chunk is a run of 64-key
 // tiles. Every q tile of a request gets the same number of chunks (a chunk past a
 // tile's keys is empty and exits at once). The kernel finds its (request, head,
