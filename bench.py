@@ -257,6 +257,23 @@ def per_config(path, reps=20, warm=5):
         del q, k, v, o
         return res
 
+    def inject_call(name, M=CANVAS, d=EMBED, hidden=2048, V=VOCAB):
+        """dg_selfcond_inject at the step's shapes (bf16): two MFMA GEMMs (gate/up and down,
+        6 M d hidden flops) and the weights read once (3 d hidden values)."""
+        E = gen(seed_for(2, TID_E), (V, d), std=0.02)
+        tokens = torch.randint(0, V, (M,), generator=torch.Generator().manual_seed(seed_for(2, 10))).to(dev, torch.int32)
+        s = gen(seed_for(2, 11), (M, d))
+        wgu = gen(seed_for(2, 12), (d, 2 * hidden), std=d ** -0.5)
+        wd = gen(seed_for(2, 13), (hidden, d), std=hidden ** -0.5)
+        out = torch.empty(M, d, device=dev, dtype=torch.bfloat16)
+        call = dg.prepare_inject(tokens, E, s, wgu, wd, out)
+        flop = 6 * M * d * hidden
+        nbytes = 2 * (3 * d * hidden + 3 * M * d) + 4 * M
+        e = entry(med_us(call), flop, nbytes, False)
+        print(f"[per-config] {name}: {e}", file=sys.stderr, flush=True)
+        del E
+        return e
+
     def kv_write_call(name, counts, B=256, hkv=8, d=256):
         """dg_kv_write of `counts` new rows per request (each request's rows after a
         4096-row cache in its own table), bf16: reads and writes each K/V byte once."""
@@ -313,6 +330,7 @@ def per_config(path, reps=20, warm=5):
     c2 = attn_case(2)
     r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)], paged_block=256)
     r["kv_write_canvas256"] = kv_write_call("cfg2 kv_write_canvas256", [256])
+    r["selfcond_inject_hidden2048"] = inject_call("cfg2 selfcond_inject_hidden2048")
     r.update(sampler_and_selfcond(2, True))
     out["configs"]["2"] = r
     c3 = attn_case(3)

@@ -82,8 +82,15 @@ class DgSelfcondArgs(ctypes.Structure):
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class DgInjectArgs(ctypes.Structure):
+    _fields_ = [("M", _c_int32), ("d", _c_int32), ("hidden", _c_int32), ("vocab", _c_int32), ("dtype", _c_int32),
+                ("tokens", _vp), ("embed", _vp), ("s", _vp), ("w_gate_up", _vp), ("w_down", _vp), ("out", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+
+
 EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sampler_workspace_size",
-           "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_status_string", "dg_last_error",
+           "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_selfcond_inject",
+           "dg_selfcond_inject_workspace_size", "dg_status_string", "dg_last_error",
            "dg_abi_version"]
 
 _lib = None
@@ -115,6 +122,10 @@ def load() -> ctypes.CDLL:
     lib.dg_selfcond_embed.restype = ctypes.c_int
     lib.dg_selfcond_workspace_size.argtypes = [ctypes.POINTER(DgSelfcondArgs)]
     lib.dg_selfcond_workspace_size.restype = ctypes.c_size_t
+    lib.dg_selfcond_inject.argtypes = [ctypes.POINTER(DgInjectArgs), _vp]
+    lib.dg_selfcond_inject.restype = ctypes.c_int
+    lib.dg_selfcond_inject_workspace_size.argtypes = [ctypes.POINTER(DgInjectArgs)]
+    lib.dg_selfcond_inject_workspace_size.restype = ctypes.c_size_t
     lib.dg_kv_write.argtypes = [ctypes.POINTER(DgKvWriteArgs), _vp]
     lib.dg_kv_write.restype = ctypes.c_int
     lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -251,6 +262,44 @@ def dg_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, 
 def prepare_kv_write(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size):
     a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size)
     return Prepared(load().dg_kv_write, a, ())
+
+
+# ---- dg_selfcond_inject ------------------------------------------------------------
+
+def make_inject_args(tokens, embed, s, w_gate_up, w_down, out):
+    """tokens [M] int32; embed [V, d]; s [M, d]; w_gate_up [d, 2h]; w_down [h, d]; out [M, d]."""
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be int32")
+    a = DgInjectArgs()
+    a.M, a.d = s.shape[0], s.shape[1]
+    a.hidden = w_down.shape[0]
+    a.vocab = embed.shape[0]
+    a.dtype = _dtype(s)
+    a.tokens, a.embed, a.s, a.w_gate_up, a.w_down, a.out = (_ptr(tokens), _ptr(embed), _ptr(s), _ptr(w_gate_up),
+                                                            _ptr(w_down), _ptr(out))
+    return a
+
+
+def inject_workspace_size(args: DgInjectArgs) -> int:
+    return load().dg_selfcond_inject_workspace_size(ctypes.byref(args))
+
+
+def dg_selfcond_inject(tokens, embed, s, w_gate_up, w_down, out, workspace=None, stream=None):
+    """out = embed[tokens] + GeGLU(s) (see include/dg.h). Returns the workspace used."""
+    a = make_inject_args(tokens, embed, s, w_gate_up, w_down, out)
+    ws = _workspace(inject_workspace_size(a), s, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().dg_selfcond_inject(ctypes.byref(a), _stream(stream)))
+    return ws
+
+
+def prepare_inject(tokens, embed, s, w_gate_up, w_down, out):
+    a = make_inject_args(tokens, embed, s, w_gate_up, w_down, out)
+    ws = _workspace(inject_workspace_size(a), s, None)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel()
+    return Prepared(load().dg_selfcond_inject, a, (ws,))
 
 
 # ---- dg_sampler_step -------------------------------------------------------------

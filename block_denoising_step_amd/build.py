@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["dg_host.cpp", "sampler.hip", "selfcond.hip", "attn.hip", "kvcache.hip"]
+SOURCES = ["dg_host.cpp", "sampler.hip", "selfcond.hip", "attn.hip", "kvcache.hip", "inject.hip"]
 
 # Packed-fp32 instructions are kept out of every code object (the compiler would
 # otherwise form v_pk_* from plain float code).

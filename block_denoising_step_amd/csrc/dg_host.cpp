@@ -366,6 +366,57 @@ dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char
   return DG_OK;
 }
 
+// ---- self-conditioning injection ------------------------------------------------
+
+dg_status inject_plan(const dg_inject_args* a, InjectPlan* plan, const char** msg) {
+  auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
+  if (!a) return bad(DG_ERR_INVALID_ARG, "args is NULL");
+  if (a->M < 1 || a->vocab < 1) return bad(DG_ERR_INVALID_ARG, "M and vocab must be >= 1");
+  if (a->d < 128 || a->d % 128 || a->hidden < 128 || a->hidden % 128)
+    return bad(DG_ERR_UNSUPPORTED, "d and hidden must be positive multiples of 128");
+  if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (!a->tokens || !a->embed || !a->s || !a->w_gate_up || !a->w_down || !a->out)
+    return bad(DG_ERR_INVALID_ARG, "tokens, embed, s, w_gate_up, w_down and out must be non-NULL");
+  if (!aligned4(a->tokens) || !aligned16(a->embed) || !aligned16(a->s) || !aligned16(a->w_gate_up) ||
+      !aligned16(a->w_down) || !aligned16(a->out))
+    return bad(DG_ERR_INVALID_ARG, "tokens must be 4-byte and the other tensors 16-byte aligned");
+  const size_t esz = a->dtype == DG_BF16 ? 2 : 4;
+  void* const fake = reinterpret_cast<void*>(uintptr_t{256});  // a workspace address, set at launch
+  dg_selfcond_args& g1 = plan->gemm1;
+  g1 = dg_selfcond_args{};
+  g1.M = a->M;
+  g1.V = a->d;
+  g1.d = 2 * a->hidden;
+  g1.dtype = a->dtype;
+  g1.p = a->s;
+  g1.ldp = a->d;
+  g1.embed = a->w_gate_up;
+  g1.lde = 2 * a->hidden;
+  g1.out = fake;
+  g1.ldo = 2 * a->hidden;
+  dg_selfcond_args& g2 = plan->gemm2;
+  g2 = dg_selfcond_args{};
+  g2.M = a->M;
+  g2.V = a->hidden;
+  g2.d = a->d;
+  g2.dtype = a->dtype;
+  g2.p = fake;
+  g2.ldp = a->hidden;
+  g2.embed = a->w_down;
+  g2.lde = a->d;
+  g2.out = a->out;
+  g2.ldo = a->d;
+  dg_status st = selfcond_plan(&g1, &plan->plan1, msg);
+  if (st != DG_OK) return st;
+  st = selfcond_plan(&g2, &plan->plan2, msg);
+  if (st != DG_OK) return st;
+  plan->gu_offset = 0;
+  plan->h_offset = align_up((size_t)a->M * 2 * a->hidden * esz, 256);
+  plan->gemm_ws_offset = plan->h_offset + align_up((size_t)a->M * a->hidden * esz, 256);
+  plan->bytes = plan->gemm_ws_offset + std::max(plan->plan1.bytes, plan->plan2.bytes);
+  return DG_OK;
+}
+
 }  // namespace dg
 
 // ---- C ABI -------------------------------------------------------------------
@@ -444,6 +495,26 @@ dg_status dg_selfcond_embed(const dg_selfcond_args* a, void* stream) {
   if (plan.bytes && (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace)))
     return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_selfcond_workspace_size");
   int e = launch_selfcond(a, plan, stream);
+  if (e) return fail(DG_ERR_HIP, hip_error_name(e));
+  g_last_error[0] = 0;
+  return DG_OK;
+}
+
+size_t dg_selfcond_inject_workspace_size(const dg_inject_args* a) {
+  InjectPlan plan;
+  const char* msg = "";
+  if (inject_plan(a, &plan, &msg) != DG_OK) return (size_t)-1;
+  return plan.bytes;
+}
+
+dg_status dg_selfcond_inject(const dg_inject_args* a, void* stream) {
+  InjectPlan plan;
+  const char* msg = "";
+  dg_status s = inject_plan(a, &plan, &msg);
+  if (s != DG_OK) return fail(s, msg);
+  if (!a->workspace || a->workspace_bytes < plan.bytes || !aligned16(a->workspace))
+    return fail(DG_ERR_WORKSPACE, "workspace missing, misaligned or smaller than dg_selfcond_inject_workspace_size");
+  int e = launch_inject(a, plan, stream);
   if (e) return fail(DG_ERR_HIP, hip_error_name(e));
   g_last_error[0] = 0;
   return DG_OK;

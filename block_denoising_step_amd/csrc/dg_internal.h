@@ -89,12 +89,26 @@ struct KvWritePlan {
 };
 dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char** msg);
 
+// ---- self-conditioning injection ------------------------------------------------
+
+struct InjectPlan {
+  dg_selfcond_args gemm1;   // s . w_gate_up -> gu [M, 2 hidden] (workspace)
+  dg_selfcond_args gemm2;   // h . w_down -> out
+  SelfcondPlan plan1, plan2;
+  size_t gu_offset, h_offset, gemm_ws_offset;  // workspace layout
+  size_t bytes;
+};
+// Validates args (everything but the workspace) and fills the plan; the GEMM argument
+// structs get their workspace pointers when the workspace is known (the call).
+dg_status inject_plan(const dg_inject_args* a, InjectPlan* plan, const char** msg);
+
 // ---- launchers (HIP side); return 0 on success or a hipError_t value ---------
 
 int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream);
 int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stream);
 int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream);
 int launch_kv_write(const dg_kv_write_args* a, const KvWritePlan& plan, void* stream);
+int launch_inject(const dg_inject_args* a, InjectPlan& plan, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace dg

@@ -304,6 +304,38 @@ typedef struct {
 
 dg_status dg_kv_write(const dg_kv_write_args* args, void* stream);
 
+/* ------------------------------------------------------------------------------
+ * dg_selfcond_inject: the canvas embedding with the self-conditioning vector injected
+ * ([P1] section "안정성을 위한 셀프 컨디셔닝": the probability-weighted average of token
+ * embeddings is added to the canvas embedding through a gated MLP; section
+ * "ModelState 인터페이스": prepare_inputs handles the canvas embedding and the
+ * self-conditioning). The pages name the gated MLP but not its form; this call takes
+ * the plainest one, a GeGLU with the tanh GELU, no bias:
+ *   out[i, :] = embed[tokens[i], :] + (gelu(s[i] . Wg) * (s[i] . Wu)) . Wd
+ *   gelu(x)   = x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ * where Wg = w_gate_up[:, 0:hidden] and Wu = w_gate_up[:, hidden:2 hidden] (weights are
+ * [in, out], row-major: x . W). Products accumulate in fp32; the gate/up product and
+ * the GeGLU output are rounded to the input dtype, as is out.
+ * ------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t M;                    /* canvas rows, >= 1 */
+  int32_t d;                    /* model width, a multiple of 128 */
+  int32_t hidden;               /* MLP width, a multiple of 128 */
+  int32_t vocab;                /* rows of embed, >= 1 */
+  int32_t dtype;                /* dg_dtype of every float tensor */
+  const int32_t* tokens;        /* device [M] canvas tokens; an entry outside [0, vocab) is clamped into it */
+  const void* embed;            /* device [vocab, d] token embedding table */
+  const void* s;                /* device [M, d] self-conditioning vectors (dg_selfcond_embed's output) */
+  const void* w_gate_up;        /* device [d, 2 * hidden] */
+  const void* w_down;           /* device [hidden, d] */
+  void* out;                    /* device [M, d] */
+  void* workspace;              /* device, >= dg_selfcond_inject_workspace_size(args) bytes */
+  size_t workspace_bytes;
+} dg_inject_args;
+
+dg_status dg_selfcond_inject(const dg_inject_args* args, void* stream);
+size_t dg_selfcond_inject_workspace_size(const dg_inject_args* args);
+
 /* ------------------------------------------------------------------------------ */
 const char* dg_status_string(dg_status s); /* static string for a status */
 const char* dg_last_error(void);           /* message of this thread's last failed call */

@@ -22,3 +22,4 @@ from .philox import philox4x64_10, uniform24, renoise_token  # noqa: F401
 from .sampler import (row_stats, candidate, select, convergence, sampler_step,  # noqa: F401
                       CONF_NEG_ENTROPY, CONF_MAX_PROB, CONV_AND, CONV_OR, FIXED_SHIFT)
 from .selfcond import selfcond_embed, softmax_rows  # noqa: F401
+from .inject import selfcond_inject, gelu_tanh  # noqa: F401

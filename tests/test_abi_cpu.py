@@ -185,6 +185,38 @@ def test_kv_write_nothing_to_write_is_ok():
     assert dg.load().dg_kv_write(ctypes.byref(a), None) == dg.DG_OK
 
 
+def _inject(**over):
+    a = dg.make_inject_args(_T((256,), dtype="i32"), _T((4096, 256)), _T((256, 256)), _T((256, 512)),
+                            _T((256, 256)), _T((256, 256)))
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(M=0), dg.DG_ERR_INVALID_ARG), (dict(vocab=0), dg.DG_ERR_INVALID_ARG),
+    (dict(d=200), dg.DG_ERR_UNSUPPORTED), (dict(hidden=64), dg.DG_ERR_UNSUPPORTED),
+    (dict(dtype=4), dg.DG_ERR_INVALID_ARG), (dict(tokens=None), dg.DG_ERR_INVALID_ARG),
+    (dict(tokens=FAKE + 2), dg.DG_ERR_INVALID_ARG), (dict(w_down=FAKE + 8), dg.DG_ERR_INVALID_ARG),
+    (dict(out=None), dg.DG_ERR_INVALID_ARG),
+])
+def test_inject_validation(change, status):
+    a = _inject(**change)
+    assert dg.load().dg_selfcond_inject(ctypes.byref(a), None) == status
+    assert dg.last_error()
+
+
+def test_inject_workspace():
+    a = _inject()
+    need = dg.inject_workspace_size(a)
+    # gate/up [M, 2h] and GeGLU [M, h] intermediates at least
+    assert need >= 256 * 3 * 256 * 2
+    assert dg.load().dg_selfcond_inject(ctypes.byref(a), None) == dg.DG_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert dg.load().dg_selfcond_inject(ctypes.byref(a), None) == dg.DG_ERR_WORKSPACE
+    assert dg.inject_workspace_size(_inject(M=0)) == ctypes.c_size_t(-1).value
+
+
 def _sampler(**over):
     bufs = dg.SamplerBuffers.__new__(dg.SamplerBuffers)
     for n in ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
