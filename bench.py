@@ -352,6 +352,20 @@ def per_config(path, reps=20, warm=5):
     print(f"[per-config] wrote {path}", file=sys.stderr, flush=True)
 
 
+def wait_flag(flags, slot, timeout_s=30.0):
+    """Spin until the selection kernel has written slot `slot` of the pinned flag pair
+    (the host set it to -1 before enqueueing that step); return the flag."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        f = int(flags[slot].item())
+        if f >= 0:
+            return f
+        n += 1
+        if n % 4096 == 0 and time.perf_counter() - t0 > timeout_s:
+            raise RuntimeError("the converged flag of a step was not written in time")
+
+
 def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
     """The block-autoregressive loop on a paged cache, at the step workload's shapes:
     a prefill of `prompt` tokens (K/V written through the block table, one causal pass),
@@ -422,21 +436,21 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
                 samp.args._keep[0].step = t
                 samp.args._keep[0].seed = (seed + b) & ((1 << 64) - 1)
                 slot = issued % 2
+                flags[slot] = -1
                 samp.args.converged = flags[slot:slot + 1].data_ptr()
                 samp(stream)
                 sc_call(stream)
-                ev = torch.cuda.Event()
-                ev.record(stream)
                 issued += 1
                 t += 1
                 done = False
                 if pending is not None:  # the previous step's flag, read while this step runs
-                    pending[0].synchronize()
-                    done = bool(flags[pending[1]].item())
-                pending = (ev, slot)
+                    done = bool(wait_flag(flags, pending))
+                pending = slot
                 if done or t >= STEP_LIMIT:
-                    break  # the step just issued was speculative
-            ev.synchronize()
+                    # the step just issued was speculative; its flag slot is reused two
+                    # steps on, so wait until it has been written
+                    wait_flag(flags, pending)
+                    break
             steps.append(t - 1 if done else t)
             dg.prepare_kv_write(ck, cv, kp, vp, [(0, CANVAS, 0, prefix)], table, block_size)(stream)
             dg.prepare_attn(cq, kp, vp, out_c, [Seq(0, CANVAS, 0, prefix, CAUSAL)], -1, HQ, HKV,
@@ -525,7 +539,10 @@ def main():
     stream = torch.cuda.current_stream()
     # The selection writes each step's converged flag straight into pinned host memory,
     # alternating between two slots so that step t never overwrites the flag of step t-1
-    # before the host has read it; no copy sits on the stream between steps.
+    # before the host has read it. The host sets a slot to -1 before the step that
+    # writes it is enqueued, then waits for a 0 or 1 there: the flag itself says that the
+    # step's selection has run, so neither a copy nor an event (whose record costs about
+    # 6 us of GPU time) sits on the stream between steps.
     flags = torch.zeros(2, dtype=torch.int32, pin_memory=True)
 
     if args.copy_calibration_mib:
@@ -548,55 +565,52 @@ def main():
 
     def one_step(ev=None):
         """Enqueue one step; return the previous step's converged flag. ev: None, or four
-        events [before attention, after attention, before self-conditioning, after it],
-        of which the first two may be None (an event record costs about 2 us of GPU time,
-        so attention and the sampler are timed on a sample of the steps only)."""
+        events [before attention, after attention, before self-conditioning, after it]
+        (a sample of the timed steps is bracketed by events: each record costs GPU time)."""
         t = state["t"]
         i = min(t, settle - 1)
         samp = samp_calls[i]
         samp.args._keep[0].step = t
         samp.args._keep[0].seed = (seed + state["block"]) & ((1 << 64) - 1)
         slot = state["issued"] % 2
+        flags[slot] = -1  # its last value (two steps back) has been read
         samp.args.converged = flags[slot:slot + 1].data_ptr()
-        if ev is not None and ev[0] is not None:
+        if ev is not None:
             ev[0].record(stream)
         attn_call(stream)
-        if ev is not None and ev[1] is not None:
+        if ev is not None:
             ev[1].record(stream)
         samp(stream)
         if ev is not None:
             ev[2].record(stream)
         sc_call(stream)
         if ev is not None:
-            ev[3].record(stream)  # also the event the host waits on for this step's flag
-            fe = ev[3]
-        else:
-            fe = torch.cuda.Event()
-            fe.record(stream)
+            ev[3].record(stream)
         state["issued"] += 1
         state["t"] = t + 1
         # the host reads the previous step's flag while this step runs on the GPU
         prev_done = False
         if state["pending"] is not None:
-            pev, pslot = state["pending"]
-            pev.synchronize()
-            prev_done = bool(flags[pslot].item())
-        state["pending"] = (fe, slot)
+            prev_done = bool(wait_flag(flags, state["pending"]))
+        state["pending"] = slot
         return prev_done
 
     def run(n, events=None):
         for s_ in range(n):
             if one_step(events[s_] if events is not None else None) or state["t"] >= STEP_LIMIT:
-                state["block"] += 1  # converged: the step just issued was speculative; start a new block
+                # converged: the step just issued was speculative. Its flag slot is reused
+                # two steps on, so wait until it has been written before the new block
+                wait_flag(flags, state["pending"])
+                state["block"] += 1
                 start_block()
 
     start_block()
     run(args.warmup)
     torch.cuda.synchronize()
-    # self-conditioning (the roofline kernel) is timed on every step, attention and the
-    # sampler on every SAMPLE_EVERY-th step
+    # every SAMPLE_EVERY-th timed step is bracketed by events (per-call times, including
+    # the roofline kernel's); the others run without any
     SAMPLE_EVERY = 8
-    events = [[torch.cuda.Event(enable_timing=True) if (i % SAMPLE_EVERY == 0 or j >= 2) else None for j in range(4)]
+    events = [[torch.cuda.Event(enable_timing=True) for j in range(4)] if i % SAMPLE_EVERY == 0 else None
               for i in range(args.steps)]
     blocks0 = state["block"]
     torch.cuda.synchronize()
@@ -606,10 +620,10 @@ def main():
     elapsed = time.perf_counter() - t0
     blocks = state["block"] - blocks0
 
-    sampled = [e for e in events if e[0] is not None]
+    sampled = [e for e in events if e is not None]
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sampled]))
     samp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sampled]))
-    sc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    sc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sampled]))
     alg = algorithmic()
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps / elapsed
@@ -660,8 +674,8 @@ def main():
                              "frac_hbm_peak_with_probs_write": round(samp_rw_gbs / PEAK_HBM_GBS, 4)},
             "selfcond_embed": {"ms": round(sc_ms, 4), "gbs": round(sc_gbs, 1), "tflops": round(sc_tflops, 1),
                                "frac_hbm_peak": round(sc_gbs / PEAK_HBM_GBS, 4)},
-            "timing": f"HIP events on the launch stream: self-conditioning on all {args.steps} timed steps, "
-                      f"attention and sampler on {len(sampled)} of them (every {SAMPLE_EVERY}th)",
+            "timing": f"HIP events on the launch stream around each call, on {len(sampled)} of the {args.steps} "
+                      f"timed steps (every {SAMPLE_EVERY}th)",
         },
     }
     if not args.no_cpu_baseline:
