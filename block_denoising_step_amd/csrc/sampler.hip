@@ -315,8 +315,18 @@ __device__ __forceinline__ long long block_exclusive_scan_ll(long long v, long l
 // Selection for request r by one work group of kThreads: rank sort by (confidence
 // desc, position asc), exact integer prefix sum of floor(H * 2^40), budget cut, canvas
 // update and convergence bookkeeping. Every input is loaded up front.
+// Sort key of position j with confidence c: c's bits made order-preserving as an
+// unsigned integer (-0 folded into +0 first, so that equal confidences give equal
+// keys) in the high word, ~j in the low word. key_i > key_j exactly when c_i > c_j,
+// or c_i == c_j and i < j (confidences are finite).
+__device__ __forceinline__ uint64_t rank_key(float c, int j) {
+  const uint32_t u = __float_as_uint(c + 0.f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)j;
+}
+
 __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& sp, const RowOut& o) {
-  __shared__ __attribute__((aligned(16))) float key[DG_MAX_CANVAS + 16];
+  __shared__ __attribute__((aligned(16))) uint64_t key[DG_MAX_CANVAS + 16];
   __shared__ long long sorted[DG_MAX_CANVAS];
   __shared__ long long wred[kWaves];
   __shared__ int ired[kWaves];
@@ -326,6 +336,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
   const uint64_t seed = reqs.seed[r];
   const int prev_stable = o.stable_count[r];  // loaded early: the bookkeeping at the end needs it
   float c[kPerThread];
+  uint64_t kj[kPerThread];
   long long fx[kPerThread];
   int am[kPerThread], cand[kPerThread], old[kPerThread];
   long long sum = 0;
@@ -334,6 +345,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
   for (int q = 0; q < kPerThread; ++q) {
     const int j = tid + kThreads * q;
     c[q] = kNegInf;
+    kj[q] = 0;
     fx[q] = 0;
     am[q] = cand[q] = old[q] = 0;
     if (j < n) {
@@ -345,34 +357,27 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
       cand[q] = o.cand[row0 + j];
       old[q] = o.canvas[row0 + j];
       sum += fx[q];
-      key[j] = c[q];
+      kj[q] = rank_key(c[q], j);
+      key[j] = kj[q];
     }
   }
-  // pad to a multiple of 16 with -inf: a finite confidence never ranks below it
-  if (tid < 16) key[n + tid] = kNegInf;
+  // pad to a multiple of 16 with 0, below every position's key
+  if (tid < 16) key[n + tid] = 0;
   __syncthreads();
   int rank[kPerThread];
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) rank[q] = 0;
-  // rank = #{i : key_i > c_j or (key_i == c_j and i < j)}; 16 keys per iteration,
-  // read as float4 so the loads pipeline
+  // rank_j = #{i : key_i > key_j} = #{i : c_i > c_j or (c_i == c_j and i < j)};
+  // 16 keys per iteration, read 2 per 16-byte load so the loads pipeline
   for (int i0 = 0; i0 < n; i0 += 16) {
-    float4 k4[4];
+    ulonglong2 k2[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) k4[u] = *reinterpret_cast<const float4*>(&key[i0 + 4 * u]);
+    for (int u = 0; u < 8; ++u) k2[u] = *reinterpret_cast<const ulonglong2*>(&key[i0 + 2 * u]);
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
-      const int j = tid + kThreads * q;
       if (kThreads * q >= n) break;  // no thread has a position here (uniform)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float kv[4] = {k4[u].x, k4[u].y, k4[u].z, k4[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + 4 * u + e;
-          rank[q] += (kv[e] > c[q]) || (kv[e] == c[q] && i < j);
-        }
-      }
+      for (int u = 0; u < 8; ++u) rank[q] += (int)(k2[u].x > kj[q]) + (int)(k2[u].y > kj[q]);
     }
   }
 #pragma unroll
