@@ -103,6 +103,8 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
       return bad(DG_ERR_INVALID_ARG, "seq key rows exceed total_kv");
     if (paged && (int64_t)q.kv_start + ceil_div((int64_t)q.prefix_len + q.num_q, a->block_size) > a->block_table_len)
       return bad(DG_ERR_INVALID_ARG, "seq block table entries exceed block_table_len");
+    if (paged && (int64_t)q.kv_start + ceil_div((int64_t)q.prefix_len + q.num_q, a->block_size) > INT32_MAX)
+      return bad(DG_ERR_UNSUPPORTED, "seq block table entries past index 2^31 - 1");
     if ((int64_t)q.prefix_len + q.num_q > INT32_MAX - kKeyTile) return bad(DG_ERR_INVALID_ARG, "seq too long");
     if (q.num_q > 0) qranges.push_back({q.q_start, (int64_t)q.q_start + q.num_q});
   }
@@ -355,6 +357,9 @@ dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char
     if ((int64_t)q.src_start + q.num > a->total_new) return bad(DG_ERR_INVALID_ARG, "seq source rows exceed total_new");
     if ((int64_t)q.table_start + ceil_div((int64_t)q.pos + q.num, a->block_size) > a->block_table_len)
       return bad(DG_ERR_INVALID_ARG, "seq block table entries exceed block_table_len");
+    if ((int64_t)q.table_start + ceil_div((int64_t)q.pos + q.num, a->block_size) > INT32_MAX ||
+        (int64_t)q.pos + q.num > INT32_MAX)
+      return bad(DG_ERR_UNSUPPORTED, "seq block table entries or positions past 2^31 - 1");
     rows += q.num;
   }
   plan->row_bytes = (int64_t)a->num_kv_heads * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);

@@ -180,6 +180,16 @@ def test_kv_write_validation(change, status):
     assert dg.last_error()
 
 
+def test_paged_table_indices_stay_in_32_bits():
+    """Table indices are 32-bit in the kernels: a table range past 2^31 - 1 is refused."""
+    a = _attn(seqs=[(0, 32, 2**31 - 2, 64, BIDIR)])
+    a.block_size, a.block_table, a.block_table_len, a.total_kv = 64, FAKE, 2**40, 64
+    assert _status(a) == dg.DG_ERR_UNSUPPORTED
+    k = _kv(seqs=[(0, 32, 2**31 - 1, 10)])
+    k.block_table_len = 2**40
+    assert dg.load().dg_kv_write(ctypes.byref(k), None) == dg.DG_ERR_UNSUPPORTED
+
+
 def test_kv_write_nothing_to_write_is_ok():
     a = _kv(seqs=[(0, 0, 0, 0)])
     assert dg.load().dg_kv_write(ctypes.byref(a), None) == dg.DG_OK
