@@ -555,8 +555,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
   // items [key chunk][kv head][q tile]: the q tiles of one (chunk, head) are consecutive,
-  // and a run of xcd_order's deal covers one head, so an XCD keeps to few heads' Q
-  const int qt = local % nqt;
+  // and a run of xcd_order's deal covers one head, so an XCD keeps to few heads' Q. A
+  // causal request's later q tiles see more keys: they come first, so that the long
+  // items of every chunk start early and short ones fill in behind them.
+  const int qt = sp.mode == DG_CAUSAL ? nqt - 1 - local % nqt : local % nqt;
   const int rest = local / nqt;
   const int g = rest % a.hkv;
   const int chunk = rest / a.hkv;
@@ -896,7 +898,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   const AttnSeqPlan sp = a.seqs[s_];
   const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
   const int local = w - sp.work_begin;
-  const int qt = local % nqt;  // items [key chunk][kv head][q tile], as in attn_fwd_bf16_d256
+  // items [key chunk][kv head][q tile], causal q tiles longest first, as in attn_fwd_bf16_d256
+  const int qt = sp.mode == DG_CAUSAL ? nqt - 1 - local % nqt : local % nqt;
   const int rest = local / nqt;
   const int g = rest % a.hkv;
   const int chunk = rest / a.hkv;
