@@ -473,21 +473,35 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restr
                                                              SelectParams sp, RowOut o) {
   using VT = Vec<kBf16>;
   __shared__ float mass_s[kWaves][1024];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index (so the row and its request) is uniform: scalar loads and branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * kWaves + wave;
   if (row >= num_rows) return;
   float* mass = mass_s[wave];
   const float4* st = stats + (int64_t)row * num_chunks;
 
+  // this lane's first chunk statistics, loaded before the work below so that it waits
+  // on them: which request (if any) owns this row, and its candidate's uniform u
+  // (Philox counter (step, position, stream 0))
+  const float4 s_first = lane < num_chunks ? st[lane] : make_float4(kNegInf, 0.f, 0.f, 0.f);
+  int r = -1;
+  for (int i = 0; i < reqs.n; ++i)
+    if (row >= reqs.row_start[i] && row < reqs.row_start[i] + reqs.num_rows[i]) r = i;
+  float u = 0.f;
+  if (r >= 0) {
+    const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)reqs.step[r], (uint64_t)(row - reqs.row_start[r]), 0);
+    u = (float)(x0 >> 40) * 0x1p-24f;
+  }
+
   // merge the chunk statistics (lane c, c + 64, ... in order)
-  float mx = kNegInf;
-  for (int c = lane; c < num_chunks; c += 64) mx = fmaxf(mx, st[c].x);
+  float mx = s_first.x;
+  for (int c = lane + 64; c < num_chunks; c += 64) mx = fmaxf(mx, st[c].x);
   const float m = wave_max(mx);
   const float nm2 = -m * kLog2e;
   float z = 0.f, t = 0.f;
   int am = INT_MAX;
   for (int c = lane; c < num_chunks; c += 64) {
-    const float4 s = st[c];
+    const float4 s = c == lane ? s_first : st[c];
     float mc = 0.f;
     if (s.x != kNegInf) {
       const float delta = nm2 - (-s.x * kLog2e);  // <= 0: chunk's y offset relative to the row
@@ -529,19 +543,12 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restr
     o.argmax[row] = amax;
   }
 
-  // which request (if any) owns this row
-  int r = -1;
-  for (int i = 0; i < reqs.n; ++i)
-    if (row >= reqs.row_start[i] && row < reqs.row_start[i] + reqs.num_rows[i]) r = i;
   if (r < 0) {
     if (lane == 0) o.cand[row] = -1;
     return;
   }
   // candidate: the first token whose cumulative mass exceeds u*Z. Rounding can leave
   // u*Z past the mass a level sums to; then the last token with mass is taken.
-  const int j = row - reqs.row_start[r];
-  const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)reqs.step[r], (uint64_t)j, 0);
-  const float u = (float)(x0 >> 40) * 0x1p-24f;
   const float target = u * Z;
   // level 1: chunks
   float carry = 0.f, rem = 0.f;
