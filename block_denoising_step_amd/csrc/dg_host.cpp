@@ -137,8 +137,14 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
       units += nt * a->num_kv_heads;
     }
     if (a->kv_chunk > 0) r.chunk_tiles = a->kv_chunk / kKeyTile;
-    // a request too small to fill the GPU even at one tile per chunk takes one-tile chunks
-    else r.chunk_tiles = units < kTargetGroups ? 1 : std::max<int64_t>(kMinChunkTiles, ceil_div(units, kTargetGroups));
+    // a request too small to fill the GPU even at one tile per chunk takes one-tile chunks;
+    // otherwise every q tile gets as many chunks as its longest key range needs, so the
+    // chunk is sized from that range: about kTargetGroups work groups in all (a causal
+    // request's shorter q tiles leave some of their chunks empty)
+    else r.chunk_tiles = units < kTargetGroups
+                             ? 1
+                             : std::max<int64_t>(kMinChunkTiles,
+                                                 ceil_div(max_tiles * r.ntiles_q * a->num_kv_heads, kTargetGroups));
     r.nch = max_tiles > 0 ? ceil_div(max_tiles, r.chunk_tiles) : 0;
     r.sub_tiles = units * (kKeyTile / 32);  // 32-key sub-tiles over all (q tile, kv head) units
     return r;
