@@ -198,6 +198,31 @@ def test_stability_counting_and_convergence():
              stable_k=3, tau=5.0, combine=comb, label=f"stability comb={comb}")
 
 
+def test_selection_ties_and_signed_zero_entropies():
+    """Entropies fed in (DG_ENTROPY_IN) in groups of exactly equal values, with +0 and
+    -0 among them (equal confidences) and a budget that cuts inside a tie group: ties
+    rank by position, so the accepted set is the oracle's bit for bit."""
+    M, V = 256, 64
+    rng = np.random.default_rng(21)
+    l = (rng.standard_normal((M, V)) * 2).astype(np.float32)
+    vals = np.array([0.0, -0.0, 0.75, 0.75, 1.5, 0.125, 2.0, 0.125], np.float32)
+    ent = np.repeat(vals, M // len(vals))[rng.permutation(M)].astype(np.float32)
+    ent[rng.integers(0, M, 20)] = -0.0
+    for budget in (3.3, 10.0, 40.1):
+        ref = sampler_step(l, [(0, M, 3, 1)], V, budget, 1, np.zeros(M, np.int64), np.full(M, -1, np.int64), [0],
+                           entropy_in=ent, with_candidates=False)
+        b = dg.SamplerBuffers(M, 1, DEV)
+        b.entropy.copy_(torch.from_numpy(ent))
+        dg.dg_sampler_step(dev(l), [(0, M, 3, 1)], V, b, budget, flags=dg.DG_ENTROPY_IN)
+        torch.cuda.synchronize()
+        acc = host(b.accept).astype(bool)
+        say(f"[sampler] ties, budget {budget}: accepted {int(acc.sum())} (oracle {int(ref['accept'].sum())})")
+        assert np.array_equal(acc, ref["accept"])
+        assert host(b.num_accepted)[0] == ref["num_accepted"][0]
+        # a tie group straddles the cut: its accepted members are its lowest positions
+        assert 0 < acc.sum() < M
+
+
 def test_converged_flag_into_pinned_host_memory():
     """The selection writes the converged flag straight into pinned host memory (read
     by the host after the step completes, with no copy on the stream); over several
