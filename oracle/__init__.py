@@ -23,3 +23,5 @@ from .sampler import (row_stats, candidate, select, convergence, sampler_step,  
                       CONF_NEG_ENTROPY, CONF_MAX_PROB, CONV_AND, CONV_OR, FIXED_SHIFT)
 from .selfcond import selfcond_embed, softmax_rows  # noqa: F401
 from .inject import selfcond_inject, gelu_tanh  # noqa: F401
+from .fp8 import (e4m3_value, e4m3_decode, e4m3_encode, quantize, dequantize, attn_mixed_fp8,  # noqa: F401
+                  attn_mixed_paged_fp8, kv_write_fp8, E4M3_MAX)
