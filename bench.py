@@ -145,9 +145,11 @@ def key_range(mode, prefix, num_q, window, i):
     return lo, hi
 
 
-def attn_work(seqs, window, hq, hkv, d, esz):
+def attn_work(seqs, window, hq, hkv, d, esz, kv_esz=None):
     """Algorithmic FLOPs and bytes of one attention call: allowed (query, key) pairs,
-    Q and O once, each touched K/V row once per KV head."""
+    Q and O once, each touched K/V row once per KV head (kv_esz bytes per K/V element:
+    1 for an FP8 cache)."""
+    kv_esz = esz if kv_esz is None else kv_esz
     pairs, touched, nq = 0, 0, 0
     for s in seqs:
         if s.num_q == 0:
@@ -156,7 +158,7 @@ def attn_work(seqs, window, hq, hkv, d, esz):
         pairs += sum(h - l + 1 for l, h in zip(los, his))
         touched += max(his) - min(los) + 1  # key ranges of consecutive queries overlap or touch
         nq += s.num_q
-    return 4 * d * hq * pairs, esz * (2 * nq * hq * d + 2 * touched * hkv * d)
+    return 4 * d * hq * pairs, esz * 2 * nq * hq * d + kv_esz * 2 * touched * hkv * d
 
 
 def per_config(path, reps=20, warm=5):
@@ -232,7 +234,18 @@ def per_config(path, reps=20, warm=5):
             b0 += nb
         return kp.view((-1,) + tuple(k.shape[1:])), vp.view((-1,) + tuple(k.shape[1:])), perm.to(dev, torch.int32), pseqs
 
-    def attn_calls(case, variants, paged_block=0):
+    def fp8_codes(x, scale):
+        """bf16 K or V rows as E4M3 codes, quantized by dg_kv_write into a pool whose
+        table is the identity (so the pool is the contiguous layout); rows past the
+        input's end stay zero."""
+        B = 256
+        nb = -(-x.shape[0] // B)
+        pool = torch.zeros((nb * B,) + tuple(x.shape[1:]), device=dev, dtype=torch.float8_e4m3fn)
+        table = torch.arange(nb, device=dev, dtype=torch.int32)
+        dg.dg_kv_write(x, x, pool, pool, [(0, x.shape[0], 0, 0)], table, B, k_scale=scale, v_scale=scale)
+        return pool
+
+    def attn_calls(case, variants, paged_block=0, fp8=False):
         dt = torch.bfloat16 if case.bf16 else torch.float32
         esz = 2 if case.bf16 else 4
         q = gen(seed_for(case.cfg, 1), (case.total_q, case.num_q_heads, case.head_dim), dtype=dt)
@@ -254,6 +267,18 @@ def per_config(path, reps=20, warm=5):
                 res[pname] = entry(med_us(c), flop, nbytes, not case.bf16)
                 print(f"[per-config] cfg{case.cfg} {pname}: {res[pname]}", file=sys.stderr, flush=True)
                 del kp, vp, table
+        if fp8:
+            # the same calls over an FP8 (E4M3) cache: K/V bytes halve, queries and output stay bf16
+            sc = 1.0 / 64
+            k8, v8 = fp8_codes(k, sc), fp8_codes(v, sc)
+            for name, seqs, window in variants:
+                c = dg.prepare_attn(q, k8, v8, o, seqs, window, case.num_q_heads, case.num_kv_heads, k_scale=sc,
+                                    v_scale=sc)
+                flop, nbytes = attn_work(seqs, window, case.num_q_heads, case.num_kv_heads, case.head_dim, esz, 1)
+                fname = f"{name}_fp8_kv"
+                res[fname] = entry(med_us(c), flop, nbytes, False)
+                print(f"[per-config] cfg{case.cfg} {fname}: {res[fname]}", file=sys.stderr, flush=True)
+            del k8, v8
         del q, k, v, o
         return res
 
@@ -328,7 +353,7 @@ def per_config(path, reps=20, warm=5):
     r.update(sampler_and_selfcond(1, True))
     out["configs"]["1"] = r
     c2 = attn_case(2)
-    r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)], paged_block=256)
+    r = attn_calls(c2, [("attn_bidir_global", c2.seqs, -1)], paged_block=256, fp8=True)
     r["kv_write_canvas256"] = kv_write_call("cfg2 kv_write_canvas256", [256])
     r["selfcond_inject_hidden2048"] = inject_call("cfg2 selfcond_inject_hidden2048")
     r.update(sampler_and_selfcond(2, True))
@@ -337,13 +362,14 @@ def per_config(path, reps=20, warm=5):
     out["configs"]["3"] = attn_calls(c3, [("attn_bidir_w512", c3.seqs, 512),
                                           ("attn_causal_w512", c3.with_mode(CAUSAL).seqs, 512)])
     c4 = attn_case(4)
-    r = attn_calls(c4, [("attn_global_layer", c4.seqs, -1), ("attn_w512_layer", c4.seqs, 512)], paged_block=256)
+    r = attn_calls(c4, [("attn_global_layer", c4.seqs, -1), ("attn_w512_layer", c4.seqs, 512)], paged_block=256,
+                   fp8=True)
     r["kv_write_prefill2048_and_commit256"] = kv_write_call("cfg4 kv_write_prefill2048_and_commit256", [2048, 256])
     r.update(sampler_and_selfcond(4, False))
     out["configs"]["4"] = r
     torch.cuda.empty_cache()
     c5 = attn_case(5)
-    r = attn_calls(c5, [("attn_bidir_global", c5.seqs, -1)], paged_block=256)
+    r = attn_calls(c5, [("attn_bidir_global", c5.seqs, -1)], paged_block=256, fp8=True)
     torch.cuda.empty_cache()
     r.update(sampler_and_selfcond(5, True))
     out["configs"]["5"] = r

@@ -43,7 +43,8 @@ class DgAttnArgs(ctypes.Structure):
                 ("scale", ctypes.c_float), ("dtype", _c_int32), ("total_q", _c_int64), ("total_kv", _c_int64),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("out", _vp), ("lse", _vp), ("kv_chunk", _c_int32),
                 ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
-                ("block_size", _c_int32), ("block_table", _vp), ("block_table_len", _c_int64)]
+                ("block_size", _c_int32), ("block_table", _vp), ("block_table_len", _c_int64),
+                ("kv_fp8", _c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class DgKvSeq(ctypes.Structure):
@@ -54,7 +55,8 @@ class DgKvWriteArgs(ctypes.Structure):
     _fields_ = [("num_seqs", _c_int32), ("seqs", ctypes.POINTER(DgKvSeq)), ("num_kv_heads", _c_int32),
                 ("head_dim", _c_int32), ("dtype", _c_int32), ("block_size", _c_int32), ("block_table", _vp),
                 ("block_table_len", _c_int64), ("total_new", _c_int64), ("pool_rows", _c_int64),
-                ("k_new", _vp), ("v_new", _vp), ("k_pool", _vp), ("v_pool", _vp)]
+                ("k_new", _vp), ("v_new", _vp), ("k_pool", _vp), ("v_pool", _vp),
+                ("pool_fp8", _c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class DgSreq(ctypes.Structure):
@@ -163,6 +165,11 @@ def _dtype(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _is_fp8(t: torch.Tensor) -> bool:
+    """E4M3 codes: torch.float8_e4m3fn, or raw codes in uint8."""
+    return t.dtype in (torch.float8_e4m3fn, torch.uint8)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -183,9 +190,10 @@ def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor
 
 def make_attn_args(q, k, v, out, seqs: Sequence, window: int, num_q_heads: int, num_kv_heads: int,
                    lse=None, scale: float = 0.0, kv_chunk: int = 0, workspace=None, block_table=None,
-                   block_size: int = 0):
+                   block_size: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
     """block_size > 0: k/v are paged pools and block_table an int32 device tensor; each
-    request's kv_start is then the index of its first table entry."""
+    request's kv_start is then the index of its first table entry. k/v of dtype
+    float8_e4m3fn (or uint8) hold E4M3 codes whose values are code * k_scale / v_scale."""
     seq_arr = (DgSeq * max(1, len(seqs)))()
     for i, s in enumerate(seqs):
         f = (s.q_start, s.num_q, s.kv_start, s.prefix_len, s.mode) if hasattr(s, "q_start") else tuple(s)
@@ -201,6 +209,10 @@ def make_attn_args(q, k, v, out, seqs: Sequence, window: int, num_q_heads: int, 
     a.total_q, a.total_kv = q.shape[0], k.shape[0]
     a.q, a.k, a.v, a.out, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
     a.kv_chunk = kv_chunk
+    a.kv_fp8 = int(_is_fp8(k))
+    if a.kv_fp8 != int(_is_fp8(v)):
+        raise TypeError("k and v must both hold E4M3 codes, or neither")
+    a.k_scale, a.v_scale = (k_scale, v_scale) if a.kv_fp8 else (0.0, 0.0)
     a.block_size = block_size
     if block_size:
         if block_table is None or block_table.dtype != torch.int32:
@@ -217,12 +229,14 @@ def attn_workspace_size(args: DgAttnArgs) -> int:
 def dg_attn_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, seqs: Sequence,
                   window: int, num_q_heads: int, num_kv_heads: int, lse: Optional[torch.Tensor] = None,
                   scale: float = 0.0, kv_chunk: int = 0, workspace: Optional[torch.Tensor] = None,
-                  stream=None, block_table: Optional[torch.Tensor] = None, block_size: int = 0) -> Optional[torch.Tensor]:
+                  stream=None, block_table: Optional[torch.Tensor] = None, block_size: int = 0,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> Optional[torch.Tensor]:
     """Mixed-mode attention (see include/dg.h). q [T, Hq, D], k/v [S, Hkv, D], out like q,
     lse [T, Hq] fp32 or None; with block_size > 0, k/v are paged pools read through
-    block_table. Returns the workspace tensor used (reusable)."""
+    block_table; k/v in float8_e4m3fn (or uint8) are E4M3 codes with scales k_scale and
+    v_scale. Returns the workspace tensor used (reusable)."""
     a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk,
-                       block_table=block_table, block_size=block_size)
+                       block_table=block_table, block_size=block_size, k_scale=k_scale, v_scale=v_scale)
     ws = _workspace(attn_workspace_size(a), q, workspace)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -232,8 +246,10 @@ def dg_attn_mixed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
 
 # ---- dg_kv_write -----------------------------------------------------------------
 
-def make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs: Sequence, block_table, block_size: int):
-    """seqs: (src_start, num, table_start, pos) per request."""
+def make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs: Sequence, block_table, block_size: int,
+                       k_scale: float = 1.0, v_scale: float = 1.0):
+    """seqs: (src_start, num, table_start, pos) per request. Pools of dtype float8_e4m3fn
+    (or uint8) take E4M3 codes of the new values at scales k_scale and v_scale."""
     if block_table.dtype != torch.int32:
         raise TypeError("block_table must be an int32 tensor")
     arr = (DgKvSeq * max(1, len(seqs)))()
@@ -248,19 +264,25 @@ def make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs: Sequence, block_table
     a.block_table, a.block_table_len = _ptr(block_table), block_table.numel()
     a.total_new, a.pool_rows = k_new.shape[0], k_pool.shape[0]
     a.k_new, a.v_new, a.k_pool, a.v_pool = _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool)
+    a.pool_fp8 = int(_is_fp8(k_pool))
+    if a.pool_fp8 != int(_is_fp8(v_pool)):
+        raise TypeError("k_pool and v_pool must both hold E4M3 codes, or neither")
+    a.k_scale, a.v_scale = (k_scale, v_scale) if a.pool_fp8 else (0.0, 0.0)
     a._keep = arr
     return a
 
 
 def dg_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                seqs: Sequence, block_table: torch.Tensor, block_size: int, stream=None) -> None:
-    """Scatter new K/V rows [T, Hkv, D] into paged pools [rows, Hkv, D] (see include/dg.h)."""
-    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size)
+                seqs: Sequence, block_table: torch.Tensor, block_size: int, stream=None, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> None:
+    """Scatter new K/V rows [T, Hkv, D] into paged pools [rows, Hkv, D] (see include/dg.h);
+    pools of E4M3 codes take the quantized values."""
+    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size, k_scale, v_scale)
     _check(load().dg_kv_write(ctypes.byref(a), _stream(stream)))
 
 
-def prepare_kv_write(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size):
-    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size)
+def prepare_kv_write(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size, k_scale=1.0, v_scale=1.0):
+    a = make_kv_write_args(k_new, v_new, k_pool, v_pool, seqs, block_table, block_size, k_scale, v_scale)
     return Prepared(load().dg_kv_write, a, ())
 
 
@@ -430,9 +452,9 @@ class Prepared:
 
 
 def prepare_attn(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse=None, scale=0.0, kv_chunk=0,
-                 block_table=None, block_size=0):
+                 block_table=None, block_size=0, k_scale=1.0, v_scale=1.0):
     a = make_attn_args(q, k, v, out, seqs, window, num_q_heads, num_kv_heads, lse, scale, kv_chunk,
-                       block_table=block_table, block_size=block_size)
+                       block_table=block_table, block_size=block_size, k_scale=k_scale, v_scale=v_scale)
     ws = _workspace(attn_workspace_size(a), q, None)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel()

@@ -16,6 +16,11 @@
 //   O^T += V^T . P^T (MFMA 32x32; P^T taken straight from the S^T accumulators,
 //   V transposed into LDS with the key order permuted to match them), so the
 //   softmax rescale of O is a per-lane multiply.
+// FP8 K/V (OCP E4M3 codes with per-tensor scales, the FP8 configuration of [P1]
+// section "성능 및 양자화"): attn_fwd's <kFp8> instance loads 8 codes where it loaded
+// 8 bf16 and widens them to bf16 while staging the tile, exactly (every E4M3 value
+// is a bf16 value), so the LDS layout and the inner loop are the bf16 ones; k_scale
+// is folded into the score scale and v_scale into the output normalisation.
 // A request whose keys were split into several chunks writes partials: O of the
 // chunk normalised by its own sum, in the input dtype, plus the chunk's (max, sum)
 // in fp32; attn_merge combines them in chunk order.
@@ -39,7 +44,8 @@ struct AttnArgs {
   float* part_ml;
   int hq, hkv, group, window, num_seqs;
   int work_offset;  // work index of this launch's block 0
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e) (times k_scale for FP8 K/V)
+  float v_scale;     // FP8 K/V: the value scale, applied with the output normalisation
   const int32_t* block_table;  // paged K/V: a request's table starts at its kv_start
   int64_t pool_blocks;         // blocks in the K and V pools
   int block_shift;             // log2(block_size)
@@ -132,11 +138,34 @@ struct Lds {
   static constexpr int v_bytes = D * v_pitch;
 };
 
+// Two E4M3 codes (bytes 0-1, or 2-3 with kHi, of w) as two bf16 in one word. The
+// conversion is to fp32 and exact, and an E4M3 value needs at most 4 significant
+// bits, so the upper half of each fp32 is its bf16 value.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// The 16 LDS bytes of chunk c of a staged row: 16 source bytes, or 8 E4M3 codes
+// widened to 8 bf16.
+template <bool kFp8>
+__device__ __forceinline__ uint4 load_chunk(const char* row, int c) {
+  if constexpr (!kFp8) {
+    return *reinterpret_cast<const uint4*>(row + c * 16);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + c * 8);
+    return make_uint4(e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
+                      e4m3x2_to_bf16x2<true>(w.y));
+  }
+}
+
 // Stage one 64-key tile of K (row-major) and V (transposed) into LDS. Key rows at
-// or past `nkeys` (request-local) are zero.
-template <bool kBf16, int D>
+// or past `nvalid` (request-local) are zero. kFp8: the source rows hold E4M3 codes.
+template <bool kBf16, int D, bool kFp8 = false>
 __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, const char* vg, int64_t row_stride,
                                            int nvalid) {
+  static_assert(kBf16 || !kFp8, "FP8 K/V are widened to bf16");
   using L = Lds<kBf16, D>;
   constexpr int esz = L::esz;
   constexpr int cpr = D * esz / 16;  // 16-byte chunks per key row
@@ -146,7 +175,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   for (int q = tid; q < kKT * cpr; q += kThreads) {
     const int key = q / cpr, col = q % cpr;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < nvalid) val = *reinterpret_cast<const uint4*>(kg + (int64_t)key * row_stride + col * 16);
+    if (key < nvalid) val = load_chunk<kFp8>(kg + (int64_t)key * row_stride, col);
     *reinterpret_cast<uint4*>(lk + key * L::k_pitch + col * 16) = val;
   }
   // V^T: within each 16-key group, key w sits at position w with bits 2 and 3 swapped
@@ -161,7 +190,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
       for (int j = 0; j < 8; ++j) {
         const int key = 16 * a16 + 4 * c + (j & 3) + ((j >> 2) << 3);
         r[j] = make_uint4(0, 0, 0, 0);
-        if (key < nvalid) r[j] = *reinterpret_cast<const uint4*>(vg + (int64_t)key * row_stride + dgp * 16);
+        if (key < nvalid) r[j] = load_chunk<kFp8>(vg + (int64_t)key * row_stride, dgp);
       }
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -197,11 +226,12 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   }
 }
 
-template <bool kBf16, int D, bool kPaged>
+template <bool kBf16, int D, bool kPaged, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   using OP = Op<kBf16>;
   using L = Lds<kBf16, D>;
   constexpr int esz = L::esz;
+  constexpr int kv_esz = kFp8 ? 1 : esz;  // bytes per K/V element in HBM
   constexpr int KS = D / 16;  // k16 steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide output blocks
   __shared__ __attribute__((aligned(16))) char lk[L::k_bytes];
@@ -253,15 +283,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   float m_run = kNegInf;  // running max of scale*log2e*score (base-2 units)
   float l_run = 0.f;      // this lane's share of the running sum
 
-  const int64_t row_stride = (int64_t)a.hkv * D * esz;
-  const char* kg = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * esz;
-  const char* vg = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * esz;
+  const int64_t row_stride = (int64_t)a.hkv * D * kv_esz;
+  const char* kg = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * kv_esz;
+  const char* vg = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * kv_esz;
 
   for (int kt = t_begin; kt < t_end; ++kt) {
     const int k0 = kt * kKT;
     const int64_t r0 = key_row<kPaged>(a, sp, k0) * row_stride;  // the tile's 64 rows are consecutive
     __syncthreads();  // previous tile fully consumed
-    stage_tile<kBf16, D>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
+    stage_tile<kBf16, D, kFp8>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
     __syncthreads();
 
     // S^T blocks: sblk[kb][i] = score of key k0 + 32kb + 8(i/4) + 4hh + i%4 for this lane's row
@@ -330,7 +360,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!valid) return;
   {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if constexpr (kFp8) inv *= a.v_scale;
     const int64_t prow = sp.part_begin + (int64_t)local * kRows + row;
     char* orow = sp.num_chunks == 1
                      ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * esz
@@ -1230,6 +1261,17 @@ int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
+// FP8 K/V: the register-staged kernel at bf16, then the merge of bf16 partials
+template <int D, bool kPaged>
+int launch_fp8(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
+  if (plan.num_work > 0) {
+    args.work_offset = 0;
+    hipLaunchKernelGGL((attn_fwd<true, D, kPaged, true>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
+  }
+  if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<true, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream) {
@@ -1256,7 +1298,17 @@ int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream) {
   args.block_shift = plan.block_shift;
   for (int i = 0; i < plan.num_seqs; ++i) args.seqs[i] = plan.seqs[i];
   for (int i = plan.num_seqs; i < DG_MAX_SEQS; ++i) args.seqs[i] = AttnSeqPlan{};
+  args.v_scale = 1.f;
   const bool paged = plan.block_shift >= 0;
+  if (plan.kv_fp8) {
+    args.scale_log2 = scale * a->k_scale * kLog2e;
+    args.v_scale = a->v_scale;
+    switch (a->head_dim) {
+      case 64: return paged ? launch_fp8<64, true>(args, plan, s) : launch_fp8<64, false>(args, plan, s);
+      case 128: return paged ? launch_fp8<128, true>(args, plan, s) : launch_fp8<128, false>(args, plan, s);
+      default: return paged ? launch_fp8<256, true>(args, plan, s) : launch_fp8<256, false>(args, plan, s);
+    }
+  }
   if (a->dtype == DG_BF16) {
     switch (a->head_dim) {
       case 64: return paged ? launch_typed<true, 64, true>(args, plan, s) : launch_typed<true, 64, false>(args, plan, s);

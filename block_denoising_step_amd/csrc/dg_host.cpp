@@ -76,6 +76,14 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
     return bad(DG_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (a->lse && !aligned4(a->lse)) return bad(DG_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  // FP8 K/V: E4M3 codes with per-tensor scales, bf16 queries; the register-staged kernel
+  if (a->kv_fp8 != 0 && a->kv_fp8 != 1) return bad(DG_ERR_INVALID_ARG, "kv_fp8 must be 0 or 1");
+  plan->kv_fp8 = a->kv_fp8;
+  if (a->kv_fp8) {
+    if (a->dtype != DG_BF16) return bad(DG_ERR_UNSUPPORTED, "kv_fp8 needs dtype DG_BF16");
+    if (!std::isfinite(a->k_scale) || !(a->k_scale > 0.f) || !std::isfinite(a->v_scale) || !(a->v_scale > 0.f))
+      return bad(DG_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0 with kv_fp8");
+  }
   // paged K/V: pools of block_size-row blocks, a block table per request
   const bool paged = a->block_size != 0;
   plan->block_shift = -1;
@@ -116,7 +124,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   // that request alone, so its result is the same whatever else is in the batch.
   // The LDS-DMA kernels (bf16, head_dim 256) take 32-bit byte offsets within a request's K/V.
   // Paged requests are addressed per sub-tile, so only the contiguous layout has the limit.
-  plan->dma = a->dtype == DG_BF16 && a->head_dim == 256;
+  plan->dma = a->dtype == DG_BF16 && a->head_dim == 256 && !a->kv_fp8;
   for (int s = 0; s < a->num_seqs && !paged; ++s) {
     const dg_seq& q = a->seqs[s];
     if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
@@ -344,6 +352,10 @@ dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char
   if (a->num_seqs < 1 || a->num_seqs > DG_MAX_SEQS) return bad(DG_ERR_INVALID_ARG, "num_seqs must be in [1, DG_MAX_SEQS]");
   if (!a->seqs) return bad(DG_ERR_INVALID_ARG, "seqs is NULL");
   if (a->dtype != DG_F32 && a->dtype != DG_BF16) return bad(DG_ERR_INVALID_ARG, "dtype must be DG_F32 or DG_BF16");
+  if (a->pool_fp8 != 0 && a->pool_fp8 != 1) return bad(DG_ERR_INVALID_ARG, "pool_fp8 must be 0 or 1");
+  if (a->pool_fp8 && (!std::isfinite(a->k_scale) || !(a->k_scale > 0.f) || !std::isfinite(a->v_scale) ||
+                      !(a->v_scale > 0.f)))
+    return bad(DG_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0 with pool_fp8");
   if (a->num_kv_heads < 1) return bad(DG_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
   if (a->head_dim < 8 || a->head_dim % 8) return bad(DG_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8");
   if (a->block_size < 1 || (a->block_size & (a->block_size - 1)))
@@ -369,11 +381,17 @@ dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char
     rows += q.num;
   }
   plan->row_bytes = (int64_t)a->num_kv_heads * a->head_dim * (a->dtype == DG_BF16 ? 2 : 4);
+  plan->pool_fp8 = a->pool_fp8;
+  // the reciprocals of the scales, rounded to fp32 once, here
+  plan->k_inv = a->pool_fp8 ? 1.0f / a->k_scale : 0.f;
+  plan->v_inv = a->pool_fp8 ? 1.0f / a->v_scale : 0.f;
   plan->total_rows = rows;
   int sh = 0;
   while ((1 << sh) < a->block_size) ++sh;
   plan->block_shift = sh;
-  if (rows * (plan->row_bytes / 16) > INT32_MAX) return bad(DG_ERR_UNSUPPORTED, "too many rows for one call");
+  // threads: one per 16 source bytes (a copy) or per 8 elements (quantized)
+  const int64_t per_row = a->pool_fp8 ? (int64_t)a->num_kv_heads * a->head_dim / 8 : plan->row_bytes / 16;
+  if (rows * per_row > INT32_MAX) return bad(DG_ERR_UNSUPPORTED, "too many rows for one call");
   return DG_OK;
 }
 

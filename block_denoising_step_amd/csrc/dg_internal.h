@@ -47,6 +47,7 @@ struct AttnPlan {
   int64_t part_rows;    // partial rows (each D wide)
   int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB (or paged): LDS-DMA kernel
   int block_shift;      // paged K/V: log2(block_size); -1 for the contiguous layout
+  int kv_fp8;           // K/V hold E4M3 codes (bf16 queries, register-staged kernel)
   size_t part_o_offset;   // workspace: [part_rows][D] partial outputs, input dtype
   size_t part_ml_offset;  // workspace: [part_rows][2] fp32 (max, sum) in log2 units
   size_t bytes;
@@ -83,9 +84,11 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
 // ---- paged K/V writes ----------------------------------------------------------
 
 struct KvWritePlan {
-  int64_t row_bytes;   // bytes of one key row (Hkv * D * element size)
+  int64_t row_bytes;   // bytes of one source row (Hkv * D * element size of dtype)
   int64_t total_rows;  // rows written over all requests
   int block_shift;     // log2(block_size)
+  int pool_fp8;        // pools hold E4M3 codes: values are quantized
+  float k_inv, v_inv;  // pool_fp8: 1 / k_scale and 1 / v_scale, rounded to fp32
 };
 dg_status kv_write_plan(const dg_kv_write_args* a, KvWritePlan* plan, const char** msg);
 

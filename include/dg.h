@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 2
+#define DG_ABI_VERSION 3
 #define DG_MAX_SEQS 64      /* requests per dg_attn_mixed call */
 #define DG_MAX_REQS 64      /* requests per dg_sampler_step call */
 #define DG_MAX_CANVAS 1024  /* positions per sampler request */
@@ -96,6 +96,16 @@ typedef enum { DG_CAUSAL = 0, DG_BIDIR = 1 } dg_mode;
  * device data and are not checked on the host: an entry outside [0, total_kv /
  * block_size) gives unspecified results for that request (the kernels clamp it, so
  * they never read outside the pools). dg_kv_write fills the pools.
+ *
+ * FP8 K/V (kv_fp8 = 1). The measured model runs in FP8 ([P1] section "성능 및
+ * 양자화"; [P3] section "Izmjerene performanse"). In this mode k and v hold one byte
+ * per element, a code of the OCP 8-bit floating point format E4M3 (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN; largest
+ * finite 448), in the same layouts as above (contiguous or paged), and
+ *   k[j, g, :] = code * k_scale,   v[j, g, :] = code * v_scale
+ * enter the formulas above. q and out stay bf16 (dtype must be DG_BF16); the codes
+ * are widened to bf16 exactly and the products accumulate in fp32; k_scale joins the
+ * score scale and v_scale the output normalisation, both in fp32.
  * ------------------------------------------------------------------------------ */
 typedef struct {
   int32_t q_start, num_q, kv_start, prefix_len, mode; /* mode: dg_mode */
@@ -123,6 +133,9 @@ typedef struct {
   int32_t block_size;           /* 0: contiguous K/V; else a power of two >= 64, dividing total_kv (paged) */
   const int32_t* block_table;   /* device [block_table_len] int32 when block_size > 0, else ignored */
   int64_t block_table_len;      /* every request needs kv_start + ceil((prefix_len + num_q) / block_size) <= this */
+  int32_t kv_fp8;               /* 0: k and v are in dtype; 1: k and v hold E4M3 codes (dtype must be DG_BF16) */
+  float k_scale;                /* kv_fp8: finite, > 0; ignored otherwise */
+  float v_scale;                /* kv_fp8: finite, > 0; ignored otherwise */
 } dg_attn_args;
 
 dg_status dg_attn_mixed(const dg_attn_args* args, void* stream);
@@ -277,6 +290,10 @@ size_t dg_selfcond_workspace_size(const dg_selfcond_args* args);
  * Rows of the pools that no request writes are left untouched. Target rows of
  * different requests must not overlap (they would race). Table entries are not
  * checked on the host; the kernel skips a row whose entry lies outside the pool.
+ * FP8 pools (pool_fp8 = 1): the pools hold E4M3 codes, one byte per element (the
+ * format dg_attn_mixed reads with kv_fp8 = 1), and each new value x (in dtype) is
+ * quantized: y = x * r in fp32, r = 1 / scale rounded to fp32 on the host, y clamped
+ * to [-448, 448], then the nearest E4M3 value, ties to the even code (NaN stays NaN).
  * ------------------------------------------------------------------------------ */
 typedef struct {
   int32_t src_start;            /* first row of k_new / v_new */
@@ -290,7 +307,7 @@ typedef struct {
   const dg_kv_seq* seqs;        /* host array [num_seqs] */
   int32_t num_kv_heads;         /* Hkv >= 1 */
   int32_t head_dim;             /* D >= 8, a multiple of 8 */
-  int32_t dtype;                /* dg_dtype of all four tensors */
+  int32_t dtype;                /* dg_dtype of k_new and v_new (and of the pools unless pool_fp8) */
   int32_t block_size;           /* a power of two >= 1 */
   const int32_t* block_table;   /* device [block_table_len] int32 */
   int64_t block_table_len;      /* every request needs table_start + ceil((pos + num) / block_size) <= this */
@@ -298,8 +315,11 @@ typedef struct {
   int64_t pool_rows;            /* rows of k_pool / v_pool, a multiple of block_size */
   const void* k_new;            /* device [total_new, Hkv, D] */
   const void* v_new;            /* device [total_new, Hkv, D] */
-  void* k_pool;                 /* device [pool_rows, Hkv, D] */
-  void* v_pool;                 /* device [pool_rows, Hkv, D] */
+  void* k_pool;                 /* device [pool_rows, Hkv, D], dtype, or E4M3 codes when pool_fp8 */
+  void* v_pool;                 /* device [pool_rows, Hkv, D], dtype, or E4M3 codes when pool_fp8 */
+  int32_t pool_fp8;             /* 0: pools in dtype (a copy); 1: E4M3 pools, values quantized */
+  float k_scale;                /* pool_fp8: finite, > 0; ignored otherwise */
+  float v_scale;                /* pool_fp8: finite, > 0; ignored otherwise */
 } dg_kv_write_args;
 
 dg_status dg_kv_write(const dg_kv_write_args* args, void* stream);

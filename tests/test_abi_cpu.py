@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(dg.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dg_abi_version() == 2
+    assert lib.dg_abi_version() == 3
     for s in range(5):
         assert lib.dg_status_string(s).decode().startswith("DG_")
 
@@ -40,7 +40,8 @@ class _T:
         self.shape = shape
         self._ptr = ptr
         import torch
-        self.dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}[dtype]
+        self.dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32,
+                      "fp8": torch.float8_e4m3fn}[dtype]
 
     def data_ptr(self):
         return self._ptr
@@ -150,6 +151,53 @@ def test_attn_paged_sizes_a_workspace_and_ignores_the_contiguous_span():
     assert dg.attn_workspace_size(a) != ctypes.c_size_t(-1).value
     a.block_table_len = 6
     assert dg.attn_workspace_size(a) == ctypes.c_size_t(-1).value
+
+
+def _attn_fp8(**over):
+    q = over.pop("q", _T((32, 4, 64)))
+    a = dg.make_attn_args(q, _T((96, 2, 64), dtype="fp8"), _T((96, 2, 64), dtype="fp8"), _T(q.shape),
+                          pack_seqs([(64, 32, BIDIR)]), -1, 4, 2, k_scale=0.5, v_scale=2.0)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def test_attn_fp8_fields_and_validation():
+    a = _attn_fp8()
+    assert a.kv_fp8 == 1 and a.k_scale == 0.5 and a.v_scale == 2.0
+    assert dg.attn_workspace_size(a) != ctypes.c_size_t(-1).value
+    for change, status in [(dict(kv_fp8=2), dg.DG_ERR_INVALID_ARG), (dict(k_scale=0.0), dg.DG_ERR_INVALID_ARG),
+                           (dict(v_scale=-1.0), dg.DG_ERR_INVALID_ARG),
+                           (dict(k_scale=float("inf")), dg.DG_ERR_INVALID_ARG),
+                           (dict(v_scale=float("nan")), dg.DG_ERR_INVALID_ARG),
+                           (dict(dtype=dg.DG_F32), dg.DG_ERR_UNSUPPORTED)]:
+        b = _attn_fp8(**change)
+        assert _status(b) == status, change
+        assert dg.last_error()
+    # the binding refuses a K/V pair of which only one holds codes
+    with pytest.raises(TypeError):
+        dg.make_attn_args(_T((32, 4, 64)), _T((96, 2, 64), dtype="fp8"), _T((96, 2, 64)), _T((32, 4, 64)),
+                          pack_seqs([(64, 32, BIDIR)]), -1, 4, 2)
+    # without codes the scales are not read: zero scales are no error
+    plain = _attn()
+    assert plain.kv_fp8 == 0 and plain.k_scale == 0.0
+    assert dg.attn_workspace_size(plain) != ctypes.c_size_t(-1).value
+
+
+def test_kv_write_fp8_validation():
+    a = dg.make_kv_write_args(_T((32, 2, 64)), _T((32, 2, 64)), _T((256, 2, 64), dtype="fp8"),
+                              _T((256, 2, 64), dtype="fp8"), [(0, 32, 0, 10)], _T((4,), dtype="i32"), 64,
+                              k_scale=0.25, v_scale=4.0)
+    assert a.pool_fp8 == 1 and a.k_scale == 0.25
+    lib = dg.load()
+    for field, val in [("k_scale", 0.0), ("v_scale", float("nan")), ("pool_fp8", 3)]:
+        old = getattr(a, field)
+        setattr(a, field, val)
+        assert lib.dg_kv_write(ctypes.byref(a), None) == dg.DG_ERR_INVALID_ARG, field
+        assert dg.last_error()
+        setattr(a, field, old)
+    a.seqs[0].num = 0
+    assert lib.dg_kv_write(ctypes.byref(a), None) == dg.DG_OK
 
 
 def _kv(**over):
