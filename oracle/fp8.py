@@ -60,24 +60,17 @@ def e4m3_encode(y: np.ndarray) -> np.ndarray:
     """Values -> E4M3 codes: clamp to +-448, nearest value, ties to the even code.
     Zero keeps its sign; NaN gives 0x7F (or 0xFF with the sign bit)."""
     y = np.asarray(y, dtype=np.float64)
-    out = np.empty(y.shape, dtype=np.uint8)
-    flat_y, flat_o = y.reshape(-1), out.reshape(-1)
-    for i, x in enumerate(flat_y):
-        neg = bool(np.signbit(x))
-        if np.isnan(x):
-            flat_o[i] = 0xFF if neg else 0x7F
-            continue
-        a = min(abs(x), E4M3_MAX)
-        # the two codes around a, then the nearer one (ties: even code)
-        hi = int(np.searchsorted(_POS, a, side="left"))  # first code with value >= a
-        if hi < 127 and _POS[hi] == a:
-            c = hi
-        else:
-            lo = hi - 1
-            dl, dh = a - _POS[lo], _POS[hi] - a
-            c = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
-        flat_o[i] = c | (0x80 if neg else 0)
-    return out
+    neg = np.signbit(y)
+    nan = np.isnan(y)
+    a = np.minimum(np.abs(np.where(nan, 0.0, y)), E4M3_MAX)
+    # the two codes around a (values _POS[lo] < a <= _POS[hi]), then the nearer one
+    hi = np.searchsorted(_POS, a, side="left")  # first code with value >= a; <= 126
+    lo = np.maximum(hi - 1, 0)
+    dl, dh = a - _POS[lo], _POS[hi] - a
+    nearest = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    c = np.where(_POS[hi] == a, hi, nearest)
+    c = np.where(nan, 0x7F, c)
+    return (c | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
 def quantize(x: np.ndarray, scale: float) -> np.ndarray:
