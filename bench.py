@@ -502,6 +502,82 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
     print(json.dumps(res), flush=True)
 
 
+def graph_steps(path, args, dg, torch, attn_call, step_logits, bufs, sc_call, seed, flags):
+    """The step loop with every step replayed from a recorded HIP graph: attention, the
+    sampler (reading its step from a device counter that the selection advances) and
+    self-conditioning, recorded once per (logits buffer, converged-flag slot) pair, so
+    the host enqueues one replay per step. Blocks restart with an eager DG_INIT_CANVAS
+    call that zeroes the counter; the seed stays the same from block to block (it is a
+    recorded argument). Writes JSON to `path` and prints one line."""
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    counter = torch.zeros(1, dtype=torch.int32, device=dev)
+    kw = dict(stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR, step_counter=counter)
+    init = dg.prepare_sampler(None, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
+                              num_rows=CANVAS, step_counter=counter)
+    side = torch.cuda.Stream()
+    graphs = []
+    t_rec = time.perf_counter()
+    for lg in step_logits:
+        pair = []
+        for slot in range(2):
+            samp = dg.prepare_sampler(lg, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, **kw)
+            samp.args.converged = flags[slot:slot + 1].data_ptr()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                attn_call()
+                samp()
+                sc_call()
+            pair.append((g, samp))
+        graphs.append(pair)
+    torch.cuda.synchronize()
+    t_rec = time.perf_counter() - t_rec
+    state = {"t": 0, "issued": 0, "pending": None, "blocks": 0}
+
+    def start_block():
+        init(stream)
+        state["t"] = 0
+        state["pending"] = None
+
+    def one_step():
+        t = state["t"]
+        slot = state["issued"] % 2
+        flags[slot] = -1
+        graphs[min(t, len(graphs) - 1)][slot][0].replay()
+        state["issued"] += 1
+        state["t"] = t + 1
+        prev_done = False
+        if state["pending"] is not None:
+            prev_done = bool(wait_flag(flags, state["pending"]))
+        state["pending"] = slot
+        return prev_done
+
+    def run(n):
+        for _ in range(n):
+            if one_step() or state["t"] >= STEP_LIMIT:
+                wait_flag(flags, state["pending"])
+                state["blocks"] += 1
+                start_block()
+
+    start_block()
+    run(args.warmup)
+    torch.cuda.synchronize()
+    b0 = state["blocks"]
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    res = {"mode": "each step replayed from a recorded HIP graph (attention, sampler with a device step counter, "
+                   "self-conditioning)",
+           "steps_per_s": round(args.steps / elapsed, 3), "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+           "steps": args.steps, "warmup": args.warmup, "blocks_in_timed_region": state["blocks"] - b0,
+           "graphs": len(graphs) * 2, "record_seconds": round(t_rec, 4),
+           "workload": "the default step workload (canvas 256 on prefix 4096, vocab 262144, embed 2048, bf16)"}
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -514,6 +590,8 @@ def main():
                     help="instead of the step loop, time every call of the five workloads and write JSON to PATH")
     ap.add_argument("--block-loop", metavar="PATH",
                     help="instead of the step loop, time the block-autoregressive loop on a paged cache; JSON to PATH")
+    ap.add_argument("--graph", metavar="PATH",
+                    help="instead of the eager step loop, replay each step from a recorded HIP graph; JSON to PATH")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -572,6 +650,9 @@ def main():
     # step's selection has run, so neither a copy nor an event (whose record costs about
     # 6 us of GPU time) sits on the stream between steps.
     flags = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+    if args.graph:
+        graph_steps(args.graph, args, dg, torch, attn_call, step_logits, bufs, sc_call, seed, flags)
+        return
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4

@@ -74,7 +74,8 @@ class DgSamplerArgs(ctypes.Structure):
                 ("cand", _vp), ("accept", _vp), ("canvas", _vp), ("prev_argmax", _vp),
                 ("stable_count", _vp), ("num_accepted", _vp), ("converged", _vp), ("mean_entropy", _vp),
                 ("probs", _vp), ("ldq", _c_int64), ("probs_scale", _vp),
-                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("step_counter", _vp)]
 
 
 class DgSelfcondArgs(ctypes.Structure):
@@ -358,7 +359,12 @@ def make_sampler_args(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, 
                       bufs: SamplerBuffers, budget: float, min_accept: int = 1,
                       conf_mode: int = DG_CONF_NEG_ENTROPY, renoise: int = 1, stable_k: int = 3, tau: float = 0.05,
                       step_limit: int = 48, combine: int = DG_CONV_AND, flags: int = 0, num_rows: Optional[int] = None,
-                      probs: Optional[torch.Tensor] = None, probs_scale: Optional[torch.Tensor] = None):
+                      probs: Optional[torch.Tensor] = None, probs_scale: Optional[torch.Tensor] = None,
+                      step_counter: Optional[torch.Tensor] = None):
+    """step_counter: an int32 device tensor [num_reqs] that holds each request's step
+    (read and advanced by the kernels; see include/dg.h), or None."""
+    if step_counter is not None and (step_counter.dtype != torch.int32 or step_counter.numel() < len(reqs)):
+        raise TypeError("step_counter must be an int32 tensor with one entry per request")
     req_arr = (DgSreq * max(1, len(reqs)))()
     for i, (row_start, n, seed, step) in enumerate(reqs):
         req_arr[i] = DgSreq(row_start, n, seed, step, 0)
@@ -377,6 +383,7 @@ def make_sampler_args(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, 
         setattr(a, name, _ptr(getattr(bufs, name)))
     a.probs, a.probs_scale = _ptr(probs), _ptr(probs_scale)
     a.ldq = probs.stride(0) if probs is not None else 0
+    a.step_counter = _ptr(step_counter)
     a._keep = req_arr
     return a
 

@@ -268,6 +268,7 @@ dg_status sampler_plan(const dg_sampler_args* a, SamplerPlan* plan, const char**
   if (!a->accept) return bad(DG_ERR_INVALID_ARG, "accept is NULL");
   if ((a->probs == nullptr) != (a->probs_scale == nullptr)) return bad(DG_ERR_INVALID_ARG, "set both probs and probs_scale, or neither");
   if (a->probs && (!aligned16(a->probs) || !aligned4(a->probs_scale))) return bad(DG_ERR_INVALID_ARG, "probs must be 16-byte aligned");
+  if (a->step_counter && !aligned4(a->step_counter)) return bad(DG_ERR_INVALID_ARG, "step_counter must be 4-byte aligned");
   if (a->probs && (a->ldq < a->vocab || a->ldq % 8)) return bad(DG_ERR_INVALID_ARG, "ldq must be >= vocab and a multiple of 8");
   std::vector<std::pair<int64_t, int64_t>> r;
   for (int i = 0; i < a->num_reqs; ++i) {

@@ -45,7 +45,13 @@ struct ReqTable {
   int32_t num_rows[DG_MAX_REQS];
   int32_t step[DG_MAX_REQS];
   uint64_t seed[DG_MAX_REQS];
+  int32_t* step_dev;  // device step counters [n], or null: the steps above
 };
+
+// Request r's denoise step: the device counter when there is one (a recorded step
+// replays with the step that the previous replay's selection stored), else the
+// call's argument.
+__device__ __forceinline__ int req_step(const ReqTable& t, int r) { return t.step_dev ? t.step_dev[r] : t.step[r]; }
 
 // Elements of a 16-byte load.
 template <bool kBf16> struct Vec;
@@ -332,7 +338,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
   __shared__ int ired[kWaves];
   __shared__ int conv_flag;
   const int tid = threadIdx.x;
-  const int n = reqs.num_rows[r], step = reqs.step[r], row0 = reqs.row_start[r];
+  const int n = reqs.num_rows[r], step = req_step(reqs, r), row0 = reqs.row_start[r];
   const uint64_t seed = reqs.seed[r];
   const int prev_stable = o.stable_count[r];  // loaded early: the bookkeeping at the end needs it
   float c[kPerThread];
@@ -445,6 +451,7 @@ __device__ void select_request(int r, const ReqTable& reqs, const SelectParams& 
     o.converged[r] = conv;
     o.num_accepted[r] = count;
     o.mean_entropy[r] = (float)((double)total * 0x1p-40 / (double)n);
+    if (reqs.step_dev) reqs.step_dev[r] = step + 1;  // every read of it in this call is done
     conv_flag = conv;
   }
   __syncthreads();
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void sampler_finalize(const void* __restr
     if (row >= reqs.row_start[i] && row < reqs.row_start[i] + reqs.num_rows[i]) r = i;
   float u = 0.f;
   if (r >= 0) {
-    const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)reqs.step[r], (uint64_t)(row - reqs.row_start[r]), 0);
+    const uint64_t x0 = philox_word0(reqs.seed[r], (uint64_t)req_step(reqs, r), (uint64_t)(row - reqs.row_start[r]), 0);
     u = (float)(x0 >> 40) * 0x1p-24f;
   }
 
@@ -637,6 +644,7 @@ __global__ __launch_bounds__(kThreads) void sampler_init(ReqTable reqs, int voca
     o.accept[row0 + j] = 0;
   }
   if (tid == 0) {
+    if (reqs.step_dev) reqs.step_dev[r] = 0;
     o.stable_count[r] = 0;
     o.converged[r] = 0;
     o.num_accepted[r] = 0;
@@ -656,6 +664,7 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
     t.step[i] = a->reqs[i].step;
     t.seed[i] = a->reqs[i].seed;
   }
+  t.step_dev = a->step_counter;
   float4* stats = reinterpret_cast<float4*>(a->workspace);
   float* sub = reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + plan.sub_offset);
   RowOut o{a->entropy, a->conf, a->row_max, a->row_sum, a->argmax, a->cand, a->probs_scale, a->accept, a->canvas,

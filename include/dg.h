@@ -241,6 +241,13 @@ typedef struct {
   float* probs_scale;          /* device [M, ceil(V / DG_PROB_BLOCK)] or NULL (set both or neither) */
   void* workspace;             /* device, >= dg_sampler_workspace_size(args) bytes */
   size_t workspace_bytes;
+  int32_t* step_counter;       /* device [num_reqs] int32, or NULL (then reqs[r].step is the step). When set,
+                                  request r's step is read from step_counter[r] when the kernels run and
+                                  reqs[r].step is ignored; DG_INIT_CANVAS draws with reqs[r].step as
+                                  before and sets step_counter[r] = 0; a call that runs the selection
+                                  (no DG_SKIP_SELECT) stores step + 1 there after it. So one recorded
+                                  sequence of calls (a HIP graph of a denoise step) replays as
+                                  successive steps. */
 } dg_sampler_args;
 
 dg_status dg_sampler_step(const dg_sampler_args* args, void* stream);

@@ -296,7 +296,7 @@ def _sampler(**over):
     dict(flags=4 | 8), dict(flags=4 | 2), dict(flags=8 | 2),
     dict(logits=None), dict(entropy=None), dict(accept=None), dict(canvas=FAKE + 2), dict(dtype=3),
     dict(probs=FAKE, ldq=4096), dict(probs_scale=FAKE), dict(probs=FAKE, probs_scale=FAKE, ldq=4000),
-    dict(probs=FAKE + 8, probs_scale=FAKE, ldq=4096),
+    dict(probs=FAKE + 8, probs_scale=FAKE, ldq=4096), dict(step_counter=FAKE + 2),
 ])
 def test_sampler_validation(change):
     a = _sampler(**change)
