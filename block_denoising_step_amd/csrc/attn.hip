@@ -226,6 +226,78 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   }
 }
 
+// FP8 tiles are staged in two halves so that the next tile's loads are in flight while
+// the current one is computed: fp8_load issues a tile's global loads (8 codes per load)
+// into registers, fp8_store widens them and writes the same LDS layout as stage_tile.
+template <int D>
+struct Fp8Regs {
+  static constexpr int kK = kKT * (D / 8) / kThreads;  // K loads per thread (8 codes each)
+  static constexpr int kVBlocks = (kKT / 8) * (D / 8);  // V blocks of 8 keys x 8 dims (<= kThreads)
+  uint2 k[kK];
+  uint2 v[8];
+};
+
+template <int D>
+__device__ __forceinline__ void fp8_load(Fp8Regs<D>& r, const char* kg, const char* vg, int64_t row_stride,
+                                         int nvalid) {
+  constexpr int cpr = D / 8;  // 8-code chunks per key row
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Fp8Regs<D>::kK; ++i) {
+    const int q = i * kThreads + tid;
+    const int key = q / cpr, col = q % cpr;
+    r.k[i] = key < nvalid ? *reinterpret_cast<const uint2*>(kg + (int64_t)key * row_stride + col * 8)
+                          : make_uint2(0, 0);
+  }
+  if (tid < Fp8Regs<D>::kVBlocks) {
+    constexpr int dgroups = D / 8;
+    const int dgp = tid % dgroups, kb = tid / dgroups;
+    const int a16 = kb >> 1, c = kb & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = 16 * a16 + 4 * c + (j & 3) + ((j >> 2) << 3);
+      r.v[j] = key < nvalid ? *reinterpret_cast<const uint2*>(vg + (int64_t)key * row_stride + dgp * 8)
+                            : make_uint2(0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_store(const Fp8Regs<D>& r, char* lk, char* lv) {
+  using L = Lds<true, D>;
+  constexpr int cpr = D / 8;
+  const int tid = threadIdx.x;
+  auto widen = [](uint2 w) {
+    return make_uint4(e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
+                      e4m3x2_to_bf16x2<true>(w.y));
+  };
+#pragma unroll
+  for (int i = 0; i < Fp8Regs<D>::kK; ++i) {
+    const int q = i * kThreads + tid;
+    const int key = q / cpr, col = q % cpr;
+    *reinterpret_cast<uint4*>(lk + key * L::k_pitch + col * 16) = widen(r.k[i]);
+  }
+  if (tid < Fp8Regs<D>::kVBlocks) {
+    constexpr int dgroups = D / 8;
+    const int dgp = tid % dgroups, kb = tid / dgroups;
+    const int a16 = kb >> 1, c = kb & 1;
+    uint4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = widen(r.v[j]);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int w = dd >> 1;
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      uint4 o;
+      o.x = __builtin_amdgcn_perm((&x[1].x)[w], (&x[0].x)[w], sel);
+      o.y = __builtin_amdgcn_perm((&x[3].x)[w], (&x[2].x)[w], sel);
+      o.z = __builtin_amdgcn_perm((&x[5].x)[w], (&x[4].x)[w], sel);
+      o.w = __builtin_amdgcn_perm((&x[7].x)[w], (&x[6].x)[w], sel);
+      *reinterpret_cast<uint4*>(lv + (dgp * 8 + dd) * L::v_pitch + (16 * a16 + 8 * c) * 2) = o;
+    }
+  }
+}
+
 template <bool kBf16, int D, bool kPaged, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   using OP = Op<kBf16>;
@@ -287,12 +359,26 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   const char* kg = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * kv_esz;
   const char* vg = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * kv_esz;
 
+  Fp8Regs<D> pre;  // FP8: the next tile's codes, loaded during the current tile's compute
+  if constexpr (kFp8) {
+    const int64_t r0 = key_row<kPaged>(a, sp, t_begin * kKT) * row_stride;
+    fp8_load<D>(pre, kg + r0, vg + r0, row_stride, nkeys - t_begin * kKT);
+  }
   for (int kt = t_begin; kt < t_end; ++kt) {
     const int k0 = kt * kKT;
-    const int64_t r0 = key_row<kPaged>(a, sp, k0) * row_stride;  // the tile's 64 rows are consecutive
     __syncthreads();  // previous tile fully consumed
-    stage_tile<kBf16, D, kFp8>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
-    __syncthreads();
+    if constexpr (kFp8) {
+      fp8_store<D>(pre, lk, lv);
+      __syncthreads();
+      if (kt + 1 < t_end) {
+        const int64_t r1 = key_row<kPaged>(a, sp, k0 + kKT) * row_stride;
+        fp8_load<D>(pre, kg + r1, vg + r1, row_stride, nkeys - k0 - kKT);
+      }
+    } else {
+      const int64_t r0 = key_row<kPaged>(a, sp, k0) * row_stride;  // the tile's 64 rows are consecutive
+      stage_tile<kBf16, D>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
+      __syncthreads();
+    }
 
     // S^T blocks: sblk[kb][i] = score of key k0 + 32kb + 8(i/4) + 4hh + i%4 for this lane's row
     f32x16_t sblk[2];
