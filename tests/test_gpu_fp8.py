@@ -30,10 +30,17 @@ def codes_dev(c: np.ndarray, fp8_dtype: bool = True) -> torch.Tensor:
     return t.view(torch.float8_e4m3fn) if fp8_dtype else t
 
 
+_CODES = {}
+
+
 def _fp8_kv(seed, shape, scale):
     """Seeded normal K or V rows as E4M3 codes at `scale` (values up to ~4.5 sigma
-    land near the top of the format at scale 1/64)."""
-    return quantize(normal(seed, shape), scale)
+    land near the top of the format at scale 1/64); memoised, as the large ones take
+    seconds to quantize."""
+    key = (seed, tuple(shape), scale)
+    if key not in _CODES:
+        _CODES[key] = quantize(normal(seed, shape), scale)
+    return _CODES[key]
 
 
 def test_every_code_widens_exactly():
@@ -111,6 +118,34 @@ def test_fp8_attention_against_oracle(case):
         got, glse, want, wlse = got[rows], glse[rows], want[rows], wlse[rows]
     err = max_rel_rows(got, want)
     lerr = float(np.abs(glse - wlse).max())
+    say(f"  max-rel {err:.3e}  lse abs {lerr:.3e}")
+    assert err <= 2e-2 and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("window", [-1, 512])
+def test_fp8_mixed_four_request_batch_sampled(window):
+    """The four-request mixed batch at its full size (a 2048-token causal prefill, a causal
+    commit after 8192 tokens, denoise canvases after 1024 and 16384), over an FP8 cache,
+    in the launch configuration the per-call timings use; sampled rows of every request."""
+    spec = [(0, 2048, CAUSAL), (8192, 256, CAUSAL), (1024, 256, BIDIR), (16384, 256, BIDIR)]
+    hq, hkv, D, sc = 16, 8, 256, 1.0 / 64
+    seqs = pack_seqs(spec)
+    T = sum(n for _, n, _ in spec)
+    S = sum(p + n for p, n, _ in spec)
+    q = normal(461, (T, hq, D), bf16=True)
+    kc, vc = _fp8_kv(462, (S, hkv, D), sc), _fp8_kv(463, (S, hkv, D), sc)
+    out = torch.empty(T, hq, D, device=DEV, dtype=torch.bfloat16)
+    lse = torch.empty(T, hq, device=DEV)
+    say(f"[fp8 4-request batch] W={window}")
+    dg.dg_attn_mixed(dev(q, True), codes_dev(kc), codes_dev(vc), out, seqs, window, hq, hkv, lse=lse, k_scale=sc,
+                     v_scale=sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(464)
+    rows = np.concatenate([s.q_start + np.concatenate([[0, s.num_q - 1], rng.choice(s.num_q, 6, replace=False)])
+                           for s in seqs])
+    want, wlse = attn_mixed_fp8(seqs, window, q, kc, vc, sc, sc, hq, hkv, rows=rows)
+    err = max_rel_rows(host(out)[rows], want[rows])
+    lerr = float(np.abs(host(lse)[rows] - wlse[rows]).max())
     say(f"  max-rel {err:.3e}  lse abs {lerr:.3e}")
     assert err <= 2e-2 and lerr <= 1e-3
 
