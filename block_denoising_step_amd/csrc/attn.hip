@@ -19,8 +19,9 @@
 // FP8 K/V (OCP E4M3 codes with per-tensor scales, the FP8 configuration of [P1]
 // section "성능 및 양자화"): attn_fwd's <kFp8> instance loads 8 codes where it loaded
 // 8 bf16 and widens them to bf16 while staging the tile, exactly (every E4M3 value
-// is a bf16 value), so the LDS layout and the inner loop are the bf16 ones; k_scale
-// is folded into the score scale and v_scale into the output normalisation.
+// is a bf16 value), so the LDS layout and the inner loop are the bf16 ones; the next
+// tile's codes are loaded while the current tile is computed. k_scale is folded into
+// the score scale and v_scale into the output normalisation.
 // A request whose keys were split into several chunks writes partials: O of the
 // chunk normalised by its own sum, in the input dtype, plus the chunk's (max, sum)
 // in fp32; attn_merge combines them in chunk order.
@@ -147,25 +148,11 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
 }
 
-// The 16 LDS bytes of chunk c of a staged row: 16 source bytes, or 8 E4M3 codes
-// widened to 8 bf16.
-template <bool kFp8>
-__device__ __forceinline__ uint4 load_chunk(const char* row, int c) {
-  if constexpr (!kFp8) {
-    return *reinterpret_cast<const uint4*>(row + c * 16);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(row + c * 8);
-    return make_uint4(e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x), e4m3x2_to_bf16x2<false>(w.y),
-                      e4m3x2_to_bf16x2<true>(w.y));
-  }
-}
-
 // Stage one 64-key tile of K (row-major) and V (transposed) into LDS. Key rows at
-// or past `nvalid` (request-local) are zero. kFp8: the source rows hold E4M3 codes.
-template <bool kBf16, int D, bool kFp8 = false>
+// or past `nvalid` (request-local) are zero.
+template <bool kBf16, int D>
 __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, const char* vg, int64_t row_stride,
                                            int nvalid) {
-  static_assert(kBf16 || !kFp8, "FP8 K/V are widened to bf16");
   using L = Lds<kBf16, D>;
   constexpr int esz = L::esz;
   constexpr int cpr = D * esz / 16;  // 16-byte chunks per key row
@@ -175,7 +162,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
   for (int q = tid; q < kKT * cpr; q += kThreads) {
     const int key = q / cpr, col = q % cpr;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < nvalid) val = load_chunk<kFp8>(kg + (int64_t)key * row_stride, col);
+    if (key < nvalid) val = *reinterpret_cast<const uint4*>(kg + (int64_t)key * row_stride + col * 16);
     *reinterpret_cast<uint4*>(lk + key * L::k_pitch + col * 16) = val;
   }
   // V^T: within each 16-key group, key w sits at position w with bits 2 and 3 swapped
@@ -190,7 +177,7 @@ __device__ __forceinline__ void stage_tile(char* lk, char* lv, const char* kg, c
       for (int j = 0; j < 8; ++j) {
         const int key = 16 * a16 + 4 * c + (j & 3) + ((j >> 2) << 3);
         r[j] = make_uint4(0, 0, 0, 0);
-        if (key < nvalid) r[j] = load_chunk<kFp8>(vg + (int64_t)key * row_stride, dgp);
+        if (key < nvalid) r[j] = *reinterpret_cast<const uint4*>(vg + (int64_t)key * row_stride + dgp * 16);
       }
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
