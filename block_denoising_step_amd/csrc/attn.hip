@@ -293,8 +293,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   constexpr int kv_esz = kFp8 ? 1 : esz;  // bytes per K/V element in HBM
   constexpr int KS = D / 16;  // k16 steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide output blocks
-  __shared__ __attribute__((aligned(16))) char lk[L::k_bytes];
-  __shared__ __attribute__((aligned(16))) char lv[L::v_bytes];
+  // FP8: two tile buffers (the next tile is stored while no wave reads its buffer)
+  constexpr int kBufs = kFp8 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char lk_s[kBufs][L::k_bytes];
+  __shared__ __attribute__((aligned(16))) char lv_s[kBufs][L::v_bytes];
 
   const int w = a.work_offset + blockIdx.x;
   const int s = find_seq(a, w, false);
@@ -346,24 +348,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
   const char* kg = reinterpret_cast<const char*>(a.k) + (int64_t)g * D * kv_esz;
   const char* vg = reinterpret_cast<const char*>(a.v) + (int64_t)g * D * kv_esz;
 
-  Fp8Regs<D> pre;  // FP8: the next tile's codes, loaded during the current tile's compute
+  // FP8: tile t_begin + i sits in buffer i % 2. Tile kt + 1 is stored into the other
+  // buffer after tile kt's compute (that buffer's last reads, of tile kt - 1, ended at
+  // the previous barrier), one barrier publishes it, and the loads of tile kt + 2 are
+  // issued right after that barrier, so they are in flight during tile kt + 1.
+  Fp8Regs<D> pre;
+  auto fp8_fetch = [&](int kt) {
+    const int64_t r = key_row<kPaged>(a, sp, kt * kKT) * row_stride;
+    fp8_load<D>(pre, kg + r, vg + r, row_stride, nkeys - kt * kKT);
+  };
   if constexpr (kFp8) {
-    const int64_t r0 = key_row<kPaged>(a, sp, t_begin * kKT) * row_stride;
-    fp8_load<D>(pre, kg + r0, vg + r0, row_stride, nkeys - t_begin * kKT);
+    fp8_fetch(t_begin);
+    fp8_store<D>(pre, lk_s[0], lv_s[0]);
+    __syncthreads();
+    if (t_begin + 1 < t_end) fp8_fetch(t_begin + 1);
   }
   for (int kt = t_begin; kt < t_end; ++kt) {
     const int k0 = kt * kKT;
-    __syncthreads();  // previous tile fully consumed
-    if constexpr (kFp8) {
-      fp8_store<D>(pre, lk, lv);
-      __syncthreads();
-      if (kt + 1 < t_end) {
-        const int64_t r1 = key_row<kPaged>(a, sp, k0 + kKT) * row_stride;
-        fp8_load<D>(pre, kg + r1, vg + r1, row_stride, nkeys - k0 - kKT);
-      }
-    } else {
+    const char* lk = lk_s[kFp8 ? (kt - t_begin) & 1 : 0];
+    const char* lv = lv_s[kFp8 ? (kt - t_begin) & 1 : 0];
+    if constexpr (!kFp8) {
+      __syncthreads();  // previous tile fully consumed
       const int64_t r0 = key_row<kPaged>(a, sp, k0) * row_stride;  // the tile's 64 rows are consecutive
-      stage_tile<kBf16, D>(lk, lv, kg + r0, vg + r0, row_stride, nkeys - k0);
+      stage_tile<kBf16, D>(lk_s[0], lv_s[0], kg + r0, vg + r0, row_stride, nkeys - k0);
       __syncthreads();
     }
 
@@ -425,6 +432,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
         const typename OP::Frag vf = OP::lds(lv + (32 * b + l32) * L::v_pitch + (16 * u + 8 * hh) * esz);
         OP::mma(o[b], vf, pf);
       }
+    }
+    if constexpr (kFp8) {
+      if (kt + 1 < t_end) fp8_store<D>(pre, lk_s[(kt + 1 - t_begin) & 1], lv_s[(kt + 1 - t_begin) & 1]);
+      __syncthreads();
+      if (kt + 2 < t_end) fp8_fetch(kt + 2);
     }
   }
 

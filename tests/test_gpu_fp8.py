@@ -93,6 +93,11 @@ CASES = [
     ("d256 canvas 256 prefix 4096", [(4096, 256, BIDIR)], -1, 16, 8, 256, 0, 1 / 64, 1 / 64),
     ("d256 mixed W=512 forced chunks", [(0, 300, CAUSAL), (1000, 256, BIDIR), (5000, 64, CAUSAL)], 512, 16, 8,
      256, 256, 0.013, 0.021),
+    # degenerate requests: no queries, a single token with no cache, W = 0 (itself only)
+    ("d128 edges: empty, one-token, W=0", [(50, 0, BIDIR), (0, 1, CAUSAL), (63, 1, BIDIR), (70, 30, CAUSAL)], 0,
+     8, 8, 128, 0, 0.5, 0.25),
+    ("d64 edges: empty, one-token, global", [(50, 0, BIDIR), (0, 1, BIDIR), (0, 1, CAUSAL), (129, 65, BIDIR)], -1,
+     2, 1, 64, 64, 0.07, 0.09),
 ]
 
 
