@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdg.so")
 
 DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_WORKSPACE, DG_ERR_HIP = 0, 1, 2, 3, 4
+ABI_VERSION = 3  # DG_ABI_VERSION of the include/dg.h these structs mirror
 DG_F32, DG_BF16 = 0, 1
 DG_CAUSAL, DG_BIDIR = 0, 1
 DG_CONF_NEG_ENTROPY, DG_CONF_MAX_PROB = 0, 1
@@ -137,6 +138,10 @@ def load() -> ctypes.CDLL:
     lib.dg_last_error.restype = ctypes.c_char_p
     lib.dg_abi_version.argtypes = []
     lib.dg_abi_version.restype = ctypes.c_int
+    if lib.dg_abi_version() != ABI_VERSION:
+        # the structs above would not match the library's: refuse rather than pass garbage
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.dg_abi_version()}, this binding needs {ABI_VERSION}; "
+                           "rebuild it")
     _lib = lib
     return lib
 

@@ -59,6 +59,20 @@ class _T:
         return s
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libdg.so every entry point raises."""
+    monkeypatch.setattr(dg, "_lib", None)
+    monkeypatch.setattr(dg, "LIB_PATH", str(tmp_path / "libdg.so"))
+    with pytest.raises(RuntimeError):
+        dg.load()
+    with pytest.raises(RuntimeError):
+        dg.attn_workspace_size(dg.DgAttnArgs())
+
+
+def test_binding_matches_the_library_abi():
+    assert dg.ABI_VERSION == dg.load().dg_abi_version()
+
+
 def _attn(**over):
     seqs = over.pop("seqs", pack_seqs([(64, 32, BIDIR)]))
     q = over.pop("q", _T((32, 4, 64)))
