@@ -41,17 +41,19 @@ class _Step:
     """The three calls of a step on their own buffers; the sampler optionally reads a
     device step counter."""
 
-    def __init__(self, q, k, v, E, logits, counter=None):
+    def __init__(self, q, k, v, E, logits, counter=None, budget=BUDGET):
+        n, hq, hkv = q.shape[0], q.shape[1], k.shape[1]
+        prefix, vocab = k.shape[0] - n, E.shape[0]
         self.attn_out = torch.empty_like(q)
-        self.bufs = dg.SamplerBuffers(N, 1, DEV, vocab=V, probs_dtype=torch.float32)
-        self.sc = torch.empty(N, EMB, device=DEV)
-        self.attn = dg.prepare_attn(q, k, v, self.attn_out, [Seq(0, N, 0, P, BIDIR)], -1, HQ, HKV)
+        self.bufs = dg.SamplerBuffers(n, 1, DEV, vocab=vocab, probs_dtype=logits[0].dtype)
+        self.sc = torch.empty(n, E.shape[1], device=DEV, dtype=E.dtype)
+        self.attn = dg.prepare_attn(q, k, v, self.attn_out, [Seq(0, n, 0, prefix, BIDIR)], -1, hq, hkv)
         kw = dict(stable_k=STABLE_K, tau=TAU, step_limit=LIMIT, combine=dg.DG_CONV_OR)
         if counter is not None:
             kw["step_counter"] = counter
-        self.samp = [dg.prepare_sampler(l, [(0, N, SEED, 0)], V, self.bufs, BUDGET, **kw) for l in logits]
-        self.init = dg.prepare_sampler(None, [(0, N, SEED, 0)], V, self.bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
-                                       num_rows=N, **({"step_counter": counter} if counter is not None else {}))
+        self.samp = [dg.prepare_sampler(l, [(0, n, SEED, 0)], vocab, self.bufs, budget, **kw) for l in logits]
+        self.init = dg.prepare_sampler(None, [(0, n, SEED, 0)], vocab, self.bufs, budget, flags=dg.DG_INIT_CANVAS,
+                                       num_rows=n, **({"step_counter": counter} if counter is not None else {}))
         self.selfcond = dg.prepare_selfcond(self.bufs.probs, E, self.sc, p_scale=self.bufs.probs_scale)
 
     def enqueue(self, t, host_step=None):
@@ -73,7 +75,57 @@ class _Step:
 def _bits_equal(a, b):
     if a.dtype == torch.float32:
         return torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
     return torch.equal(a, b)
+
+
+def _replay_against_eager(q, k, v, E, logits, steps, budget=BUDGET):
+    """Eager host-stepped calls, then two recorded graphs replayed alternately with the
+    step read from a device counter; every replay is compared with the eager step."""
+    eager = _Step(q, k, v, E, logits, budget=budget)
+    eager.init()
+    want = []
+    for t in range(steps):
+        eager.enqueue(t, host_step=t)
+        torch.cuda.synchronize()
+        want.append(eager.snapshot())
+    counter = torch.full((1,), 777, dtype=torch.int32, device=DEV)
+    rec = _Step(q, k, v, E, logits, counter, budget=budget)
+    rec.init()
+    graphs = []
+    side = torch.cuda.Stream()
+    for i in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            rec.enqueue(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        graphs[t % 2].replay()
+        torch.cuda.synchronize()
+        got = rec.snapshot()
+        for name, w in want[t].items():
+            assert _bits_equal(got[name], w), (t, name)
+        assert int(counter.item()) == t + 1
+    return want
+
+
+def test_step_shapes_replay_against_eager():
+    """The step's shapes and dtypes: canvas 256 on a 4096-token prefix (16 q / 8 kv heads
+    x 256, bf16), bf16 logits [256 x 262144], bf16 embedding table [262144 x 2048]."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8201)
+    bf = torch.bfloat16
+    q = torch.randn(256, 16, 256, device=DEV, generator=g).to(bf)
+    k = torch.randn(4352, 8, 256, device=DEV, generator=g).to(bf)
+    v = torch.randn(4352, 8, 256, device=DEV, generator=g).to(bf)
+    E = (torch.randn(262144, 2048, device=DEV, generator=g) * 0.02).to(bf)
+    sig = torch.exp(torch.empty(256, 1, device=DEV).uniform_(-2.3, 2.3, generator=g))
+    logits = [(torch.randn(256, 262144, device=DEV, generator=g) * sig).to(bf) for _ in range(2)]
+    want = _replay_against_eager(q, k, v, E, logits, steps=6, budget=128.0)
+    say(f"[graph] step shapes: 6 replays equal the eager steps; accepted at the last step "
+        f"{int(want[-1]['num_accepted'][0])}")
 
 
 def test_recorded_step_replays_as_successive_steps():
