@@ -82,4 +82,10 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t seed, uint64_t c0, uin
   return x0;
 }
 
+// tanh-approximated GELU: x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * x * (1.f + tanhf(k * fmaf(0.044715f * x, x * x, x)));
+}
+
 }  // namespace dg

@@ -109,7 +109,18 @@ dg_status inject_plan(const dg_inject_args* a, InjectPlan* plan, const char** ms
 
 int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream);
 int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stream);
-int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream);
+// Epilogue of the split-K reduce, for the injection's two bf16 products (plain: the
+// product itself).
+enum { kReducePlain = 0, kReduceGeglu = 1, kReduceAddRows = 2 };
+struct ReduceEpi {
+  int mode;
+  int half_tiles;          // geglu: column tiles of the gate half (hidden / tile_n); out is [M][hidden]
+  const void* embed;       // add rows: [vocab][d] bf16
+  const int32_t* tokens;   // add rows: [M], clamped to [0, vocab)
+  int vocab;
+};
+int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream,
+                    const ReduceEpi* epi = nullptr);
 int launch_kv_write(const dg_kv_write_args* a, const KvWritePlan& plan, void* stream);
 int launch_inject(const dg_inject_args* a, InjectPlan& plan, void* stream);
 const char* hip_error_name(int err);

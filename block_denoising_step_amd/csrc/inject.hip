@@ -8,6 +8,8 @@
 //   h   = gelu(gu[:, :h]) * gu[:, h:]   inject_geglu (elementwise, 8 values per thread)
 //   out = h . w_down               MFMA GEMM ([M, h] x [h, d])
 //   out += embed[tokens]           inject_add_rows (gather and add, 8 values per thread)
+// For bf16 products split over K, the GeGLU and the gather run in the split-K reduce's
+// epilogue instead (no gu tensor, two launches fewer).
 //
 // The two contractions are dense GEMMs on the matrix cores; the two elementwise
 // passes touch M x (3h + 2d) values, a few MB at the canvas sizes.
@@ -49,12 +51,6 @@ __device__ __forceinline__ void store8(void* base, int64_t i, const float (&x)[8
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
   }
-}
-
-// tanh-approximated GELU: x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k = 0.7978845608028654f;  // sqrt(2 / pi)
-  return 0.5f * x * (1.f + tanhf(k * fmaf(0.044715f * x, x * x, x)));
 }
 
 template <bool kBf16>
@@ -104,14 +100,32 @@ int launch_inject(const dg_inject_args* a, InjectPlan& plan, void* stream) {
   plan.gemm2.workspace = gemm_ws;
   plan.gemm2.workspace_bytes = plan.plan2.bytes;
   const bool bf = a->dtype == DG_BF16;
-  int e = launch_selfcond(&plan.gemm1, plan.plan1, stream);
-  if (e) return e;
-  const int64_t n1 = (int64_t)a->M * (a->hidden / 8);
-  const dim3 g1((unsigned)((n1 + kThreads - 1) / kThreads));
-  if (bf) hipLaunchKernelGGL(inject_geglu<true>, g1, dim3(kThreads), 0, s, gu, h, a->M, a->hidden);
-  else hipLaunchKernelGGL(inject_geglu<false>, g1, dim3(kThreads), 0, s, gu, h, a->M, a->hidden);
-  e = (int)hipGetLastError();
-  if (e) return e;
+  // bf16 products split over K: the GeGLU and the embedding gather run in the reduce's
+  // epilogue (the gate half must be whole column tiles of the product)
+  const bool fuse1 = bf && plan.plan1.splits > 1 && a->hidden % plan.plan1.tile_n == 0;
+  const bool fuse2 = bf && plan.plan2.splits > 1;
+  int e;
+  if (fuse1) {
+    dg_selfcond_args g1 = plan.gemm1;
+    g1.out = h;
+    g1.ldo = a->hidden;
+    const ReduceEpi epi{kReduceGeglu, a->hidden / plan.plan1.tile_n, nullptr, nullptr, 0};
+    e = launch_selfcond(&g1, plan.plan1, stream, &epi);
+    if (e) return e;
+  } else {
+    e = launch_selfcond(&plan.gemm1, plan.plan1, stream);
+    if (e) return e;
+    const int64_t n1 = (int64_t)a->M * (a->hidden / 8);
+    const dim3 g1((unsigned)((n1 + kThreads - 1) / kThreads));
+    if (bf) hipLaunchKernelGGL(inject_geglu<true>, g1, dim3(kThreads), 0, s, gu, h, a->M, a->hidden);
+    else hipLaunchKernelGGL(inject_geglu<false>, g1, dim3(kThreads), 0, s, gu, h, a->M, a->hidden);
+    e = (int)hipGetLastError();
+    if (e) return e;
+  }
+  if (fuse2) {
+    const ReduceEpi epi{kReduceAddRows, 0, a->embed, a->tokens, a->vocab};
+    return launch_selfcond(&plan.gemm2, plan.plan2, stream, &epi);
+  }
   e = launch_selfcond(&plan.gemm2, plan.plan2, stream);
   if (e) return e;
   const int64_t n2 = (int64_t)a->M * (a->d / 8);

@@ -671,9 +671,86 @@ __global__ __launch_bounds__(256) void selfcond_reduce(const void* __restrict__ 
   }
 }
 
+// The reduce with an epilogue, for the self-conditioning injection's two bf16 products
+// (bf16 partials). Same slice order and tile decode as selfcond_reduce.
+//   kReduceGeglu:   the product is [gate | up], N = 2 hidden with hidden a multiple of the
+//                   tile width; a thread sums a gate element and its partner hidden
+//                   columns on (same rows, `half_tiles` column tiles on), rounds both to
+//                   bf16, and stores h = bf16(gelu(g) * u) into out [M][hidden];
+//   kReduceAddRows: out[r][c] = bf16(sum + embed[token r][c]), one rounding.
+template <int kMode>
+__global__ __launch_bounds__(256) void selfcond_reduce_epi(const uint2* __restrict__ part, int splits, int m_tiles,
+                                                           int n_tiles, int tile_m, int tile_n, int M, int d,
+                                                           uint16_t* __restrict__ out, int64_t ldo, int half_tiles,
+                                                           const uint16_t* __restrict__ embed,
+                                                           const int32_t* __restrict__ tokens, int vocab) {
+  constexpr int kTile4 = 65536 / 4;
+  const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t i = j;
+  if constexpr (kMode == kReduceGeglu) {
+    // j walks the gate tiles only: (mt, nt < half_tiles, q)
+    const int64_t per_row_tiles = (int64_t)half_tiles * kTile4;
+    if (j >= (int64_t)m_tiles * per_row_tiles) return;
+    i = (j / per_row_tiles) * n_tiles * kTile4 + j % per_row_tiles;
+  } else {
+    if (j >= per_split) return;
+  }
+  auto sum = [&](int64_t idx) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    for (; k + 8 <= splits; k += 8) {
+      uint2 u[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) u[t] = part[(int64_t)(k + t) * per_split + idx];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        s.x += bf16lo(u[t].x);
+        s.y += bf16hi(u[t].x);
+        s.z += bf16lo(u[t].y);
+        s.w += bf16hi(u[t].y);
+      }
+    }
+    for (; k < splits; ++k) {
+      const uint2 u = part[(int64_t)k * per_split + idx];
+      s.x += bf16lo(u.x);
+      s.y += bf16hi(u.x);
+      s.z += bf16lo(u.y);
+      s.w += bf16hi(u.y);
+    }
+    return s;
+  };
+  const float4 s = sum(i);
+  float4 s2 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (kMode == kReduceGeglu) s2 = sum(i + (int64_t)half_tiles * kTile4);
+  const int q = (int)(i % kTile4);
+  const int64_t tile = i / kTile4;
+  const int mt = (int)(tile / n_tiles), nt = (int)(tile % n_tiles);
+  const int chs = tile_n / 128;
+  const int lane = q & 63, e4 = (q >> 6) & 3, jj = (q >> 8) & 3, ch = (q >> 10) % chs, rb = (q >> 10) / chs;
+  const int r = mt * tile_m + 32 * rb + 8 * e4 + 4 * (lane >> 5);
+  const int c = nt * tile_n + 128 * ch + 32 * jj + (lane & 31);
+  if (c >= d) return;
+  const float v[4] = {s.x, s.y, s.z, s.w};
+  const float w[4] = {s2.x, s2.y, s2.z, s2.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (r + e >= M) break;
+    float x;
+    if constexpr (kMode == kReduceGeglu) {
+      const float g = bf16lo(pack_bf16(v[e], 0.f)), u = bf16lo(pack_bf16(w[e], 0.f));
+      x = gelu_tanh(g) * u;
+    } else {
+      const int tok = min(max(tokens[r + e], 0), vocab - 1);
+      x = v[e] + bf16lo((uint32_t)embed[(int64_t)tok * d + c]);
+    }
+    out[(int64_t)(r + e) * ldo + c] = (uint16_t)(pack_bf16(x, 0.f) & 0xFFFFu);
+  }
+}
+
 }  // namespace
 
-int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream) {
+int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* stream, const ReduceEpi* epi) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(a->workspace);
   GemmArgs g;
@@ -716,7 +793,22 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
     if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<false, true>), grid, dim3(kThreads), 0, s, g);
     else hipLaunchKernelGGL((selfcond_gemm_reg<false, false>), grid, dim3(kThreads), 0, s, g);
   }
-  if (plan.splits > 1) {
+  if (plan.splits > 1 && epi && epi->mode != kReducePlain) {
+    const int64_t n4 = (int64_t)plan.m_tiles * (epi->mode == kReduceGeglu ? epi->half_tiles : plan.n_tiles) *
+                       (plan.tile_m * plan.tile_n / 4);
+    const dim3 rg((unsigned)((n4 + 255) / 256));
+    const uint2* part = reinterpret_cast<const uint2*>(g.part);
+    uint16_t* o = reinterpret_cast<uint16_t*>(a->out);
+    const uint16_t* emb = reinterpret_cast<const uint16_t*>(epi->embed);
+    if (epi->mode == kReduceGeglu)
+      hipLaunchKernelGGL(selfcond_reduce_epi<kReduceGeglu>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles,
+                         plan.n_tiles, plan.tile_m, plan.tile_n, a->M, a->d, o, a->ldo, epi->half_tiles, emb,
+                         epi->tokens, epi->vocab);
+    else
+      hipLaunchKernelGGL(selfcond_reduce_epi<kReduceAddRows>, rg, dim3(256), 0, s, part, plan.splits, plan.m_tiles,
+                         plan.n_tiles, plan.tile_m, plan.tile_n, a->M, a->d, o, a->ldo, epi->half_tiles, emb,
+                         epi->tokens, epi->vocab);
+  } else if (plan.splits > 1) {
     const int64_t n4 = (int64_t)plan.m_tiles * plan.n_tiles * (plan.tile_m * plan.tile_n / 4);
     const dim3 rg((unsigned)((n4 + 255) / 256));
     const void* part = g.part;
