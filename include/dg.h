@@ -133,7 +133,8 @@ typedef struct {
   int32_t block_size;           /* 0: contiguous K/V; else a power of two >= 64, dividing total_kv (paged) */
   const int32_t* block_table;   /* device [block_table_len] int32 when block_size > 0, else ignored */
   int64_t block_table_len;      /* every request needs kv_start + ceil((prefix_len + num_q) / block_size) <= this */
-  int32_t kv_fp8;               /* 0: k and v are in dtype; 1: k and v hold E4M3 codes (dtype must be DG_BF16) */
+  int32_t kv_fp8;               /* 0: k and v are in dtype; 1: k and v hold E4M3 codes, dtype must be DG_BF16
+                                   (else DG_ERR_UNSUPPORTED); other values and bad scales: DG_ERR_INVALID_ARG */
   float k_scale;                /* kv_fp8: finite, > 0; ignored otherwise */
   float v_scale;                /* kv_fp8: finite, > 0; ignored otherwise */
 } dg_attn_args;
@@ -241,7 +242,8 @@ typedef struct {
   float* probs_scale;          /* device [M, ceil(V / DG_PROB_BLOCK)] or NULL (set both or neither) */
   void* workspace;             /* device, >= dg_sampler_workspace_size(args) bytes */
   size_t workspace_bytes;
-  int32_t* step_counter;       /* device [num_reqs] int32, or NULL (then reqs[r].step is the step). When set,
+  int32_t* step_counter;       /* device [num_reqs] int32 (4-byte aligned, else DG_ERR_INVALID_ARG), caller-owned,
+                                  or NULL (then reqs[r].step is the step). When set,
                                   request r's step is read from step_counter[r] when the kernels run and
                                   reqs[r].step is ignored; DG_INIT_CANVAS draws with reqs[r].step as
                                   before and sets step_counter[r] = 0; a call that runs the selection
@@ -324,7 +326,8 @@ typedef struct {
   const void* v_new;            /* device [total_new, Hkv, D] */
   void* k_pool;                 /* device [pool_rows, Hkv, D], dtype, or E4M3 codes when pool_fp8 */
   void* v_pool;                 /* device [pool_rows, Hkv, D], dtype, or E4M3 codes when pool_fp8 */
-  int32_t pool_fp8;             /* 0: pools in dtype (a copy); 1: E4M3 pools, values quantized */
+  int32_t pool_fp8;             /* 0: pools in dtype (a copy); 1: E4M3 pools, values quantized; other values
+                                   and bad scales: DG_ERR_INVALID_ARG */
   float k_scale;                /* pool_fp8: finite, > 0; ignored otherwise */
   float v_scale;                /* pool_fp8: finite, > 0; ignored otherwise */
 } dg_kv_write_args;
