@@ -36,7 +36,10 @@ def _case(M, d, hidden, V, bf16, seed, E=None):
 
 
 @pytest.mark.parametrize("M,d,hidden,V,bf16", [(77, 256, 384, 1000, False), (300, 512, 256, 5000, True),
-                                               (1, 128, 128, 7, True), (256, 1024, 640, 4096, False)])
+                                               (1, 128, 128, 7, True), (256, 1024, 640, 4096, False),
+                                               # both products split over K: the reduce's GeGLU and
+                                               # gather epilogues, on a ragged row count
+                                               (300, 1024, 1024, 5000, True)])
 def test_shapes(M, d, hidden, V, bf16):
     err = _case(M, d, hidden, V, bf16, seed=M + d + hidden)
     say(f"[inject] M={M} d={d} hidden={hidden} V={V} bf16={bf16}: max-rel {err:.3e}")
