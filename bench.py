@@ -55,10 +55,24 @@ def algorithmic():
                 sc_flop=sc_flop, sc_bytes=sc_bytes)
 
 
-def cpu_baseline(q, k, v, logits_by_step, E, seqs, seed, min_seconds=10.0, max_steps=6):
+def _blas():
+    """The BLAS numpy runs on, and its thread count (threadpoolctl's report)."""
+    try:
+        import threadpoolctl
+        for info in threadpoolctl.threadpool_info():
+            if info.get("user_api") == "blas":
+                return {"blas": f"{info.get('internal_api')} {info.get('version')}",
+                        "blas_threads": info.get("num_threads")}
+    except Exception:  # pragma: no cover - reporting only
+        pass
+    return {"blas": "unknown", "blas_threads": None}
+
+
+def cpu_baseline(q, k, v, logits_by_step, E, seqs, seed, min_seconds=10.0, max_steps=6, one_core=True):
     """The oracle, as it stands, on whole steps of the same workload (all canvas rows:
     attention, sampler with its state carried from step to step, self-conditioning),
-    run until `min_seconds` have passed."""
+    run until `min_seconds` have passed, on every host core the process may use (BLAS
+    and NumPy threads set to that count); then one more step with BLAS on one thread."""
     from oracle.attn import attn_mixed
     from oracle.sampler import sampler_step, init_canvas, CONV_OR
     from oracle.selfcond import selfcond_embed
@@ -67,23 +81,46 @@ def cpu_baseline(q, k, v, logits_by_step, E, seqs, seed, min_seconds=10.0, max_s
     except AttributeError:
         cores = os.cpu_count() or 1
     cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
-    canvas = init_canvas([(0, CANVAS, seed, 0)], VOCAB)
-    prev = np.full(CANVAS, -1, np.int64)
-    stable = [0]
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits
+    except ImportError:  # pragma: no cover
+        limit = None
+    state = {"canvas": init_canvas([(0, CANVAS, seed, 0)], VOCAB), "prev": np.full(CANVAS, -1, np.int64),
+             "stable": [0], "t": 0}
+
+    def one_step():
+        t = state["t"]
+        logits = logits_by_step(t)
+        attn_mixed(seqs, -1, q, k, v, HQ, HKV)
+        r = sampler_step(logits, [(0, CANVAS, seed, t)], VOCAB, BUDGET, 1, state["canvas"], state["prev"],
+                         state["stable"], stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=CONV_OR)
+        state["canvas"], state["prev"], state["stable"] = r["canvas"], r["prev_argmax"], list(r["stable_count"])
+        selfcond_embed(E, logits=logits)
+        state["t"] = t + 1
+
+    ctx = limit(limits=cores, user_api="blas") if limit else None
+    if ctx is not None:
+        ctx.__enter__()
     steps = 0
     t0 = time.perf_counter()
     while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
-        logits = logits_by_step(steps)
-        attn_mixed(seqs, -1, q, k, v, HQ, HKV)
-        r = sampler_step(logits, [(0, CANVAS, seed, steps)], VOCAB, BUDGET, 1, canvas, prev, stable,
-                         stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=CONV_OR)
-        canvas, prev, stable = r["canvas"], r["prev_argmax"], list(r["stable_count"])
-        selfcond_embed(E, logits=logits)
+        one_step()
         steps += 1
     dt = time.perf_counter() - t0
-    return {"value": round(steps / dt, 6), "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} whole steps of the same workload (all {CANVAS} canvas rows: attention, sampler "
-                      f"with state carried, self-conditioning) in {dt:.1f} s", "cpu": _cpu_model()}
+    blas = _blas()
+    if ctx is not None:
+        ctx.__exit__(None, None, None)
+    res = {"value": round(steps / dt, 6), "unit": "steps/s", "cores": cores, "kind": "oracle",
+           "sample": f"{steps} whole steps of the same workload (all {CANVAS} canvas rows: attention, sampler "
+                     f"with state carried, self-conditioning) in {dt:.1f} s", "cpu": _cpu_model(), **blas}
+    if one_core and limit is not None:
+        with limit(limits=1, user_api="blas"):
+            t1 = time.perf_counter()
+            one_step()
+            res["one_core_value"] = round(1.0 / (time.perf_counter() - t1), 6)
+            res["one_core_note"] = "one more step with BLAS on one thread (NumPy's elementwise work is single-threaded)"
+    return res
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "denoise_step_prefix4096_canvas256_hbm_counters.md")
@@ -378,6 +415,83 @@ def per_config(path, reps=20, warm=5):
     print(f"[per-config] wrote {path}", file=sys.stderr, flush=True)
 
 
+def measure_ceilings(torch, read_sizes=(134217728, 1208991744, 4294967296), copy_bytes=1073741824,
+                     reps=20, warm=5, mfma_iters=20000):
+    """Achievable ceilings with the in-tree measurement kernels (libdg_probe.so): a streaming
+    read at each size in read_sizes (the sampler's logits, the self-conditioning call's
+    bytes, 4 GiB), a copy, and back-to-back bf16 MFMAs; the best over a few launch shapes,
+    median event time of `reps` launches each."""
+    from block_denoising_step_amd import probe
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def med_ms(fn):
+        for _ in range(warm):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return t[len(t) // 2]
+
+    res = {"cus": cus, "reps": reps, "read": [], "copy": None, "mfma_bf16": None}
+    big = torch.empty(max(max(read_sizes), 2 * copy_bytes) // 16, 4, dtype=torch.int32, device=dev)
+    big.view(torch.uint8)[::4096].fill_(1)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    for nbytes in read_sizes:
+        src = big.view(torch.uint8)[:nbytes]
+        best = None
+        for blocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+            ms = med_ms(lambda: probe.read(src, sink, blocks))
+            gbs = nbytes / ms / 1e6
+            if best is None or gbs > best["gbs"]:
+                best = {"bytes": nbytes, "blocks": blocks, "us": round(ms * 1e3, 2), "gbs": round(gbs, 1)}
+        best["frac_of_8000"] = round(best["gbs"] / PEAK_HBM_GBS, 4)
+        res["read"].append(best)
+        print(f"[ceilings] read {best}", file=sys.stderr, flush=True)
+    half = copy_bytes
+    srcb = big.view(torch.uint8)[:half]
+    dstb = big.view(torch.uint8)[half:2 * half]
+    best = None
+    for blocks in ((cus * 4, cus * 8, cus * 16) if copy_bytes else ()):
+        ms = med_ms(lambda: probe.copy(dstb, srcb, blocks))
+        gbs = 2 * half / ms / 1e6
+        if best is None or gbs > best["gbs"]:
+            best = {"bytes_each_way": half, "blocks": blocks, "us": round(ms * 1e3, 2), "gbs_read_plus_write": round(gbs, 1)}
+    if best is not None:
+        best["frac_of_8000"] = round(best["gbs_read_plus_write"] / PEAK_HBM_GBS, 4)
+        res["copy"] = best
+        print(f"[ceilings] copy {best}", file=sys.stderr, flush=True)
+    del big
+    msink = torch.empty(cus * 2 * 256, dtype=torch.float32, device=dev)
+    best = None
+    for blocks in (cus, cus * 2):
+        ms = med_ms(lambda: probe.mfma_bf16(msink, blocks, mfma_iters))
+        flop = blocks * 4 * mfma_iters * 8 * 2 * 32 * 32 * 16
+        tf = flop / ms / 1e9
+        if best is None or tf > best["tflops"]:
+            best = {"blocks": blocks, "waves_per_cu": 4 * blocks // cus, "iters": mfma_iters, "us": round(ms * 1e3, 2),
+                    "tflops": round(tf, 1)}
+    best["frac_of_2500"] = round(best["tflops"] / PEAK_BF16_TFLOPS, 4)
+    res["mfma_bf16"] = best
+    print(f"[ceilings] mfma {best}", file=sys.stderr, flush=True)
+    return res
+
+
+def ceilings(path):
+    import torch
+    torch.cuda.set_device(0)
+    res = measure_ceilings(torch)
+    res["device"] = torch.cuda.get_device_name(0)
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res), flush=True)
+
+
 def wait_flag(flags, slot, timeout_s=30.0):
     """Spin until the selection kernel has written slot `slot` of the pinned flag pair
     (the host set it to -1 before enqueueing that step); return the flag."""
@@ -502,7 +616,7 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
     print(json.dumps(res), flush=True)
 
 
-def graph_steps(path, args, dg, torch, attn_call, step_logits, bufs, sc_call, seed, flags):
+def graph_steps(path, args, dg, torch, step, seed, flags):
     """The step loop with every step replayed from a recorded HIP graph: attention, the
     sampler (reading its step from a device counter that the selection advances) and
     self-conditioning, recorded once per (logits buffer, converged-flag slot) pair, so
@@ -511,28 +625,30 @@ def graph_steps(path, args, dg, torch, attn_call, step_logits, bufs, sc_call, se
     recorded argument). Writes JSON to `path` and prints one line."""
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
+    bufs, step_logits = step.bufs, step.logits
     counter = torch.zeros(1, dtype=torch.int32, device=dev)
-    kw = dict(stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR, step_counter=counter)
+    kw = dict(stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR, step_counter=counter,
+              probs=bufs.probs, probs_scale=bufs.probs_scale)
     init = dg.prepare_sampler(None, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
                               num_rows=CANVAS, step_counter=counter)
     side = torch.cuda.Stream()
     graphs = []
     t_rec = time.perf_counter()
-    for lg in step_logits:
+    for i, lg in enumerate(step_logits):
         pair = []
         for slot in range(2):
             samp = dg.prepare_sampler(lg, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, **kw)
             samp.args.converged = flags[slot:slot + 1].data_ptr()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=side):
-                attn_call()
+                step.attn()
                 samp()
-                sc_call()
+                step.selfcond[i]()
             pair.append((g, samp))
         graphs.append(pair)
     torch.cuda.synchronize()
     t_rec = time.perf_counter() - t_rec
-    state = {"t": 0, "issued": 0, "pending": None, "blocks": 0}
+    state = {"t": 0, "issued": 0, "pending": None, "blocks": 0, "spec": 0}
 
     def start_block():
         init(stream)
@@ -554,7 +670,9 @@ def graph_steps(path, args, dg, torch, attn_call, step_logits, bufs, sc_call, se
 
     def run(n):
         for _ in range(n):
-            if one_step() or state["t"] >= STEP_LIMIT:
+            prev_done = one_step()
+            if prev_done or state["t"] >= STEP_LIMIT:
+                state["spec"] += int(prev_done)
                 wait_flag(flags, state["pending"])
                 state["blocks"] += 1
                 start_block()
@@ -562,15 +680,17 @@ def graph_steps(path, args, dg, torch, attn_call, step_logits, bufs, sc_call, se
     start_block()
     run(args.warmup)
     torch.cuda.synchronize()
-    b0 = state["blocks"]
+    b0, s0 = state["blocks"], state["spec"]
     t0 = time.perf_counter()
     run(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    useful = args.steps - (state["spec"] - s0)
     res = {"mode": "each step replayed from a recorded HIP graph (attention, sampler with a device step counter, "
                    "self-conditioning)",
-           "steps_per_s": round(args.steps / elapsed, 3), "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
-           "steps": args.steps, "warmup": args.warmup, "blocks_in_timed_region": state["blocks"] - b0,
+           "steps_per_s": round(useful / elapsed, 3), "ms_per_step": round(elapsed * 1e3 / useful, 4),
+           "steps": args.steps, "speculative_steps": args.steps - useful, "warmup": args.warmup,
+           "blocks_in_timed_region": state["blocks"] - b0,
            "graphs": len(graphs) * 2, "record_seconds": round(t_rec, 4),
            "workload": "the default step workload (canvas 256 on prefix 4096, vocab 262144, embed 2048, bf16)"}
     with open(path, "w") as f:
@@ -590,8 +710,14 @@ def main():
                     help="instead of the step loop, time every call of the five workloads and write JSON to PATH")
     ap.add_argument("--block-loop", metavar="PATH",
                     help="instead of the step loop, time the block-autoregressive loop on a paged cache; JSON to PATH")
+    ap.add_argument("--ceilings", metavar="PATH",
+                    help="instead of the step loop, measure the achievable HBM read/copy and bf16 MFMA ceilings "
+                         "with the in-tree measurement kernels; JSON to PATH")
     ap.add_argument("--graph", metavar="PATH",
                     help="instead of the eager step loop, replay each step from a recorded HIP graph; JSON to PATH")
+    ap.add_argument("--selfcond-input", choices=("probs", "logits"), default="probs",
+                    help="what self-conditioning reads: the sampler's block-scaled probabilities, or the logits "
+                         "with the sampler's row statistics")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -605,9 +731,13 @@ def main():
     if args.block_loop:
         block_loop(args.block_loop)
         return
+    if args.ceilings:
+        ceilings(args.ceilings)
+        return
 
     import torch
     import block_denoising_step_amd as dg
+    from block_denoising_step_amd.step import DenoiseStep
     from workloads import attn_case, embed_table, driver_pool, driver_rows, request_seeds
 
     dev = "cuda:0"
@@ -627,20 +757,8 @@ def main():
     settle = 9  # steps >= 8 read the settled rows: 9 distinct logits tensors cover every step
     step_logits = [pool[torch.from_numpy(driver_rows(t)).to(dev)].contiguous() for t in range(settle)]
     seed = request_seeds(2, 1)[0]
-
-    attn_out = torch.empty_like(q)
-    lse = torch.empty(CANVAS, HQ, device=dev, dtype=torch.float32)
-    # the sampler also writes block-scaled probabilities for self-conditioning
-    bufs = dg.SamplerBuffers(CANVAS, 1, dev, vocab=VOCAB, probs_dtype=torch.bfloat16)
-    sc_out = torch.empty(CANVAS, EMBED, device=dev, dtype=torch.bfloat16)
-
-    attn_call = dg.prepare_attn(q, k, v, attn_out, case.seqs, -1, HQ, HKV, lse=lse)
-    samp_calls = [dg.prepare_sampler(step_logits[t], [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET,
-                                     stable_k=STABLE_K, tau=TAU, step_limit=STEP_LIMIT, combine=dg.DG_CONV_OR)
-                  for t in range(settle)]
-    init_call = dg.prepare_sampler(None, [(0, CANVAS, seed, 0)], VOCAB, bufs, BUDGET, flags=dg.DG_INIT_CANVAS,
-                                   num_rows=CANVAS)
-    sc_call = dg.prepare_selfcond(bufs.probs, E, sc_out, p_scale=bufs.probs_scale)
+    step = DenoiseStep(q, k, v, case.seqs, -1, HQ, HKV, step_logits, E, BUDGET, STABLE_K, TAU, STEP_LIMIT,
+                       combine=dg.DG_CONV_OR, seed=seed, selfcond_input=args.selfcond_input)
 
     stream = torch.cuda.current_stream()
     # The selection writes each step's converged flag straight into pinned host memory,
@@ -651,7 +769,7 @@ def main():
     # 6 us of GPU time) sits on the stream between steps.
     flags = torch.zeros(2, dtype=torch.int32, pin_memory=True)
     if args.graph:
-        graph_steps(args.graph, args, dg, torch, attn_call, step_logits, bufs, sc_call, seed, flags)
+        graph_steps(args.graph, args, dg, torch, step, seed, flags)
         return
 
     if args.copy_calibration_mib:
@@ -662,39 +780,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    state = {"t": 0, "block": 0, "issued": 0, "pending": None}
+    # issued: steps enqueued; spec: speculative steps (the one enqueued after a block's
+    # converging step, before the host has read its flag), whose results are dropped
+    state = {"t": 0, "block": 0, "issued": 0, "spec": 0, "pending": None}
 
     def start_block():
-        seed_b = (seed + state["block"]) & ((1 << 64) - 1)
-        init_call.args._keep[0].step = 0
-        init_call.args._keep[0].seed = seed_b
-        init_call(stream)
+        step.start_block(seed + state["block"], stream)
         state["t"] = 0
         state["pending"] = None
 
     def one_step(ev=None):
         """Enqueue one step; return the previous step's converged flag. ev: None, or four
-        events [before attention, after attention, before self-conditioning, after it]
-        (a sample of the timed steps is bracketed by events: each record costs GPU time)."""
+        events (a sample of the timed steps is bracketed by events: each record costs GPU
+        time)."""
         t = state["t"]
-        i = min(t, settle - 1)
-        samp = samp_calls[i]
-        samp.args._keep[0].step = t
-        samp.args._keep[0].seed = (seed + state["block"]) & ((1 << 64) - 1)
         slot = state["issued"] % 2
         flags[slot] = -1  # its last value (two steps back) has been read
-        samp.args.converged = flags[slot:slot + 1].data_ptr()
-        if ev is not None:
-            ev[0].record(stream)
-        attn_call(stream)
-        if ev is not None:
-            ev[1].record(stream)
-        samp(stream)
-        if ev is not None:
-            ev[2].record(stream)
-        sc_call(stream)
-        if ev is not None:
-            ev[3].record(stream)
+        step.enqueue(t, min(t, settle - 1), stream, converged_ptr=flags[slot:slot + 1].data_ptr(), events=ev)
         state["issued"] += 1
         state["t"] = t + 1
         # the host reads the previous step's flag while this step runs on the GPU
@@ -706,9 +808,13 @@ def main():
 
     def run(n, events=None):
         for s_ in range(n):
-            if one_step(events[s_] if events is not None else None) or state["t"] >= STEP_LIMIT:
-                # converged: the step just issued was speculative. Its flag slot is reused
-                # two steps on, so wait until it has been written before the new block
+            prev_done = one_step(events[s_] if events is not None else None)
+            if prev_done or state["t"] >= STEP_LIMIT:
+                # converged: the step just issued was speculative (when the flag came from
+                # the step before it). Its flag slot is reused two steps on, so wait until
+                # it has been written before the new block
+                if prev_done:
+                    state["spec"] += 1
                 wait_flag(flags, state["pending"])
                 state["block"] += 1
                 start_block()
@@ -721,24 +827,37 @@ def main():
     SAMPLE_EVERY = 8
     events = [[torch.cuda.Event(enable_timing=True) for j in range(4)] if i % SAMPLE_EVERY == 0 else None
               for i in range(args.steps)]
-    blocks0 = state["block"]
+    blocks0, spec0 = state["block"], state["spec"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.steps, events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     blocks = state["block"] - blocks0
+    spec = state["spec"] - spec0
+
+    # achievable ceilings, measured after the timed region in the same process: a streaming
+    # read of the sampler's and the self-conditioning call's byte counts, bf16 MFMA
+    alg0 = algorithmic()
+    ceil = measure_ceilings(torch, read_sizes=(alg0["samp_bytes"] // 16 * 16, alg0["sc_bytes"] // 16 * 16),
+                            copy_bytes=0, mfma_iters=4000)
+    ceil_read = {r["bytes"]: r["gbs"] for r in ceil["read"]}
+    samp_ceil = ceil_read[alg0["samp_bytes"] // 16 * 16]
+    sc_ceil = ceil_read[alg0["sc_bytes"] // 16 * 16]
+    mfma_ceil = ceil["mfma_bf16"]["tflops"]
 
     sampled = [e for e in events if e is not None]
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sampled]))
     samp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in sampled]))
     sc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sampled]))
     alg = algorithmic()
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = args.steps / elapsed
+    useful = args.steps - spec
+    ms_per_step = elapsed * 1e3 / useful
+    value = useful / elapsed
 
     attn_tflops = alg["attn_flop"] / (attn_ms * 1e-3) / 1e12
     samp_gbs = alg["samp_bytes"] / (samp_ms * 1e-3) / 1e9
+    probs_mode = args.selfcond_input == "probs"
     samp_rw_gbs = (alg["samp_bytes"] + alg["samp_probs_bytes"]) / (samp_ms * 1e-3) / 1e9
     sc_gbs = alg["sc_bytes"] / (sc_ms * 1e-3) / 1e9
     sc_tflops = alg["sc_flop"] / (sc_ms * 1e-3) / 1e12
@@ -763,7 +882,13 @@ def main():
                         "mean entropy < 0.05 (limit 48)",
             "canvas": CANVAS, "prefix": PREFIX, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
             "vocab": VOCAB, "embed_dim": EMBED, "blocks_in_timed_region": blocks,
+            "selfcond_input": args.selfcond_input,
         },
+        "steps_issued": args.steps,
+        "speculative_steps": spec,
+        "value_note": f"value and ms_per_step count the {useful} useful steps of the {args.steps} timed ones: the "
+                      f"{spec} speculative step(s) enqueued after a converging step, before the host read its flag, "
+                      "ran in the timed region but their results are dropped",
         "roofline": {
             "kernel": "dg_selfcond_embed (selfcond_gemm_dma + selfcond_reduce)",
             "bound": "hbm",
@@ -773,16 +898,25 @@ def main():
             "frac": round(sc_gbs / PEAK_HBM_GBS, 4),
             "traffic": counted_traffic(),
             "traffic_unit": "bytes per call",
+            "measured_ceiling": sc_ceil,
+            "frac_of_measured_ceiling": round(sc_gbs / sc_ceil, 4),
+            "ceiling_note": "measured_ceiling: in-tree streaming-read kernel over the same byte count, in this run",
         },
         "kernels": {
             "attn_mixed": {"ms": round(attn_ms, 4), "tflops": round(attn_tflops, 1),
-                           "frac_bf16_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
-            "sampler_step": {"ms": round(samp_ms, 4), "gbs": round(samp_gbs, 1),
-                             "frac_hbm_peak": round(samp_gbs / PEAK_HBM_GBS, 4),
-                             "gbs_with_probs_write": round(samp_rw_gbs, 1),
-                             "frac_hbm_peak_with_probs_write": round(samp_rw_gbs / PEAK_HBM_GBS, 4)},
+                           "frac_bf16_mfma_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                           "frac_measured_mfma_ceiling": round(attn_tflops / mfma_ceil, 4)},
+            "sampler_step": dict({"ms": round(samp_ms, 4), "gbs": round(samp_gbs, 1),
+                                  "frac_hbm_peak": round(samp_gbs / PEAK_HBM_GBS, 4),
+                                  "frac_measured_read_ceiling": round(samp_gbs / samp_ceil, 4)},
+                                 **({"gbs_with_probs_write": round(samp_rw_gbs, 1),
+                                     "frac_hbm_peak_with_probs_write": round(samp_rw_gbs / PEAK_HBM_GBS, 4)}
+                                    if probs_mode else {})),
             "selfcond_embed": {"ms": round(sc_ms, 4), "gbs": round(sc_gbs, 1), "tflops": round(sc_tflops, 1),
-                               "frac_hbm_peak": round(sc_gbs / PEAK_HBM_GBS, 4)},
+                               "frac_hbm_peak": round(sc_gbs / PEAK_HBM_GBS, 4),
+                               "frac_measured_read_ceiling": round(sc_gbs / sc_ceil, 4)},
+            "measured_ceilings": {"read_gbs": {str(k_): v_ for k_, v_ in ceil_read.items()},
+                                  "mfma_bf16_tflops": mfma_ceil},
             "timing": f"HIP events on the launch stream around each call, on {len(sampled)} of the {args.steps} "
                       f"timed steps (every {SAMPLE_EVERY}th)",
         },

@@ -95,7 +95,7 @@ class DgInjectArgs(ctypes.Structure):
 EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sampler_workspace_size",
            "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_selfcond_inject",
            "dg_selfcond_inject_workspace_size", "dg_status_string", "dg_last_error",
-           "dg_abi_version"]
+           "dg_abi_version", "dg_test_force_register_staged"]
 
 _lib = None
 
@@ -138,12 +138,27 @@ def load() -> ctypes.CDLL:
     lib.dg_last_error.restype = ctypes.c_char_p
     lib.dg_abi_version.argtypes = []
     lib.dg_abi_version.restype = ctypes.c_int
+    lib.dg_test_force_register_staged.argtypes = [ctypes.c_int]
+    lib.dg_test_force_register_staged.restype = ctypes.c_int
     if lib.dg_abi_version() != ABI_VERSION:
         # the structs above would not match the library's: refuse rather than pass garbage
         raise RuntimeError(f"{LIB_PATH} has ABI version {lib.dg_abi_version()}, this binding needs {ABI_VERSION}; "
                            "rebuild it")
     _lib = lib
     return lib
+
+
+class force_register_staged:
+    """Test hook as a context manager: inside it, dg_attn_mixed plans every request on the
+    register-staged attention kernel (dg_test_force_register_staged)."""
+
+    def __enter__(self):
+        self._prev = load().dg_test_force_register_staged(1)
+        return self
+
+    def __exit__(self, *exc):
+        load().dg_test_force_register_staged(self._prev)
+        return False
 
 
 def status_string(status: int) -> str:
@@ -485,9 +500,11 @@ def prepare_sampler(logits, reqs, vocab, bufs, budget, **kw):
     return Prepared(load().dg_sampler_step, a, (bufs,))
 
 
-def prepare_selfcond(p, embed, out, row_max=None, row_sum=None, p_scale=None):
+def prepare_selfcond(p, embed, out, row_max=None, row_sum=None, p_scale=None, workspace=None):
+    """workspace: a uint8 device tensor to reuse when it is large enough (calls that never
+    run concurrently can share one)."""
     a = make_selfcond_args(p, embed, out, row_max, row_sum, p_scale=p_scale)
-    ws = _workspace(selfcond_workspace_size(a), p, None)
+    ws = _workspace(selfcond_workspace_size(a), p, workspace)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel()
     return Prepared(load().dg_selfcond_embed, a, (ws,))

@@ -9,6 +9,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
 SOURCES = ["dg_host.cpp", "sampler.hip", "selfcond.hip", "attn.hip", "kvcache.hip", "inject.hip"]
+# measurement kernels (achievable ceilings), a library of their own
+PROBE_LIB = os.path.join(HERE, "libdg_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 # Packed-fp32 instructions are kept out of every code object (the compiler would
 # otherwise form v_pk_* from plain float code).
@@ -24,13 +27,14 @@ def _hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object, then link libdg.so. Always recompiles."""
+    """Compile every source to an object, then link libdg.so and libdg_probe.so. Always
+    recompiles."""
     hipcc = _hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -46,12 +50,14 @@ def build(verbose: bool = False) -> str:
             failed.append((src, out))
     if failed:
         raise RuntimeError("libdg build failed:\n" + "\n".join(f"== {s}\n{o}" for s, o in failed))
-    tmp = LIB + ".tmp"
-    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("libdg link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    probe_objs = objs[len(SOURCES):]
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, probe_objs)):
+        tmp = lib + ".tmp"
+        link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{os.path.basename(lib)} link failed:\n" + r.stdout)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -1327,20 +1327,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
 
 template <bool kBf16, int D, bool kPaged>
 int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
-  // work [0, num_wide): 64-rows-per-wave kernel; [num_wide, num_work): 128-row kernels
+  // work [0, num_wide): 64-rows-per-wave kernel; [num_wide, num_dma): 128-row LDS-DMA
+  // kernel; [num_dma, num_work): register-staged kernel (each request on one of them)
   if constexpr (kBf16 && D == 256) {
     if (plan.num_wide > 0) {
       args.work_offset = 0;
       hipLaunchKernelGGL(attn_fwd_bf16_d256_w64<kPaged>, dim3(plan.num_wide), dim3(kThreads), 0, s, args);
     }
+    if (plan.num_dma > plan.num_wide) {
+      args.work_offset = plan.num_wide;
+      hipLaunchKernelGGL(attn_fwd_bf16_d256<kPaged>, dim3(plan.num_dma - plan.num_wide), dim3(kThreads), 0, s, args);
+    }
   }
-  if (plan.num_work > plan.num_wide) {
-    args.work_offset = plan.num_wide;
-    const dim3 grid(plan.num_work - plan.num_wide);
-    if (kBf16 && D == 256 && plan.dma)
-      hipLaunchKernelGGL(attn_fwd_bf16_d256<kPaged>, grid, dim3(kThreads), 0, s, args);
-    else
-      hipLaunchKernelGGL((attn_fwd<kBf16, D, kPaged>), grid, dim3(kThreads), 0, s, args);
+  if (plan.num_work > plan.num_dma) {
+    args.work_offset = plan.num_dma;
+    hipLaunchKernelGGL((attn_fwd<kBf16, D, kPaged>), dim3(plan.num_work - plan.num_dma), dim3(kThreads), 0, s, args);
   }
   if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<kBf16, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
   return (int)hipGetLastError();

@@ -3,6 +3,7 @@
 // call either fails validation here (nothing launched, nothing written) or is
 // handed to the launchers in the .hip files.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -14,6 +15,9 @@ namespace dg {
 namespace {
 
 thread_local char g_last_error[512] = "";
+// Test hook (dg_test_force_register_staged): plan every request on the register-staged
+// attention kernel.
+std::atomic<int> g_force_register_staged{0};
 
 dg_status fail(dg_status s, const char* msg) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
@@ -122,12 +126,15 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
 
   // tiles and chunks; the split of a request, and the kernel that runs it, depend on
   // that request alone, so its result is the same whatever else is in the batch.
-  // The LDS-DMA kernels (bf16, head_dim 256) take 32-bit byte offsets within a request's K/V.
-  // Paged requests are addressed per sub-tile, so only the contiguous layout has the limit.
-  plan->dma = a->dtype == DG_BF16 && a->head_dim == 256 && !a->kv_fp8;
-  for (int s = 0; s < a->num_seqs && !paged; ++s) {
+  // The LDS-DMA kernels (bf16, head_dim 256) take 32-bit byte offsets within a request's
+  // K/V, so a contiguous request whose K/V span passes 2^31 - 1 bytes runs on the
+  // register-staged kernel; paged requests are addressed per sub-tile and have no limit.
+  const bool dma_ok = a->dtype == DG_BF16 && a->head_dim == 256 && !a->kv_fp8 &&
+                      !g_force_register_staged.load(std::memory_order_relaxed);
+  bool dma[DG_MAX_SEQS];
+  for (int s = 0; s < a->num_seqs; ++s) {
     const dg_seq& q = a->seqs[s];
-    if (((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 > INT32_MAX) plan->dma = 0;
+    dma[s] = dma_ok && (paged || ((int64_t)q.prefix_len + q.num_q) * a->num_kv_heads * a->head_dim * 2 <= INT32_MAX);
   }
   // q tiles and key chunks of request q at a given tile height
   struct Split { int64_t ntiles_q, nch, chunk_tiles, sub_tiles; };
@@ -165,7 +172,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   for (int s = 0; s < a->num_seqs; ++s) {
     const dg_seq& q = a->seqs[s];
     wide[s] = false;
-    if (plan->dma && q.num_q > 0) {
+    if (dma[s] && q.num_q > 0) {
       const Split w = split(q, kAttnWideTileRows);
       const int64_t groups = w.ntiles_q * w.nch * a->num_kv_heads;
       wide[s] = groups > 0 && w.sub_tiles >= kWideMinSub * groups;
@@ -174,9 +181,10 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     if (!wide[s]) sq[s] = split(q, kAttnTileRows);
   }
   const int mrpg = attn_merge_rows_per_group(a->dtype == DG_BF16, a->head_dim);
-  int64_t num_work = 0, num_merge = 0, part_rows = 0, num_wide = 0;
+  int64_t num_work = 0, num_merge = 0, part_rows = 0, num_wide = 0, num_dma = 0;
   plan->num_seqs = a->num_seqs;
-  // Work list: the wide kernel's requests, then the others (two launches); within each,
+  // Work list: the wide kernel's requests, then the 128-row LDS-DMA kernel's, then the
+  // register-staged kernel's (one launch each); within each,
   // requests with the longest work groups first, so that the short ones fill the tail.
   // The order changes no result: every work group computes the same thing wherever it runs.
   int order[DG_MAX_SEQS];
@@ -187,10 +195,10 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     per_group[s] = groups > 0 ? (double)sq[s].sub_tiles / (double)groups : 0.0;
   }
   std::stable_sort(order, order + a->num_seqs, [&](int x, int y) { return per_group[x] > per_group[y]; });
-  for (int pass = 0; pass < 2; ++pass)
+  for (int pass = 0; pass < 3; ++pass)
     for (int oi = 0; oi < a->num_seqs; ++oi) {
       const int s = order[oi];
-      if (wide[s] != (pass == 0)) continue;
+      if ((wide[s] ? 0 : dma[s] ? 1 : 2) != pass) continue;
       const dg_seq& q = a->seqs[s];
       const Split& r = sq[s];
       const int tile_rows = wide[s] ? kAttnWideTileRows : kAttnTileRows;
@@ -212,6 +220,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
       sp.part_begin = (int32_t)std::min<int64_t>(part_rows, INT32_MAX);
       num_work += units * r.nch;
       if (wide[s]) num_wide += units * r.nch;
+      if (dma[s]) num_dma += units * r.nch;
       if (r.nch > 1) {
         sp.merge_count = (int32_t)std::min<int64_t>(units * (tile_rows / mrpg), INT32_MAX);
         num_merge += units * (tile_rows / mrpg);
@@ -222,6 +231,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     }
   plan->group = G;
   plan->num_wide = (int)num_wide;
+  plan->num_dma = (int)num_dma;
   plan->num_work = (int)num_work;
   plan->num_merge = (int)num_merge;
   plan->part_rows = part_rows;
@@ -468,6 +478,8 @@ const char* dg_status_string(dg_status s) {
 
 const char* dg_last_error(void) { return g_last_error; }
 int dg_abi_version(void) { return DG_ABI_VERSION; }
+
+int dg_test_force_register_staged(int on) { return g_force_register_staged.exchange(on != 0); }
 
 size_t dg_attn_workspace_size(const dg_attn_args* a) {
   AttnPlan plan;

@@ -42,10 +42,10 @@ struct AttnPlan {
   int num_seqs;
   int group;            // G = Hq / Hkv
   int num_wide;         // work groups of the 64-rows-per-wave kernel: work [0, num_wide)
-  int num_work;         // all attention work groups; [num_wide, num_work) run the 128-row kernels
+  int num_dma;          // end of the 128-row LDS-DMA kernel's work: [num_wide, num_dma)
+  int num_work;         // all attention work groups; [num_dma, num_work) run the register-staged kernel
   int num_merge;        // work groups of the merge kernel
   int64_t part_rows;    // partial rows (each D wide)
-  int dma;              // bf16, head_dim 256, every request's K/V span < 2 GiB (or paged): LDS-DMA kernel
   int block_shift;      // paged K/V: log2(block_size); -1 for the contiguous layout
   int kv_fp8;           // K/V hold E4M3 codes (bf16 queries, register-staged kernel)
   size_t part_o_offset;   // workspace: [part_rows][D] partial outputs, input dtype

@@ -1,0 +1,112 @@
+// Measurement kernels for the achievable ceilings of gfx950 (the declarations and
+// their contract are in include/dg_probe.h). Not part of the denoising step.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/dg_probe.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
+
+// Grid-stride over 16-byte words, kUnroll loads issued before any is used.
+__global__ __launch_bounds__(kThreads) void probe_read(const uint4* __restrict__ src, int64_t n,
+                                                       uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // one word per work group: XOR over the block through LDS
+  __shared__ uint32_t red[kThreads / 64];
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                       int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = v[u];
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// 8 independent accumulation chains per wave, operands in registers.
+__global__ __launch_bounds__(kThreads) void probe_mfma_bf16(float* __restrict__ sink, int iters) {
+  const float x = (float)(threadIdx.x & 7) * 0.125f;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(x + 0.0078125f * e);
+    b[e] = (__bf16)(0.5f - 0.0078125f * e);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int dg_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+  if (!src || !sink || !aligned16(src) || bytes % 16 || blocks < 1 || blocks > 65536) return -1;
+  hipLaunchKernelGGL(probe_read, dim3(blocks), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const uint4*>(src), (int64_t)(bytes / 16), sink);
+  return (int)hipGetLastError();
+}
+
+int dg_probe_copy(void* dst, const void* src, size_t bytes, int blocks, void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes % 16 || blocks < 1 || blocks > 65536) return -1;
+  const char* s = reinterpret_cast<const char*>(src);
+  const char* d = reinterpret_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return -1;
+  hipLaunchKernelGGL(probe_copy, dim3(blocks), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<uint4*>(dst), reinterpret_cast<const uint4*>(src), (int64_t)(bytes / 16));
+  return (int)hipGetLastError();
+}
+
+int dg_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream) {
+  if (!sink || blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return -1;
+  hipLaunchKernelGGL(probe_mfma_bf16, dim3(blocks), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), sink,
+                     iters);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

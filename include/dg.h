@@ -116,7 +116,7 @@ typedef struct {
   const dg_seq* seqs;           /* host array [num_seqs]; query ranges must not overlap */
   int32_t window;               /* -1: global layer; W >= 0: sliding window */
   int32_t num_q_heads;          /* Hq >= 1 */
-  int32_t num_kv_heads;         /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1,2,4,8,16} */
+  int32_t num_kv_heads;         /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv in {1,2,4,8,16,32} (else DG_ERR_UNSUPPORTED) */
   int32_t head_dim;             /* D in {64, 128, 256} */
   float scale;                  /* 0 => 1/sqrt(head_dim) */
   int32_t dtype;                /* dg_dtype of q, k, v and out */
@@ -370,6 +370,14 @@ size_t dg_selfcond_inject_workspace_size(const dg_inject_args* args);
 const char* dg_status_string(dg_status s); /* static string for a status */
 const char* dg_last_error(void);           /* message of this thread's last failed call */
 int dg_abi_version(void);                  /* DG_ABI_VERSION */
+
+/* Test hook, not for production use. With on != 0, every later dg_attn_mixed call (from
+ * any thread) plans all its requests on the register-staged attention kernel, the one
+ * that otherwise serves head_dim 64/128, fp32, FP8 K/V and contiguous bf16 head_dim-256
+ * requests whose K/V span passes 2^31 - 1 bytes; results stay within the same bars, not
+ * bit-equal to the LDS-DMA kernels. on = 0 restores the normal per-request choice.
+ * Returns the previous setting (0 or 1). */
+int dg_test_force_register_staged(int on);
 
 #ifdef __cplusplus
 }

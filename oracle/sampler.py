@@ -132,16 +132,18 @@ def sampler_step(logits: np.ndarray, reqs: Sequence, vocab: int, budget: float, 
                  conf_mode: int = CONF_NEG_ENTROPY, renoise: bool = True, stable_k: int = 3,
                  tau: float = 0.05, step_limit: int = 48, combine: int = CONV_AND,
                  entropy_in: Optional[np.ndarray] = None, conf_in: Optional[np.ndarray] = None,
-                 with_candidates: bool = True) -> Dict[str, object]:
+                 with_candidates: bool = True, stats: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, object]:
     """One denoise step of the sampler over the rows of several requests.
 
     reqs: (row_start, num_rows, seed, step) per request. logits [M, V]; canvas and
     prev_argmax [M] int. With entropy_in (and conf_in for the max-probability
     confidence) the selection reads those float32 values instead of its own.
     Returns float64 statistics, float32 entropy/conf as stored, candidates, the
-    acceptance mask, the new canvas and per-request bookkeeping.
+    acceptance mask, the new canvas and per-request bookkeeping. stats: row_stats of
+    these logits when the caller already has them (they depend on each row alone);
+    None computes them here.
     """
-    st = row_stats(logits)
+    st = row_stats(logits) if stats is None else stats
     m_rows = st["max"].shape[0]
     entropy32 = st["entropy"].astype(np.float32) if entropy_in is None else np.asarray(entropy_in, np.float32)
     if conf_mode == CONF_NEG_ENTROPY:

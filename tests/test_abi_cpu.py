@@ -362,3 +362,28 @@ def test_selfcond_workspace_is_split_k_partials():
     a.ldo = 2048
     need = dg.selfcond_workspace_size(a)
     assert need > 0 and need % (256 * 2048 * 4) == 0
+
+
+def test_probe_library_exports_every_declared_function():
+    """libdg_probe.so (the ceiling measurement kernels) exports what include/dg_probe.h
+    declares, and refuses invalid arguments before any launch."""
+    from block_denoising_step_amd import probe
+    with open(os.path.join(ROOT, "include", "dg_probe.h")) as f:
+        names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dg_probe_\w+)\s*\(", f.read(), flags=re.M)))
+    assert set(names) == set(probe.EXPORTS)
+    lib = probe.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dg_probe_read(FAKE, 100, FAKE, 4, None) == -1  # bytes not a multiple of 16
+    assert lib.dg_probe_read(FAKE, 1024, FAKE, 0, None) == -1
+    assert lib.dg_probe_copy(FAKE, FAKE + 512, 1024, 4, None) == -1  # overlapping ranges
+    assert lib.dg_probe_mfma_bf16(FAKE, 4, 0, None) == -1
+
+
+def test_force_register_staged_hook_round_trips():
+    lib = dg.load()
+    assert lib.dg_test_force_register_staged(1) == 0
+    assert lib.dg_test_force_register_staged(0) == 1
+    with dg.force_register_staged():
+        assert lib.dg_test_force_register_staged(1) == 1
+    assert lib.dg_test_force_register_staged(0) == 0

@@ -333,3 +333,40 @@ def test_block_scaled_probabilities(bf16, V):
     assert rel.max() <= tol
     assert np.all(p[ref == 0] == 0)
     np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=2e-3 if bf16 else 1e-5)
+
+
+def test_selection_max_canvas_1024():
+    """One request of DG_MAX_CANVAS = 1024 positions (four positions per thread of the
+    selection's rank sort), with a previous state: entropies, argmax, candidates and,
+    with the oracle's entropies fed in, the selection bit-exact."""
+    M, V = 1024, 16384
+    rng = np.random.default_rng(1024)
+    l = round_to_bf16((rng.standard_normal((M, V)) * np.exp(rng.uniform(np.log(0.1), np.log(10), (M, 1))))
+                      .astype(np.float32))
+    prev = row_stats(l)["argmax"].astype(np.int32)
+    prev[rng.integers(0, M, 5)] += 1  # a few positions changed their argmax
+    for budget, comb in ((128.0, CONV_OR), (700.0, CONV_AND), (5000.0, CONV_AND)):
+        _run(l, True, [(0, M, 777, 6)], V, budget, prev0=prev, stable0=np.array([4], np.int32), combine=comb,
+             label=f"canvas 1024 budget {budget}")
+
+
+def test_max_requests_64():
+    """DG_MAX_REQS = 64 requests in one call: ragged canvases (1 to 40 positions, rows
+    between them that no request owns), each at its own step and seed with its own
+    stable count; everything per request against the oracle."""
+    rng = np.random.default_rng(64)
+    V = 4096
+    reqs, row = [], 0
+    for r in range(64):
+        row += int(rng.integers(0, 3))  # gaps: rows outside every request
+        n = int(rng.integers(1, 41))
+        reqs.append((row, n, int(rng.integers(0, 2**63 - 1)), int(rng.integers(0, 20))))
+        row += n
+    M = row + 2
+    l = (rng.standard_normal((M, V)) * np.exp(rng.uniform(np.log(0.1), np.log(10), (M, 1)))).astype(np.float32)
+    prev = row_stats(l)["argmax"].astype(np.int32)
+    prev[rng.integers(0, M, 20)] += 1
+    stable0 = rng.integers(0, 5, 64).astype(np.int32)
+    for comb in (CONV_AND, CONV_OR):
+        _run(l, False, reqs, V, 9.0, prev0=prev, stable0=stable0, combine=comb, tau=2.5,
+             label=f"64 requests comb={comb}")
