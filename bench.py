@@ -439,13 +439,13 @@ def measure_ceilings(torch, read_sizes=(134217728, 1208991744, 4294967296), copy
         return t[len(t) // 2]
 
     res = {"cus": cus, "reps": reps, "read": [], "copy": None, "mfma_bf16": None}
-    big = torch.empty(max(max(read_sizes), 2 * copy_bytes) // 16, 4, dtype=torch.int32, device=dev)
-    big.view(torch.uint8)[::4096].fill_(1)
+    big = torch.empty(max(max(read_sizes), 2 * copy_bytes), dtype=torch.uint8, device=dev)
+    big[::4096].fill_(1)
     sink = torch.empty(65536, dtype=torch.int32, device=dev)
     for nbytes in read_sizes:
-        src = big.view(torch.uint8)[:nbytes]
+        src = big[:nbytes]
         best = None
-        for blocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+        for blocks in (cus, cus * 2, cus * 4, cus * 8, cus * 16):
             ms = med_ms(lambda: probe.read(src, sink, blocks))
             gbs = nbytes / ms / 1e6
             if best is None or gbs > best["gbs"]:
@@ -454,13 +454,13 @@ def measure_ceilings(torch, read_sizes=(134217728, 1208991744, 4294967296), copy
         res["read"].append(best)
         print(f"[ceilings] read {best}", file=sys.stderr, flush=True)
     half = copy_bytes
-    srcb = big.view(torch.uint8)[:half]
-    dstb = big.view(torch.uint8)[half:2 * half]
+    srcb = big[:half]
+    dstb = big[half:2 * half]
     best = None
     for blocks in ((cus * 4, cus * 8, cus * 16) if copy_bytes else ()):
         ms = med_ms(lambda: probe.copy(dstb, srcb, blocks))
         gbs = 2 * half / ms / 1e6
-        if best is None or gbs > best["gbs"]:
+        if best is None or gbs > best["gbs_read_plus_write"]:
             best = {"bytes_each_way": half, "blocks": blocks, "us": round(ms * 1e3, 2), "gbs_read_plus_write": round(gbs, 1)}
     if best is not None:
         best["frac_of_8000"] = round(best["gbs_read_plus_write"] / PEAK_HBM_GBS, 4)

@@ -14,22 +14,22 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
 
-// Grid-stride over 16-byte words, kUnroll loads issued before any is used.
+// Each work group takes runs of kUnroll * kThreads consecutive 16-byte words (grid
+// stride between runs); a thread issues its kUnroll loads of a run, guarded by the end,
+// before it uses any of them.
 __global__ __launch_bounds__(kThreads) void probe_read(const uint4* __restrict__ src, int64_t n,
                                                        uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < n; base += step) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * kThreads;
+      v[u] = i < n ? src[i] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n; i += stride) {
-    const uint4 v = src[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // one word per work group: XOR over the block through LDS
   __shared__ uint32_t red[kThreads / 64];
@@ -41,16 +41,20 @@ __global__ __launch_bounds__(kThreads) void probe_read(const uint4* __restrict__
 
 __global__ __launch_bounds__(kThreads) void probe_copy(uint4* __restrict__ dst, const uint4* __restrict__ src,
                                                        int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < n; base += step) {
     uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * kThreads;
+      if (i < n) v[u] = src[i];
+    }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = v[u];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + u * kThreads;
+      if (i < n) dst[i] = v[u];
+    }
   }
-  for (; i < n; i += stride) dst[i] = src[i];
 }
 
 // 8 independent accumulation chains per wave, operands in registers.

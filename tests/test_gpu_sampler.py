@@ -3,8 +3,10 @@
 Bars: fp32 entropies within 1e-5 absolute; argmax and row max exact; acceptance
 masks, canvas re-noise tokens and convergence bookkeeping bit-exact when the GPU
 selection is fed the oracle's entropies (DG_ENTROPY_IN); candidates, being random
-draws, are checked by the bracket test C(c-1) - 1e-5 <= u < C(c) + 1e-5 against the
-oracle's float64 CDF with the same Philox uniform.
+draws, are checked by the bracket test C(c-1) - 1e-6 <= u < C(c) + 1e-6 against the
+oracle's float64 CDF with the same Philox uniform (the kernels' fp32 sums put the
+draw's target within 190 * 2^-24 = 1.1e-5 of the exact one at worst; the largest
+distance from a bracket measured over 30,720 full-size draws is 1.5e-7).
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ from tests.gpu_util import DEV, dev, host, say
 pytestmark = pytest.mark.gpu
 
 
-def _bracket_ok(row: np.ndarray, u: float, c: int, tol: float = 1e-5) -> bool:
+def _bracket_ok(row: np.ndarray, u: float, c: int, tol: float = 1e-6) -> bool:
     l = row.astype(np.float64)
     p = np.exp(l - l.max())
     p /= p.sum()
