@@ -28,6 +28,7 @@ DG_ENTROPY_IN, DG_INIT_CANVAS, DG_SKIP_SELECT, DG_SELECT_ONLY = 1, 2, 4, 8
 DG_MAX_SEQS = DG_MAX_REQS = 64
 DG_MAX_CANVAS = 1024
 DG_PROB_BLOCK = 8192
+DG_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _c_int32, _c_int64, _c_uint32, _c_uint64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
 _vp, _fp = ctypes.c_void_p, ctypes.c_void_p
@@ -93,6 +94,7 @@ class DgInjectArgs(ctypes.Structure):
 
 
 EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sampler_workspace_size",
+           "dg_sampler_step_noalloc",
            "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_selfcond_inject",
            "dg_selfcond_inject_workspace_size", "dg_status_string", "dg_last_error",
            "dg_abi_version", "dg_test_force_register_staged"]
@@ -120,6 +122,8 @@ def load() -> ctypes.CDLL:
     lib.dg_attn_workspace_size.restype = ctypes.c_size_t
     lib.dg_sampler_step.argtypes = [ctypes.POINTER(DgSamplerArgs), _vp]
     lib.dg_sampler_step.restype = ctypes.c_int
+    lib.dg_sampler_step_noalloc.argtypes = [ctypes.POINTER(DgSamplerArgs), _vp]
+    lib.dg_sampler_step_noalloc.restype = ctypes.c_int
     lib.dg_sampler_workspace_size.argtypes = [ctypes.POINTER(DgSamplerArgs)]
     lib.dg_sampler_workspace_size.restype = ctypes.c_size_t
     lib.dg_selfcond_embed.argtypes = [ctypes.POINTER(DgSelfcondArgs), _vp]
@@ -425,6 +429,16 @@ def dg_sampler_step(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, in
     a.workspace = _ptr(bufs.workspace)
     a.workspace_bytes = 0 if bufs.workspace is None else bufs.workspace.numel()
     _check(load().dg_sampler_step(ctypes.byref(a), _stream(stream)))
+
+
+def dg_sampler_step_noalloc(logits: Optional[torch.Tensor], reqs: Sequence[Tuple[int, int, int, int]], vocab: int,
+                            bufs: SamplerBuffers, budget: float, stream=None, **kw) -> None:
+    """dg_sampler_step on the library's static scratch (no workspace, nothing allocated;
+    see include/dg.h): same arguments and results."""
+    kw.setdefault("probs", bufs.probs)
+    kw.setdefault("probs_scale", bufs.probs_scale)
+    a = make_sampler_args(logits, reqs, vocab, bufs, budget, **kw)
+    _check(load().dg_sampler_step_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 # ---- dg_selfcond_embed -----------------------------------------------------------

@@ -43,6 +43,9 @@ void key_range(int mode, int prefix, int num_q, int window, int i, int* lo, int*
 
 }  // namespace
 
+dg_status record_error(dg_status s, const char* msg) { return fail(s, msg); }
+void clear_error() { g_last_error[0] = 0; }
+
 // ---- attention plan ----------------------------------------------------------
 //
 // A request with a single chunk per q tile writes its output directly; one with

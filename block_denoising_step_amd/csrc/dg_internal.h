@@ -105,6 +105,10 @@ struct InjectPlan {
 // structs get their workspace pointers when the workspace is known (the call).
 dg_status inject_plan(const dg_inject_args* a, InjectPlan* plan, const char** msg);
 
+// Thread-local message for dg_last_error (the entry points in the .hip files use these).
+dg_status record_error(dg_status s, const char* msg);
+void clear_error();
+
 // ---- launchers (HIP side); return 0 on success or a hipError_t value ---------
 
 int launch_attn(const dg_attn_args* a, const AttnPlan& plan, void* stream);

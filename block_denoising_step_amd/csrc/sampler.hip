@@ -26,6 +26,7 @@
 // tokenima", and, for re-noising, [P2] ("DiffusionGemma 개발자 가이드") sections
 // "아키텍처 (The Architecture)" and "Diffusion에 스도쿠가 흥미로운 이유".
 #include <climits>
+#include <mutex>
 
 #include "dg_common.cuh"
 #include "dg_internal.h"
@@ -710,4 +711,67 @@ int launch_sampler(const dg_sampler_args* a, const SamplerPlan& plan, void* stre
 
 const char* hip_error_name(int err) { return hipGetErrorString((hipError_t)err); }
 
+// ---- dg_sampler_step_noalloc: the sampler's workspace in a static device array ----------
+//
+// `scratch` holds the row pass's chunk statistics and sub-chunk masses. Every byte a call
+// reads there is written earlier in the same call (each (row, chunk) entry by the row
+// pass, before the finalize reads it), so nothing has to start at zero. Each GPU holds its
+// own copy at its own address, looked up once per device with hipGetSymbolAddress: in
+// host code `scratch` names a host-side stand-in, never to be passed to a kernel.
+namespace {
+constexpr size_t kScratchBytes = (size_t)DG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (looked up on the first call on each
+// device, with that device current), or null with *err set.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
 }  // namespace dg
+
+extern "C" dg_status dg_sampler_step_noalloc(const dg_sampler_args* a, void* stream) {
+  using namespace dg;
+  SamplerPlan plan;
+  const char* msg = "";
+  dg_status s = sampler_plan(a, &plan, &msg);
+  if (s != DG_OK) return record_error(s, msg);
+  if (plan.bytes > kScratchBytes)
+    return record_error(DG_ERR_WORKSPACE, "dg_sampler_step_noalloc: the call needs more than the "
+                                          "DG_NOALLOC_SCRATCH_BYTES of static scratch (see dg_sampler_workspace_size)");
+  dg_sampler_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (plan.bytes) {
+    hipError_t err = hipSuccess;
+    void* p = scratch_ptr(&err);
+    if (!p) return record_error(DG_ERR_HIP, hipGetErrorString(err));
+    b.workspace = p;
+    b.workspace_bytes = kScratchBytes;
+  }
+  const int e = launch_sampler(&b, plan, stream);
+  if (e) return record_error(DG_ERR_HIP, hip_error_name(e));
+  clear_error();
+  return DG_OK;
+}

@@ -255,6 +255,22 @@ typedef struct {
 dg_status dg_sampler_step(const dg_sampler_args* args, void* stream);
 size_t dg_sampler_workspace_size(const dg_sampler_args* args);
 
+/* dg_sampler_step_noalloc: dg_sampler_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, validation, kernels and results as dg_sampler_step, except that
+ * args->workspace and args->workspace_bytes are ignored: the workspace is a static device
+ * array of DG_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends. The call allocates and frees nothing. A call whose
+ * dg_sampler_workspace_size exceeds DG_NOALLOC_SCRATCH_BYTES returns DG_ERR_WORKSPACE
+ * and launches nothing (4 MiB holds about 1800 rows at a 262144-entry bf16 vocabulary).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on different streams, or from different threads without ordering) race and give
+ * undefined results. The array keeps the last call's contents; a call reads only what it
+ * wrote itself. The first call on each device looks up the array's device address
+ * (hipGetSymbolAddress) with that device current; a failure there returns DG_ERR_HIP. */
+#define DG_NOALLOC_SCRATCH_BYTES (4u << 20)
+dg_status dg_sampler_step_noalloc(const dg_sampler_args* args, void* stream);
+
 /* ------------------------------------------------------------------------------
  * dg_selfcond_embed: the probability-weighted average of the token embeddings
  * ([P1] section "안정성을 위한 셀프 컨디셔닝"; [P3] section

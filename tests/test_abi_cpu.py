@@ -387,3 +387,21 @@ def test_force_register_staged_hook_round_trips():
     with dg.force_register_staged():
         assert lib.dg_test_force_register_staged(1) == 1
     assert lib.dg_test_force_register_staged(0) == 0
+
+
+def test_sampler_noalloc_validation_before_any_launch():
+    """dg_sampler_step_noalloc validates like dg_sampler_step (its workspace fields are
+    ignored) and refuses a call that needs more than its static scratch, before any HIP
+    call."""
+    lib = dg.load()
+    for change in (dict(num_reqs=0), dict(vocab=0), dict(flags=16), dict(entropy=None)):
+        a = _sampler(**change)
+        assert lib.dg_sampler_step_noalloc(ctypes.byref(a), None) == dg.DG_ERR_INVALID_ARG
+    bufs = dg.SamplerBuffers.__new__(dg.SamplerBuffers)
+    for n in ("entropy", "conf", "row_max", "row_sum", "argmax", "cand", "accept", "canvas", "prev_argmax",
+              "stable_count", "num_accepted", "converged", "mean_entropy"):
+        setattr(bufs, n, _T((2048,)))
+    big = dg.make_sampler_args(_T((2048, 262144)), [(0, 1024, 1, 0), (1024, 1024, 2, 0)], 262144, bufs, 64.0)
+    assert dg.sampler_workspace_size(big) > dg.DG_NOALLOC_SCRATCH_BYTES
+    assert lib.dg_sampler_step_noalloc(ctypes.byref(big), None) == dg.DG_ERR_WORKSPACE
+    assert "DG_NOALLOC_SCRATCH_BYTES" in dg.last_error()
