@@ -468,17 +468,22 @@ def measure_ceilings(torch, read_sizes=(134217728, 1208991744, 4294967296), copy
         print(f"[ceilings] copy {best}", file=sys.stderr, flush=True)
     del big
     msink = torch.empty(cus * 2 * 256, dtype=torch.float32, device=dev)
-    best = None
-    for blocks in (cus, cus * 2):
-        ms = med_ms(lambda: probe.mfma_bf16(msink, blocks, mfma_iters))
-        flop = blocks * 4 * mfma_iters * 8 * 2 * 32 * 32 * 16
-        tf = flop / ms / 1e9
-        if best is None or tf > best["tflops"]:
-            best = {"blocks": blocks, "waves_per_cu": 4 * blocks // cus, "iters": mfma_iters, "us": round(ms * 1e3, 2),
-                    "tflops": round(tf, 1)}
-    best["frac_of_2500"] = round(best["tflops"] / PEAK_BF16_TFLOPS, 4)
-    res["mfma_bf16"] = best
-    print(f"[ceilings] mfma {best}", file=sys.stderr, flush=True)
+    # operands: N(0, 1) bf16 draws (as a GEMM's inputs vary), or one fixed pair
+    g = torch.Generator(device=dev)
+    g.manual_seed(214999)
+    ops = torch.randn(cus * 2 * 256 * 64, device=dev, generator=g).to(torch.bfloat16)
+    for label, o in (("mfma_bf16", ops), ("mfma_bf16_fixed_operands", None)):
+        best = None
+        for blocks in (cus, cus * 2):
+            ms = med_ms(lambda: probe.mfma_bf16(msink, blocks, mfma_iters, ops=o))
+            flop = blocks * 4 * mfma_iters * 8 * 2 * 32 * 32 * 16
+            tf = flop / ms / 1e9
+            if best is None or tf > best["tflops"]:
+                best = {"blocks": blocks, "waves_per_cu": 4 * blocks // cus, "iters": mfma_iters,
+                        "us": round(ms * 1e3, 2), "tflops": round(tf, 1)}
+        best["frac_of_2500"] = round(best["tflops"] / PEAK_BF16_TFLOPS, 4)
+        res[label] = best
+        print(f"[ceilings] {label} {best}", file=sys.stderr, flush=True)
     return res
 
 

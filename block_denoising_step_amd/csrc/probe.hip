@@ -57,23 +57,41 @@ __global__ __launch_bounds__(kThreads) void probe_copy(uint4* __restrict__ dst, 
   }
 }
 
-// 8 independent accumulation chains per wave, operands in registers.
-__global__ __launch_bounds__(kThreads) void probe_mfma_bf16(float* __restrict__ sink, int iters) {
-  const float x = (float)(threadIdx.x & 7) * 0.125f;
-  bf16x8 a, b;
+// 8 independent accumulation chains per wave, operands in registers. With `ops`, each
+// lane takes 4 A and 4 B operand vectors from memory and every MFMA of an unrolled
+// group of 4 iterations uses a different (A, B) pair, so the matrix inputs change from
+// instruction to instruction as a GEMM's do; without it, one fixed pair.
+__global__ __launch_bounds__(kThreads) void probe_mfma_bf16(const uint4* __restrict__ ops, float* __restrict__ sink,
+                                                            int iters) {
+  bf16x8 a[4], b[4];
+  if (ops) {
+    const uint4* o = ops + ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(x + 0.0078125f * e);
-    b[e] = (__bf16)(0.5f - 0.0078125f * e);
+    for (int t = 0; t < 4; ++t) {
+      a[t] = __builtin_bit_cast(bf16x8, o[t]);
+      b[t] = __builtin_bit_cast(bf16x8, o[4 + t]);
+    }
+  } else {
+    const float x = (float)(threadIdx.x & 7) * 0.125f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[t][e] = (__bf16)(x + 0.0078125f * e);
+        b[t][e] = (__bf16)(0.5f - 0.0078125f * e);
+      }
   }
   f32x16 acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < iters; it += 4) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(c + u) & 3], b[(3 * c + u) & 3], acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
@@ -106,10 +124,11 @@ int dg_probe_copy(void* dst, const void* src, size_t bytes, int blocks, void* st
   return (int)hipGetLastError();
 }
 
-int dg_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream) {
-  if (!sink || blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return -1;
-  hipLaunchKernelGGL(probe_mfma_bf16, dim3(blocks), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), sink,
-                     iters);
+int dg_probe_mfma_bf16(const void* ops, float* sink, int blocks, int iters, void* stream) {
+  if (!sink || blocks < 1 || blocks > 65536 || iters < 4 || iters > (1 << 24) || iters % 4) return -1;
+  if (ops && !aligned16(ops)) return -1;
+  hipLaunchKernelGGL(probe_mfma_bf16, dim3(blocks), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const uint4*>(ops), sink, iters);
   return (int)hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ def load() -> ctypes.CDLL:
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.dg_probe_read.argtypes = [vp, sz, vp, ctypes.c_int, vp]
     lib.dg_probe_copy.argtypes = [vp, vp, sz, ctypes.c_int, vp]
-    lib.dg_probe_mfma_bf16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.dg_probe_mfma_bf16.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
     for n in EXPORTS:
         getattr(lib, n).restype = ctypes.c_int
     _lib = lib
@@ -51,5 +51,8 @@ def copy(dst: torch.Tensor, src: torch.Tensor, blocks: int, stream=None) -> None
                              _stream(stream)), "dg_probe_copy")
 
 
-def mfma_bf16(sink: torch.Tensor, blocks: int, iters: int, stream=None) -> None:
-    _ok(load().dg_probe_mfma_bf16(sink.data_ptr(), blocks, iters, _stream(stream)), "dg_probe_mfma_bf16")
+def mfma_bf16(sink: torch.Tensor, blocks: int, iters: int, ops: torch.Tensor = None, stream=None) -> None:
+    """ops: [blocks * 256 * 8 * 8] bf16 operands (4 A and 4 B vectors per lane), or None
+    for one fixed operand pair."""
+    _ok(load().dg_probe_mfma_bf16(None if ops is None else ops.data_ptr(), sink.data_ptr(), blocks, iters,
+                                  _stream(stream)), "dg_probe_mfma_bf16")

@@ -9,7 +9,9 @@
  *                   the sampler's logits read or the self-conditioning embedding read;
  *   dg_probe_copy   a copy of `bytes` (read once, written once);
  *   dg_probe_mfma_bf16  back-to-back v_mfma_f32_32x32x16_bf16 on register operands,
- *                   8 independent accumulators per wave, the dense bf16 matrix ceiling.
+ *                   8 independent accumulators per wave, the dense bf16 matrix ceiling;
+ *                   with operands that change from instruction to instruction (as in a
+ *                   GEMM) or one fixed pair.
  *
  * Conventions: device pointers, 16-byte aligned; `bytes` a multiple of 16; every call
  * is asynchronous on `stream` (a hipStream_t, NULL for the default stream). Each returns
@@ -36,10 +38,12 @@ int dg_probe_copy(void* dst, const void* src, size_t bytes, int blocks, void* st
 
 /* `blocks` work groups of 4 waves (one per SIMD of a compute unit when blocks is a
  * multiple of the CU count); each wave issues iters x 8 MFMAs of 32x32x16 (bf16 inputs,
- * fp32 accumulation): 2 * 32 * 32 * 16 * 8 * iters flops per wave. Lane sums of the
- * accumulators go to sink (device [blocks * 256] float). blocks in [1, 65536],
- * iters in [1, 2^24]. */
-int dg_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream);
+ * fp32 accumulation): 2 * 32 * 32 * 16 * 8 * iters flops per wave. ops: device
+ * [blocks * 256][8] 16-byte vectors (per lane 4 A and 4 B operands, bf16; each MFMA of a
+ * group of 4 iterations takes another pair), or NULL for one fixed pair. Lane sums of
+ * the accumulators go to sink (device [blocks * 256] float). blocks in [1, 65536],
+ * iters a multiple of 4 in [4, 2^24]. */
+int dg_probe_mfma_bf16(const void* ops, float* sink, int blocks, int iters, void* stream);
 
 #ifdef __cplusplus
 }

@@ -377,7 +377,8 @@ def test_probe_library_exports_every_declared_function():
     assert lib.dg_probe_read(FAKE, 100, FAKE, 4, None) == -1  # bytes not a multiple of 16
     assert lib.dg_probe_read(FAKE, 1024, FAKE, 0, None) == -1
     assert lib.dg_probe_copy(FAKE, FAKE + 512, 1024, 4, None) == -1  # overlapping ranges
-    assert lib.dg_probe_mfma_bf16(FAKE, 4, 0, None) == -1
+    assert lib.dg_probe_mfma_bf16(None, FAKE, 4, 0, None) == -1
+    assert lib.dg_probe_mfma_bf16(None, FAKE, 4, 6, None) == -1  # not a multiple of 4
 
 
 def test_force_register_staged_hook_round_trips():
