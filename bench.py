@@ -198,7 +198,7 @@ def attn_work(seqs, window, hq, hkv, d, esz, kv_esz=None):
     return 4 * d * hq * pairs, esz * 2 * nq * hq * d + kv_esz * 2 * touched * hkv * d
 
 
-def per_config(path, reps=20, warm=5):
+def per_config(path, reps=20, warm=5, no_oracle=False):
     """Median event time of every call of the five workloads, with each call's
     algorithmic rate and its fraction of the binding roof; written to `path` as JSON."""
     import torch
@@ -410,9 +410,113 @@ def per_config(path, reps=20, warm=5):
     torch.cuda.empty_cache()
     r.update(sampler_and_selfcond(5, True))
     out["configs"]["5"] = r
+    if not no_oracle:
+        torch.cuda.empty_cache()
+        out["oracle"] = oracle_per_config()
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(f"[per-config] wrote {path}", file=sys.stderr, flush=True)
+
+
+def oracle_per_config(rows_per_request=6, cfgs=(1, 2, 3, 4, 5)):
+    """The oracle's time for one step of every workload, on the host cores (BLAS on all
+    of them). Attention is timed on `rows_per_request` query rows per request, spread
+    over the request, and scaled to all its rows by the keys each row sees (the oracle's
+    cost per row is proportional to them); the sampler and self-conditioning run whole."""
+    from oracle.attn import attn_mixed, key_range as o_key_range
+    from oracle.sampler import sampler_step
+    from oracle.selfcond import selfcond_embed
+    from workloads import attn_case, sampler_case, logits as synth_logits, embed_table, request_seeds
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    try:
+        import threadpoolctl
+        ctx = threadpoolctl.threadpool_limits(limits=cores, user_api="blas")
+    except ImportError:  # pragma: no cover
+        ctx = None
+
+    def attn_time(case, window, full):
+        """Seconds for the oracle's attention call: timed whole (full), or per request on
+        one row and on `rows_per_request` rows, fitted as a fixed part (the request's K/V
+        upcast) plus a part proportional to the keys the rows see, and extrapolated."""
+        q, k, v = case.tensors()
+        if full:
+            t0 = time.perf_counter()
+            attn_mixed(case.seqs, window, q, k, v, case.num_q_heads, case.num_kv_heads)
+            return time.perf_counter() - t0, case.total_q
+        est, timed_rows = 0.0, 0
+        for s in case.seqs:
+            if s.num_q == 0:
+                continue
+            nk = np.array([hi - lo + 1 for lo, hi in
+                           (o_key_range(s.mode, s.prefix_len, s.num_q, window, i) for i in range(s.num_q))], np.float64)
+            pick = sorted(set(int(x) for x in np.linspace(0, s.num_q - 1, min(rows_per_request, s.num_q))))
+            ts = []
+            for rows in ([pick[0]], pick):
+                t0 = time.perf_counter()
+                attn_mixed([s], window, q, k, v, case.num_q_heads, case.num_kv_heads, rows=[s.q_start + i for i in rows])
+                ts.append(time.perf_counter() - t0)
+            ka, kb = nk[pick[0]], nk[pick].sum()
+            slope = max(0.0, (ts[1] - ts[0]) / (kb - ka)) if kb > ka else ts[1] / kb
+            fixed = max(0.0, ts[0] - slope * ka)
+            est += fixed + slope * nk.sum()
+            timed_rows += len(pick) + 1
+        return est, timed_rows
+
+    def samp_sc_time(cfg, with_sc):
+        sc = sampler_case(cfg)
+        l = synth_logits(cfg, sc.total_rows, sc.vocab, bf16=sc.bf16)
+        seeds = request_seeds(cfg, len(sc.canvases))
+        reqs, r0 = [], 0
+        for i, n in enumerate(sc.canvases):
+            reqs.append((r0, n, seeds[i], 0))
+            r0 += n
+        M = sc.total_rows
+        t0 = time.perf_counter()
+        sampler_step(l, reqs, sc.vocab, sc.budget, 1, np.zeros(M, np.int64), np.full(M, -1, np.int64),
+                     [0] * len(reqs))
+        ts = time.perf_counter() - t0
+        tsc = 0.0
+        if with_sc:
+            E = embed_table(cfg, sc.vocab, sc.embed_dim, bf16=sc.bf16)
+            t0 = time.perf_counter()
+            selfcond_embed(E, logits=l)
+            tsc = time.perf_counter() - t0
+        return ts, tsc
+
+    res = {"cores": cores, **_blas(), "cpu": _cpu_model(), "configs": {}}
+    for cfg in cfgs:
+        case = attn_case(cfg)
+        parts = {}
+        if cfg == 3:
+            t, n = attn_time(case, 512, True)
+            parts["attn_bidir_w512"] = t
+        elif cfg == 4:
+            t1, n = attn_time(case, -1, False)
+            t2, _ = attn_time(case, 512, False)
+            parts["attn_global_layer"], parts["attn_w512_layer"] = t1, t2
+        else:
+            t, n = attn_time(case, case.window, cfg != 5)
+            parts["attn"] = t
+        if cfg != 3:
+            ts, tsc = samp_sc_time(cfg, cfg != 4)
+            parts["sampler"] = ts
+            if cfg != 4:
+                parts["selfcond"] = tsc
+        total = float(sum(parts.values()))
+        res["configs"][str(cfg)] = {"seconds_per_step": round(total, 3), "steps_per_s": round(1.0 / total, 5),
+                                    "parts_seconds": {k_: round(float(v_), 3) for k_, v_ in parts.items()},
+                                    "attention_rows_timed": int(n)}
+        print(f"[per-config] oracle cfg{cfg}: {res['configs'][str(cfg)]}", file=sys.stderr, flush=True)
+    if ctx is not None:
+        ctx.unregister()
+    res["sample"] = (f"configs 1-3: whole calls; configs 4 and 5: attention per request on 1 and on "
+                     f"{rows_per_request} query rows, fitted as a fixed part plus a part proportional to the keys "
+                     "the rows see and extrapolated to every row; sampler and self-conditioning on every row")
+    return res
 
 
 def measure_ceilings(torch, read_sizes=(134217728, 1208991744, 4294967296), copy_bytes=1073741824,
@@ -731,7 +835,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.per_config:
-        per_config(args.per_config)
+        per_config(args.per_config, no_oracle=args.no_cpu_baseline)
         return
     if args.block_loop:
         block_loop(args.block_loop)
