@@ -677,7 +677,7 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
                                     block_table=table, block_size=block_size) for i in range(2)]
             init_call.args._keep[0].seed = (seed + b) & ((1 << 64) - 1)
             init_call(stream)
-            t, pending = 0, None
+            t = 0
             while True:
                 draft[t % 2](stream)
                 attn[t % 2](stream)
@@ -691,16 +691,11 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
                 sc_call(stream)
                 issued += 1
                 t += 1
-                done = False
-                if pending is not None:  # the previous step's flag, read while this step runs
-                    done = bool(wait_flag(flags, pending))
-                pending = slot
-                if done or t >= STEP_LIMIT:
-                    # the step just issued was speculative; its flag slot is reused two
-                    # steps on, so wait until it has been written
-                    wait_flag(flags, pending)
+                # this step's flag, written by the selection while its self-conditioning
+                # GEMM still has most of the step to run
+                if wait_flag(flags, slot) or t >= STEP_LIMIT:
                     break
-            steps.append(t - 1 if done else t)
+            steps.append(t)
             dg.prepare_kv_write(ck, cv, kp, vp, [(0, CANVAS, 0, prefix)], table, block_size)(stream)
             dg.prepare_attn(cq, kp, vp, out_c, [Seq(0, CANVAS, 0, prefix, CAUSAL)], -1, HQ, HKV,
                             block_table=table, block_size=block_size)(stream)
@@ -718,8 +713,7 @@ def block_loop(path, blocks=8, prompt=PREFIX, block_size=256):
            "committed_tokens_per_s": round(blocks * CANVAS / elapsed, 1),
            "denoise_steps_per_s": round(issued / elapsed, 1),
            "steps_per_block": steps, "steps_issued": issued, "seconds": round(elapsed, 5),
-           "note": "includes the prefill, one speculative step per block, the commit passes and the "
-                   "host's flag reads"}
+           "note": "includes the prefill, the commit passes and the host's flag reads"}
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res), flush=True)
@@ -757,32 +751,26 @@ def graph_steps(path, args, dg, torch, step, seed, flags):
         graphs.append(pair)
     torch.cuda.synchronize()
     t_rec = time.perf_counter() - t_rec
-    state = {"t": 0, "issued": 0, "pending": None, "blocks": 0, "spec": 0}
+    state = {"t": 0, "issued": 0, "blocks": 0, "spec": 0}
 
     def start_block():
         init(stream)
         state["t"] = 0
-        state["pending"] = None
 
     def one_step():
+        """Replay one step and return its converged flag (written by the selection,
+        before the step's self-conditioning)."""
         t = state["t"]
         slot = state["issued"] % 2
         flags[slot] = -1
         graphs[min(t, len(graphs) - 1)][slot][0].replay()
         state["issued"] += 1
         state["t"] = t + 1
-        prev_done = False
-        if state["pending"] is not None:
-            prev_done = bool(wait_flag(flags, state["pending"]))
-        state["pending"] = slot
-        return prev_done
+        return bool(wait_flag(flags, slot))
 
     def run(n):
         for _ in range(n):
-            prev_done = one_step()
-            if prev_done or state["t"] >= STEP_LIMIT:
-                state["spec"] += int(prev_done)
-                wait_flag(flags, state["pending"])
+            if one_step() or state["t"] >= STEP_LIMIT:
                 state["blocks"] += 1
                 start_block()
 
@@ -889,42 +877,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # issued: steps enqueued; spec: speculative steps (the one enqueued after a block's
-    # converging step, before the host has read its flag), whose results are dropped
-    state = {"t": 0, "block": 0, "issued": 0, "spec": 0, "pending": None}
+    # issued: steps enqueued. The host enqueues a step, then waits for that step's
+    # converged flag, which the selection writes midway through the step (before
+    # self-conditioning): the step's GEMM still has most of the step's GPU time to run
+    # while the host enqueues the next step (or starts a new block), so the GPU never
+    # idles and no step is enqueued that a converged block would throw away.
+    state = {"t": 0, "block": 0, "issued": 0, "spec": 0}
 
     def start_block():
         step.start_block(seed + state["block"], stream)
         state["t"] = 0
-        state["pending"] = None
 
     def one_step(ev=None):
-        """Enqueue one step; return the previous step's converged flag. ev: None, or four
-        events (a sample of the timed steps is bracketed by events: each record costs GPU
-        time)."""
+        """Enqueue one step and return its converged flag. ev: None, or four events (a
+        sample of the timed steps is bracketed by events: each record costs GPU time)."""
         t = state["t"]
         slot = state["issued"] % 2
-        flags[slot] = -1  # its last value (two steps back) has been read
+        flags[slot] = -1
         step.enqueue(t, min(t, settle - 1), stream, converged_ptr=flags[slot:slot + 1].data_ptr(), events=ev)
         state["issued"] += 1
         state["t"] = t + 1
-        # the host reads the previous step's flag while this step runs on the GPU
-        prev_done = False
-        if state["pending"] is not None:
-            prev_done = bool(wait_flag(flags, state["pending"]))
-        state["pending"] = slot
-        return prev_done
+        return bool(wait_flag(flags, slot))
 
     def run(n, events=None):
         for s_ in range(n):
-            prev_done = one_step(events[s_] if events is not None else None)
-            if prev_done or state["t"] >= STEP_LIMIT:
-                # converged: the step just issued was speculative (when the flag came from
-                # the step before it). Its flag slot is reused two steps on, so wait until
-                # it has been written before the new block
-                if prev_done:
-                    state["spec"] += 1
-                wait_flag(flags, state["pending"])
+            if one_step(events[s_] if events is not None else None) or state["t"] >= STEP_LIMIT:
                 state["block"] += 1
                 start_block()
 
@@ -995,9 +972,9 @@ def main():
         },
         "steps_issued": args.steps,
         "speculative_steps": spec,
-        "value_note": f"value and ms_per_step count the {useful} useful steps of the {args.steps} timed ones: the "
-                      f"{spec} speculative step(s) enqueued after a converging step, before the host read its flag, "
-                      "ran in the timed region but their results are dropped",
+        "value_note": "every timed step is a useful one: the host reads each step's converged flag as soon as "
+                      "the selection writes it (before the step's self-conditioning), so no step is enqueued past a "
+                      "converged block",
         "roofline": {
             "kernel": "dg_selfcond_embed (selfcond_gemm_dma + selfcond_reduce)",
             "bound": "hbm",
