@@ -372,3 +372,12 @@ def test_max_requests_64():
     for comb in (CONV_AND, CONV_OR):
         _run(l, False, reqs, V, 9.0, prev0=prev, stable0=stable0, combine=comb, tau=2.5,
              label=f"64 requests comb={comb}")
+
+
+def test_vocab_540000_33_chunks():
+    """A vocabulary of 540000 bf16 entries: 33 row-pass chunks, the last one ragged (the
+    finalize merges more chunk statistics than one per lane of its first pass)."""
+    rng = np.random.default_rng(540000)
+    V = 540000
+    l = round_to_bf16((rng.standard_normal((9, V)) * rng.uniform(0.1, 10, (9, 1))).astype(np.float32))
+    _run(l, True, [(0, 5, 31, 2), (6, 3, 32, 0)], V, budget=20.0, label="vocab 540000 (33 chunks)")
