@@ -189,9 +189,15 @@ __global__ __launch_bounds__(kThreads) void sampler_rowpass(const void* __restri
   const int c0 = c * chunk;
   uint4 buf[kLoads];
   if (!kTail) {
+    // non-temporal loads: the logits are read once, and streamed this way they leave the
+    // probabilities this pass writes (which self-conditioning reads next) in the caches
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      buf[i] = *reinterpret_cast<const uint4*>(rowp + ((int64_t)c0 + (i * kThreads + tid) * VT::n) * (kBf16 ? 2 : 4));
+    for (int i = 0; i < kLoads; ++i) {
+      const u32x4 x = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(rowp + ((int64_t)c0 + (i * kThreads + tid) * VT::n) * (kBf16 ? 2 : 4)));
+      buf[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) buf[i] = load_vec<kBf16>(rowp, c0 + (i * kThreads + tid) * VT::n, V);
