@@ -746,19 +746,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
     dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
     dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
   };
-  // one of the 8 DMA instructions of stage j (0..3: K pairs, 4..7: V pairs), in the
-  // same order as issue(); krow / vrow are the pool rows of the stage's first K and V key
-  auto issue_one = [&](int j, int i, int64_t krow, int64_t vrow) {
-    lds_char* st = lds0 + (j & 3) * kAttStage;
-    const bool isk = i < 4;
-    const int t = i & 3;
-    const int kbase = key0 + kSub * (isk ? min(j + 1, nsub - 1) : j);
-    const char* src = (isk ? kb + krow * rs : vb + vrow * rs);
-    lds_char* dst = isk ? st + (4 * wave + t) * kKPitch : st + kKRegion + (4 * wave + t) * kVPitch;
-    const uint32_t off = kbase + kSub <= nkeys ? vo[t]
-                                               : min(2 * (4 * wave + t) + (lane & 1), nkeys - 1 - kbase) * rs + (lane >> 1) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(src + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-  };
 
   // ---- LDS read addresses: per-lane base + immediates
   const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
@@ -835,9 +822,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
       const bool refill = sub + 3 < nsub;   // uniform
       const bool has_next = sub + 1 < nsub;  // uniform
-      // pool rows of the stage refilled below (the K reads' wait also covers a table load)
-      const int64_t krow = key_row<kPaged>(a, sp, key0 + kSub * min(sub + 4, nsub - 1));
-      const int64_t vrow = key_row<kPaged>(a, sp, key0 + kSub * min(sub + 3, nsub - 1));
+      // The refill below (stage sub+3 into the slot of sub-1), addressed once here: row
+      // bases (the K reads' wait also covers a table load), the LDS slot and per-lane
+      // 32-bit offsets, which are vo except in a request's last sub-tile, whose rows past
+      // the last key repeat it.
+      const int kkb = key0 + kSub * min(sub + 4, nsub - 1), vkb = key0 + kSub * min(sub + 3, nsub - 1);
+      const char* rk = kb + key_row<kPaged>(a, sp, kkb) * rs;
+      const char* rv = vb + key_row<kPaged>(a, sp, vkb) * rs;
+      lds_char* rst = lds0 + ((sub + 3) & 3) * kAttStage;
+      uint32_t ko[4], vv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ko[t] = vv[t] = vo[t];
+      if (refill && (kkb + kSub > nkeys || vkb + kSub > nkeys)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 2 * (4 * wave + t) + (lane & 1);
+          ko[t] = (uint32_t)min(r, nkeys - 1 - kkb) * rs + (lane >> 1) * 16;
+          vv[t] = (uint32_t)min(r, nkeys - 1 - vkb) * rs + (lane >> 1) * 16;
+        }
+      }
 
       uint4 kf[KS];
       uint2 v0[DB][2], v1[DB][2];
@@ -867,20 +870,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
 
       // O^T += V^T(keys 0..15) . P^T and S(sub+1) k-steps 8..15, with the V^T reads of
       // keys 16..31, P(sub) of keys 16..31, and the refill of the ring slot of sub-1
-      StaticFor<0, DB>::run([&](auto ic) {
-        constexpr int b = decltype(ic)::value;
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, make_uint4(v0[b][0].x, v0[b][0].y, v0[b][1].x, v0[b][1].y)),
-            __builtin_bit_cast(bf16x8_t, pf[0]), o[b], 0, 0, 0);
-        snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[8 + b]),
-                                                       __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
-        v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
-        v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
-        if (refill) issue_one(sub + 3, b, krow, vrow);
-        p[8 + b] = fast_exp2(fmaf(scur[8 + b], a.scale_log2, -mu));
-        l_run += p[8 + b];
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      {
+        StaticFor<0, DB>::run([&](auto ic) {
+          constexpr int b = decltype(ic)::value;
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, make_uint4(v0[b][0].x, v0[b][0].y, v0[b][1].x, v0[b][1].y)),
+              __builtin_bit_cast(bf16x8_t, pf[0]), o[b], 0, 0, 0);
+          snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[8 + b]),
+                                                         __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
+          v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
+          v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
+          if (refill) {  // DMA b: K pairs 0..3, then V pairs 0..3
+            if constexpr (b < 4)
+              __builtin_amdgcn_global_load_lds((const void*)(rk + ko[b]),
+                                               (__attribute__((address_space(3))) void*)(rst + (4 * wave + b) * kKPitch),
+                                               16, 0, 0);
+            else
+              __builtin_amdgcn_global_load_lds(
+                  (const void*)(rv + vv[b - 4]),
+                  (__attribute__((address_space(3))) void*)(rst + kKRegion + (4 * wave + b - 4) * kVPitch), 16, 0, 0);
+          }
+          p[8 + b] = fast_exp2(fmaf(scur[8 + b], a.scale_log2, -mu));
+          l_run += p[8 + b];
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
       pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
                          pack_bf16(p[14], p[15]));
       DG_ATT_WAIT_LGKM0();
