@@ -610,6 +610,12 @@ constexpr float kOverflow = 64.f;             // log2 headroom of the fixed refe
     __builtin_amdgcn_sched_barrier(0);                               \
   } while (0)
 
+// Empty asm that takes a value: everything computing it stays above this point, so the
+// compiler cannot sink the exps and sums that run under one phase's MFMAs into the next
+// block (past a branch), where they would run with no MFMA beside them.
+#define DG_ATT_ANCHOR(val) asm volatile("" ::"v"(val))
+#define DG_ATT_ANCHOR4(u4) asm volatile("" ::"v"((u4).x), "v"((u4).y), "v"((u4).z), "v"((u4).w))
+
 template <int I, int N>
 struct StaticFor {
   template <class F>
@@ -740,11 +746,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       }
     }
   };
-  // stage j: K of sub-tile j+1 (the last stage repeats sub-tile nsub-1: unused) and V of j
+  // stage j: K of sub-tile j+1 and V of j; stages past the chunk's last sub-tile repeat
+  // it (never read: they keep every iteration's count of copies the same)
   auto issue = [&](int j) {
     lds_char* st = lds0 + (j & 3) * kAttStage;
     dma_rows(kb, st, kKPitch, key0 + kSub * min(j + 1, nsub - 1));
-    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * j);
+    dma_rows(vb, st + kKRegion, kVPitch, key0 + kSub * min(j, nsub - 1));
   };
 
   // ---- LDS read addresses: per-lane base + immediates
@@ -781,11 +788,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
     // ---- prologue: K(0) into the K region of slot 3, stages 0..2, then S(0)
     dma_rows(kb, lds0 + 3 * kAttStage, kKPitch, key0);
     issue(0);
-    if (nsub > 1) issue(1);
-    if (nsub > 2) issue(2);
-    if (nsub > 2) DG_ATT_WAIT_VM(24);
-    else if (nsub > 1) DG_ATT_WAIT_VM(16);
-    else DG_ATT_WAIT_VM(8);
+    issue(1);
+    issue(2);
+    DG_ATT_WAIT_VM(24);  // K(0) landed
     DG_ATT_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     f32x16_t scur;
@@ -811,21 +816,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
 
     bool overflow = false;
     for (int sub = 0; sub < nsub; ++sub) {
-      const int left = nsub - 1 - sub;
-      if (left >= 2) DG_ATT_WAIT_VM(16);
-      else if (left == 1) DG_ATT_WAIT_VM(8);
-      else DG_ATT_WAIT_VM(0);
+      // every iteration (and the prologue, per stage) issues one stage of copies, so two
+      // stages are younger than stage sub here
+      DG_ATT_WAIT_VM(16);
       __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t ka = lbase + (sub & 3) * kAttStage + k_lane;
       const uint32_t va = lbase + (sub & 3) * kAttStage + v_lane;
       const float mu = m_ref == kNegInf ? 0.f : m_ref;
-      const bool refill = sub + 3 < nsub;   // uniform
       const bool has_next = sub + 1 < nsub;  // uniform
-      // The refill below (stage sub+3 into the slot of sub-1), addressed once here: row
-      // bases (the K reads' wait also covers a table load), the LDS slot and per-lane
-      // 32-bit offsets, which are vo except in a request's last sub-tile, whose rows past
-      // the last key repeat it.
+      // The refill below (stage sub+3 into the slot of sub-1; past the last sub-tile it
+      // repeats that sub-tile's rows into the slot, which nothing reads again), addressed
+      // once here: row bases (the K reads' wait also covers a table load), the LDS slot
+      // and per-lane 32-bit offsets, which are vo except in a request's last sub-tile,
+      // whose rows past the last key repeat it.
       const int kkb = key0 + kSub * min(sub + 4, nsub - 1), vkb = key0 + kSub * min(sub + 3, nsub - 1);
       const char* rk = kb + key_row<kPaged>(a, sp, kkb) * rs;
       const char* rv = vb + key_row<kPaged>(a, sp, vkb) * rs;
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       uint32_t ko[4], vv[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) ko[t] = vv[t] = vo[t];
-      if (refill && (kkb + kSub > nkeys || vkb + kSub > nkeys)) {
+      if (kkb + kSub > nkeys || vkb + kSub > nkeys) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 2 * (4 * wave + t) + (lane & 1);
@@ -866,6 +870,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       });
       uint4 pf[2];
       pf[0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      DG_ATT_ANCHOR(l_run);
       DG_ATT_WAIT_LGKM0();
 
       // O^T += V^T(keys 0..15) . P^T and S(sub+1) k-steps 8..15, with the V^T reads of
@@ -880,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
                                                          __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt, 0, 0, 0);
           v1[b][0] = att_tr16<128 * b + 8 * kVPitch>(va);
           v1[b][1] = att_tr16<128 * b + 12 * kVPitch>(va);
-          if (refill) {  // DMA b: K pairs 0..3, then V pairs 0..3
+          {  // DMA b: K pairs 0..3, then V pairs 0..3
             if constexpr (b < 4)
               __builtin_amdgcn_global_load_lds((const void*)(rk + ko[b]),
                                                (__attribute__((address_space(3))) void*)(rst + (4 * wave + b) * kKPitch),
@@ -897,6 +902,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       }
       pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
                          pack_bf16(p[14], p[15]));
+      DG_ATT_ANCHOR4(pf[1]);
+      DG_ATT_ANCHOR(l_run);
       DG_ATT_WAIT_LGKM0();
 
       // O^T += V^T(keys 16..31) . P^T, with the next sub-tile's mask, row max and
@@ -920,7 +927,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
       });
       scur = snxt;
     }
-    // the loop ends with the ring drained; a rare overflow anywhere redoes the chunk
+    // the ring drains (the last stages' repeated copies too) before the barrier below,
+    // after which the LDS is free; a rare overflow anywhere redoes the chunk
+    DG_ATT_WAIT_VM(0);
     if (__any(overflow) && lane == 0) redo_flag[0] = 1;
     __syncthreads();
     const int redo = redo_flag[0];
