@@ -97,7 +97,7 @@ EXPORTS = ["dg_attn_mixed", "dg_attn_workspace_size", "dg_sampler_step", "dg_sam
            "dg_sampler_step_noalloc",
            "dg_selfcond_embed", "dg_selfcond_workspace_size", "dg_kv_write", "dg_selfcond_inject",
            "dg_selfcond_inject_workspace_size", "dg_status_string", "dg_last_error",
-           "dg_abi_version", "dg_test_force_register_staged"]
+           "dg_abi_version", "dg_test_force_register_staged", "dg_test_wide_min_sub"]
 
 _lib = None
 
@@ -144,12 +144,30 @@ def load() -> ctypes.CDLL:
     lib.dg_abi_version.restype = ctypes.c_int
     lib.dg_test_force_register_staged.argtypes = [ctypes.c_int]
     lib.dg_test_force_register_staged.restype = ctypes.c_int
+    lib.dg_test_wide_min_sub.argtypes = [ctypes.c_int]
+    lib.dg_test_wide_min_sub.restype = ctypes.c_int
     if lib.dg_abi_version() != ABI_VERSION:
         # the structs above would not match the library's: refuse rather than pass garbage
         raise RuntimeError(f"{LIB_PATH} has ABI version {lib.dg_abi_version()}, this binding needs {ABI_VERSION}; "
                            "rebuild it")
     _lib = lib
     return lib
+
+
+class wide_min_sub:
+    """Test hook as a context manager: inside it, a bf16 head_dim-256 request runs on the
+    64-rows-per-wave attention kernel from `n` sub-tiles per work group (dg_test_wide_min_sub)."""
+
+    def __init__(self, n: int):
+        self._n = n
+
+    def __enter__(self):
+        self._prev = load().dg_test_wide_min_sub(self._n)
+        return self
+
+    def __exit__(self, *exc):
+        load().dg_test_wide_min_sub(self._prev)
+        return False
 
 
 class force_register_staged:

@@ -18,6 +18,10 @@ thread_local char g_last_error[512] = "";
 // Test hook (dg_test_force_register_staged): plan every request on the register-staged
 // attention kernel.
 std::atomic<int> g_force_register_staged{0};
+// Test hook (dg_test_wide_min_sub): the sub-tiles per work group from which a request runs
+// on the 64-rows-per-wave attention kernel.
+constexpr int kWideMinSubDefault = 64;
+std::atomic<int> g_wide_min_sub{kWideMinSubDefault};
 
 dg_status fail(dg_status s, const char* msg) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
@@ -59,7 +63,6 @@ void clear_error() { g_last_error[0] = 0; }
 static constexpr int kKeyTile = kAttnKeyTile;
 static constexpr int kTargetGroups = 256;
 static constexpr int kMinChunkTiles = 4;
-static constexpr int kWideMinSub = 16;
 
 dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   auto bad = [&](dg_status s, const char* m) { *msg = m; return s; };
@@ -167,9 +170,12 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     r.sub_tiles = units * (kKeyTile / 32);  // 32-key sub-tiles over all (q tile, kv head) units
     return r;
   };
-  // The 64-rows-per-wave kernel has the faster loop but the larger fixed cost (prologue,
-  // epilogue, twice the rows per work group): it takes a request whose work groups
-  // average at least kWideMinSub sub-tiles.
+  // The 64-rows-per-wave kernel reads each K/V byte into LDS for twice the rows, but has
+  // the larger fixed cost (prologue, epilogue, twice the rows per work group) and, per
+  // row, a loop no faster than the 128-row kernel's: it takes a request whose work
+  // groups average at least kWideMinSubDefault sub-tiles (measured: a 16384-key denoise
+  // request runs faster on the 128-row kernel, a 262144-key one on this one).
+  const int64_t wide_min_sub = g_wide_min_sub.load(std::memory_order_relaxed);
   bool wide[DG_MAX_SEQS];
   Split sq[DG_MAX_SEQS];
   for (int s = 0; s < a->num_seqs; ++s) {
@@ -178,7 +184,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
     if (dma[s] && q.num_q > 0) {
       const Split w = split(q, kAttnWideTileRows);
       const int64_t groups = w.ntiles_q * w.nch * a->num_kv_heads;
-      wide[s] = groups > 0 && w.sub_tiles >= kWideMinSub * groups;
+      wide[s] = groups > 0 && w.sub_tiles >= wide_min_sub * groups;
       if (wide[s]) sq[s] = w;
     }
     if (!wide[s]) sq[s] = split(q, kAttnTileRows);
@@ -483,6 +489,7 @@ const char* dg_last_error(void) { return g_last_error; }
 int dg_abi_version(void) { return DG_ABI_VERSION; }
 
 int dg_test_force_register_staged(int on) { return g_force_register_staged.exchange(on != 0); }
+int dg_test_wide_min_sub(int n) { return g_wide_min_sub.exchange(n >= 1 ? n : kWideMinSubDefault); }
 
 size_t dg_attn_workspace_size(const dg_attn_args* a) {
   AttnPlan plan;

@@ -390,6 +390,15 @@ def test_force_register_staged_hook_round_trips():
     assert lib.dg_test_force_register_staged(0) == 0
 
 
+def test_wide_min_sub_hook_round_trips():
+    lib = dg.load()
+    assert lib.dg_test_wide_min_sub(16) == 64
+    assert lib.dg_test_wide_min_sub(0) == 16  # < 1: back to the default
+    with dg.wide_min_sub(8):
+        assert lib.dg_test_wide_min_sub(8) == 8
+    assert lib.dg_test_wide_min_sub(64) == 64
+
+
 def test_sampler_noalloc_validation_before_any_launch():
     """dg_sampler_step_noalloc validates like dg_sampler_step (its workspace fields are
     ignored) and refuses a call that needs more than its static scratch, before any HIP

@@ -149,9 +149,10 @@ def test_score_jump_far_past_first_tile(D, bf16):
         _compare(seqs, -1, q, k, v, H, H, bf16, kv_chunk=chunk, scale=1.0, label=f"score jump D={D}")
 
 
-# Requests long enough, with chunks long enough, that the planner runs them on the
-# 64-rows-per-wave kernel (work groups averaging at least 16 sub-tiles): masks, windows,
-# group sizes, ragged q tiles, 256-row partials and the merge over them.
+# The 64-rows-per-wave kernel at small shapes: with the planner's threshold lowered to 16
+# sub-tiles per work group (test hook), these requests and chunks run on it: masks,
+# windows, group sizes, ragged q tiles, 256-row partials and the merge over them.
+WIDE_MIN_SUB = 16
 WIDE_CASES = [
     # mode, window, G, N, kv_chunk
     (BIDIR, -1, 2, 200, 1024),
@@ -176,7 +177,8 @@ def test_wide_kernel_cases(mode, window, G, N, chunk):
     k = normal(seed + 1, (P + N, hkv, D), bf16=True)
     v = normal(seed + 2, (P + N, hkv, D), bf16=True)
     seqs = pack_seqs([(P, N, mode)])
-    _compare(seqs, window, q, k, v, hq, hkv, True, kv_chunk=chunk, label=f"wide mode={mode} G={G} N={N}")
+    with dg.wide_min_sub(WIDE_MIN_SUB):
+        _compare(seqs, window, q, k, v, hq, hkv, True, kv_chunk=chunk, label=f"wide mode={mode} G={G} N={N}")
 
 
 def test_wide_kernel_score_jump():
@@ -190,8 +192,9 @@ def test_wide_kernel_score_jump():
     v = rng.standard_normal((P + N, H, D))
     q, k, v = (round_to_bf16(x.astype(np.float32)) for x in (q, k, v))
     seqs = pack_seqs([(P, N, BIDIR)])
-    for chunk in (4096, 1024):
-        _compare(seqs, -1, q, k, v, H, H, True, kv_chunk=chunk, scale=1.0, label=f"wide score jump chunk={chunk}")
+    with dg.wide_min_sub(WIDE_MIN_SUB):
+        for chunk in (4096, 1024):
+            _compare(seqs, -1, q, k, v, H, H, True, kv_chunk=chunk, scale=1.0, label=f"wide score jump chunk={chunk}")
 
 
 # ---- the register-staged kernel at head_dim 256 (bf16) ---------------------------------
