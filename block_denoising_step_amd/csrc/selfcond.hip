@@ -372,11 +372,14 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
 // ---- LDS-DMA kernel (bf16) -------------------------------------------------------
 
 constexpr int kDmaBK = 32;  // k per step
-// Cache policy of the E copies: non-temporal. E is a once-per-call stream (its second
-// reader, the other row tile, runs beside the first on the same XCD); marked this way it
-// displaces less of P, which four column tiles read and the sampler has just written.
-// Measured in the step loop: 268.9 -> 258.1 us per call.
+// Cache policy of the E copies when E is larger than the last-level cache: non-temporal.
+// Such an E is a once-per-call stream (its second reader, the other row tile, runs beside
+// the first on the same XCD); marked this way it displaces less of P, which four column
+// tiles read and the sampler has just written. Measured in the step loop: 268.9 -> 258.1
+// us per call. A smaller E (a weight matrix) keeps the default policy: it is read again
+// and stays cached (non-temporal there measured 45.5 -> 50.8 us for the injection's pair).
 constexpr int kCpolStream = 2;
+constexpr int64_t kStreamMinBytes = 256ll << 20;
 // s_waitcnt with only the vector-memory counter limited (expcnt, lgkmcnt left open).
 #define DG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 // s_waitcnt for all LDS reads of this wave (vmcnt left open).
@@ -432,7 +435,7 @@ struct DmaTile {
   static constexpr int kRowsPerSegB = 1024 / kRowB;    // k rows per B segment (2 or 1)
 };
 
-template <int BN>
+template <int BN, bool kStreamE>
 __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   using T = DmaTile<BN>;
   constexpr int BM = T::BM, kStages = T::kStages, kStageA = T::kStageA, kStageBytes = T::kStageBytes;
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
     for (int t = 0; t < kSegB; ++t)
       __builtin_amdgcn_global_load_lds((const void*)(esrc[t] + s * estep),
                                        (__attribute__((address_space(3))) void*)(st + kStageA + (kSegB * dw + t) * 1024),
-                                       16, 0, kCpolStream);
+                                       16, 0, kStreamE ? kCpolStream : 0);
   };
   constexpr int kGroup = kSegA + kSegB;  // DMA instructions per stage per issuing wave (0 for the others)
 
@@ -789,8 +792,14 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
       g.ldp = a->V;
       g.row_max = g.row_sum = nullptr;
     }
-    if (plan.tile_n == 512) hipLaunchKernelGGL(selfcond_gemm_dma<512>, grid, dim3(kDmaThreads), 0, s, g);
-    else hipLaunchKernelGGL(selfcond_gemm_dma<256>, grid, dim3(kDmaThreads), 0, s, g);
+    const bool stream_e = (int64_t)a->V * a->lde * 2 > kStreamMinBytes;
+    if (plan.tile_n == 512) {
+      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<512, true>), grid, dim3(kDmaThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_dma<512, false>), grid, dim3(kDmaThreads), 0, s, g);
+    } else {
+      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<256, true>), grid, dim3(kDmaThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_dma<256, false>), grid, dim3(kDmaThreads), 0, s, g);
+    }
   } else if (a->dtype == DG_BF16) {
     if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<true, true>), grid, dim3(kThreads), 0, s, g);
     else hipLaunchKernelGGL((selfcond_gemm_reg<true, false>), grid, dim3(kThreads), 0, s, g);
