@@ -1286,8 +1286,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
 
-      // ---- S(sub+1) = K(sub+1) . Q^T, with the refill of the ring slot of sub-1 (free
-      // since the barrier) spread over its first steps
+      // ---- S(sub+1) = K(sub+1) . Q^T (the ring refill was issued at the top of the
+      // sub-tile: spreading it over these steps measured no faster, with more spills)
       if (sub + 1 < nsub) {
         compute_s(ka, [](int) {});
       }
