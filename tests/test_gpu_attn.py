@@ -109,6 +109,25 @@ def test_shapes_ragged_and_split(D, bf16, hq, hkv):
                  label=f"D={D} bf16={bf16} G={hq // hkv}")
 
 
+@pytest.mark.parametrize("chunk", [0, 64, 128, 192])
+def test_short_chunks_ring_edges(chunk):
+    """The 128-row kernel issues one ring stage per sub-tile whatever the chunk's length
+    (stages past its end repeat its last sub-tile, clamped to the request's keys), so every
+    length from one sub-tile up, with ragged last sub-tiles, is checked: key counts 1, 20,
+    32, 33, 64, 65, 100, 129 and 200 (one to seven 32-key sub-tiles), split into chunks of
+    64, 128 or 192 keys, in one batch, against the oracle."""
+    spec = [(0, 1, BIDIR), (10, 10, BIDIR), (0, 32, CAUSAL), (20, 13, BIDIR), (40, 24, CAUSAL),
+            (60, 5, BIDIR), (90, 10, BIDIR), (100, 29, CAUSAL), (150, 50, BIDIR)]
+    seqs = pack_seqs(spec)
+    tq = sum(n for _, n, _ in spec)
+    tk = sum(p + n for p, n, _ in spec)
+    q = normal(7100 + chunk, (tq, 16, 256), bf16=True)
+    k = normal(7101 + chunk, (tk, 8, 256), bf16=True)
+    v = normal(7102 + chunk, (tk, 8, 256), bf16=True)
+    for window in (-1, 24):
+        _compare(seqs, window, q, k, v, 16, 8, True, kv_chunk=chunk, label=f"short chunks chunk={chunk} W={window}")
+
+
 def test_batch_independence_bit_exact():
     """A request's output does not depend on the rest of the batch (work split per request)."""
     c = attn_case(4)

@@ -68,6 +68,8 @@ CASES = [
      256, True, 128, 256),
     ("bf16 d256 mixed global, ragged prefixes", [(1500, 200, BIDIR), (777, 256, CAUSAL), (9000, 33, BIDIR)], -1, 16, 8,
      256, True, 64, 0),
+    ("bf16 d256 short chunks, ring edges", [(0, 1, BIDIR), (20, 13, BIDIR), (60, 5, BIDIR), (100, 29, CAUSAL),
+                                            (150, 50, BIDIR)], -1, 16, 8, 256, True, 64, 64),
 ]
 
 
