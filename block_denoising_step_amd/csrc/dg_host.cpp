@@ -329,9 +329,13 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   plan->dma = a->dtype == DG_BF16 && a->V % 32 == 0;
   // The DMA kernel's 128 x 512 tile spends less of its LDS ring on P (an L2-resident
   // operand shared by the tile's neighbours) and more on E, the stream from HBM.
-  const bool wide = plan->dma && a->d % 512 == 0;
+  // A small unscaled product (a weight matrix, K <= 16384, at most 256 rows) takes a
+  // 256 x 128 tile: every byte of E read by one work group, and twice the work groups of
+  // a 64K-value tile, so that the few K steps of each still fill the GPU.
+  const bool narrow = plan->dma && !scaled && a->M <= 256 && a->V <= 16384 && a->d % 128 == 0;
+  const bool wide = plan->dma && !narrow && a->d % 512 == 0;
   plan->tile_m = wide ? 128 : 256;
-  plan->tile_n = wide ? 512 : 256;
+  plan->tile_n = wide ? 512 : narrow ? 128 : 256;
   plan->tile_k = plan->dma ? 32 : (a->dtype == DG_BF16 ? 64 : 32);
   plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
   plan->n_tiles = (int)ceil_div(a->d, plan->tile_n);

@@ -419,25 +419,25 @@ __device__ __forceinline__ uint32_t a_off(int r, int c) { return r * 64 + ((c ^ 
 constexpr int kDmaThreads = 512;
 constexpr int kDmaIssuers = 4;  // waves that refill the ring (one per SIMD)
 
-template <int BN>
+template <int BM_, int BN_>
 struct DmaTile {
-  static constexpr int BM = 65536 / BN;
-  static constexpr int kWN = BN / 128;                 // waves along N
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int kWN = BN / 128;                 // waves along N (256 x 256 tile)
   static constexpr int kStageA = BM * 64;              // BM rows x 32 bf16
   static constexpr int kRowB = BN * 2;                 // bytes per B k row
   static constexpr int kStageB = kDmaBK * kRowB;
   static constexpr int kStageBytes = kStageA + kStageB;
-  static constexpr int kStages = 163840 / kStageBytes;  // 5 or 4
+  static constexpr int kStages = 163840 / kStageBytes;  // 4, 5 or 6
   // The ring is refilled by the first kDmaIssuers waves (one per SIMD): while one wave
   // of a SIMD issues its copies, the other keeps the matrix core busy.
   static constexpr int kSegA = kStageA / 1024 / kDmaIssuers;  // 1 KB DMA segments per issuing wave
   static constexpr int kSegB = kStageB / 1024 / kDmaIssuers;
-  static constexpr int kRowsPerSegB = 1024 / kRowB;    // k rows per B segment (2 or 1)
+  static constexpr int kRowsPerSegB = 1024 / kRowB;    // k rows per B segment (1, 2 or 4)
 };
 
-template <int BN, bool kStreamE>
+template <int BM_, int BN, bool kStreamE>
 __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
-  using T = DmaTile<BN>;
+  using T = DmaTile<BM_, BN>;
   constexpr int BM = T::BM, kStages = T::kStages, kStageA = T::kStageA, kStageBytes = T::kStageBytes;
   constexpr int kSegA = T::kSegA, kSegB = T::kSegB;
   __shared__ __attribute__((aligned(1024))) char lds[kStages][kStageBytes];
@@ -449,11 +449,14 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   // Wave placement. BN = 512: SIMD s (waves s and s + 4) owns rows 64 (s / 2) .. +63 and
   // columns 256 (s % 2) .. +255; the wave that refills the ring (s) takes the first 96
   // columns and the other the next 160, so the copies the first issues are balanced by
-  // the second's extra MFMAs. BN = 256: every wave a 64 x 128 tile.
+  // the second's extra MFMAs. BN = 256: every wave a 64 x 128 tile. BN = 128 (256 rows,
+  // for small products): every wave a 64 x 64 tile.
   constexpr bool kSplit = BN == 512;
+  constexpr bool kNarrow = BN == 128;
   const int s4 = wave % kDmaIssuers;
-  const int wm = kSplit ? (s4 >> 1) * 64 : (wave / T::kWN) * 64;
-  const int wn = kSplit ? (s4 & 1) * 256 + (wave < kDmaIssuers ? 0 : 96) : (wave % T::kWN) * 128;
+  const int wm = kSplit ? (s4 >> 1) * 64 : kNarrow ? (wave >> 1) * 64 : (wave / T::kWN) * 64;
+  const int wn = kSplit ? (s4 & 1) * 256 + (wave < kDmaIssuers ? 0 : 96)
+                        : kNarrow ? (wave & 1) * 64 : (wave % T::kWN) * 128;
 
   // Per-lane DMA sources. Issuing wave w fills A segments kSegA*w .. and B segments
   // kSegB*w .. (1 KB each, lane i -> bytes 16i .. 16i+15 of the segment); the lane
@@ -476,8 +479,9 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
 #pragma unroll
   for (int t = 0; t < kSegB; ++t) {
     const int seg = kSegB * dw + t;
-    const int kk = seg * T::kRowsPerSegB + (T::kRowsPerSegB == 2 ? (lane >> 5) : 0);  // B k row
-    const int cb = (T::kRowsPerSegB == 2 ? (lane & 31) : lane) ^ swb(kk);
+    constexpr int kLanesPerRow = 64 / T::kRowsPerSegB;  // one 16-byte chunk of a k row per lane
+    const int kk = seg * T::kRowsPerSegB + lane / kLanesPerRow;  // B k row
+    const int cb = (lane % kLanesPerRow) ^ swb(kk);
     const int gcol = min(ti.n0 + cb * 8, g.d - 8);
     esrc[t] = eb + ((int64_t)(ti.k_lo + kk) * g.lde + gcol) * 2;
   }
@@ -568,7 +572,8 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
     for (int t = 0; t < pro; ++t) issue(t);
     if (nsteps > 0) {
       // step 0 has landed once at most the pro-1 groups issued after it remain
-      if (pro == 5) DG_WAIT_VM(kGroup * 4);
+      if (pro == 6) DG_WAIT_VM(kGroup * 5);
+      else if (pro == 5) DG_WAIT_VM(kGroup * 4);
       else if (pro == 4) DG_WAIT_VM(kGroup * 3);
       else if (pro == 3) DG_WAIT_VM(kGroup * 2);
       else if (pro == 2) DG_WAIT_VM(kGroup * 1);
@@ -585,7 +590,8 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
         // step s+1 has landed once at most the groups issued after it (steps s+2 ..
         // min(s+kStages-1, nsteps-1)) remain
         const int after = min(kStages - 2, nsteps - 2 - s);
-        if (after >= 3) DG_WAIT_VM(kGroup * 3);
+        if (after >= 4) DG_WAIT_VM(kGroup * 4);
+        else if (after == 3) DG_WAIT_VM(kGroup * 3);
         else if (after == 2) DG_WAIT_VM(kGroup * 2);
         else if (after == 1) DG_WAIT_VM(kGroup * 1);
         else DG_WAIT_VM(0);
@@ -599,6 +605,8 @@ __global__ __launch_bounds__(kDmaThreads) void selfcond_gemm_dma(GemmArgs g) {
   if constexpr (kSplit) {
     if (wave < kDmaIssuers) run(std::integral_constant<int, 3>{});
     else run(std::integral_constant<int, 5>{});
+  } else if constexpr (kNarrow) {
+    run(std::integral_constant<int, 2>{});
   } else {
     run(std::integral_constant<int, 4>{});
   }
@@ -625,7 +633,7 @@ template <bool kBf16>
 __global__ __launch_bounds__(256) void selfcond_reduce(const void* __restrict__ part_v, int splits, int m_tiles,
                                                        int n_tiles, int tile_m, int tile_n, int M, int d,
                                                        void* __restrict__ out, int64_t ldo) {
-  constexpr int kTile4 = 65536 / 4;  // every tile shape holds 64K values
+  const int kTile4 = tile_m * tile_n / 4;  // float4 groups per tile
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
   if (i >= per_split) return;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(256) void selfcond_reduce_epi(const uint2* __restri
                                                            uint16_t* __restrict__ out, int64_t ldo, int half_tiles,
                                                            const uint16_t* __restrict__ embed,
                                                            const int32_t* __restrict__ tokens, int vocab) {
-  constexpr int kTile4 = 65536 / 4;
+  const int kTile4 = tile_m * tile_n / 4;  // float4 groups per tile
   const int64_t per_split = (int64_t)m_tiles * n_tiles * kTile4;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int64_t i = j;
@@ -794,11 +802,13 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
     }
     const bool stream_e = (int64_t)a->V * a->lde * 2 > kStreamMinBytes;
     if (plan.tile_n == 512) {
-      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<512, true>), grid, dim3(kDmaThreads), 0, s, g);
-      else hipLaunchKernelGGL((selfcond_gemm_dma<512, false>), grid, dim3(kDmaThreads), 0, s, g);
+      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<128, 512, true>), grid, dim3(kDmaThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_dma<128, 512, false>), grid, dim3(kDmaThreads), 0, s, g);
+    } else if (plan.tile_n == 128) {  // small products: E (a weight matrix) stays cached
+      hipLaunchKernelGGL((selfcond_gemm_dma<256, 128, false>), grid, dim3(kDmaThreads), 0, s, g);
     } else {
-      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<256, true>), grid, dim3(kDmaThreads), 0, s, g);
-      else hipLaunchKernelGGL((selfcond_gemm_dma<256, false>), grid, dim3(kDmaThreads), 0, s, g);
+      if (stream_e) hipLaunchKernelGGL((selfcond_gemm_dma<256, 256, true>), grid, dim3(kDmaThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_dma<256, 256, false>), grid, dim3(kDmaThreads), 0, s, g);
     }
   } else if (a->dtype == DG_BF16) {
     if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<true, true>), grid, dim3(kThreads), 0, s, g);
