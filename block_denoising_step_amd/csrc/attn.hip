@@ -643,6 +643,21 @@ __device__ __forceinline__ uint2 att_tr16(uint32_t addr) {
   return r;
 }
 
+// max(a, b, c) in one instruction. fmaxf would also quiet signalling NaNs, which costs
+// an extra instruction per operand on scores the compiler cannot prove canonical.
+__device__ __forceinline__ float att_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max of the 16 entries and m
+__device__ __forceinline__ float att_max16(const f32x16_t& sv, float m) {
+  const float t0 = att_max3(sv[0], sv[1], sv[2]), t1 = att_max3(sv[3], sv[4], sv[5]);
+  const float t2 = att_max3(sv[6], sv[7], sv[8]), t3 = att_max3(sv[9], sv[10], sv[11]);
+  const float t4 = att_max3(sv[12], sv[13], sv[14]);
+  return att_max3(att_max3(t0, t1, t2), att_max3(t3, t4, sv[15]), m);
+}
+
 // Both halves of the wave get f(x[lane % 32], x[lane % 32 + 32]).
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -1141,10 +1156,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       }
     }
   };
-  auto max16 = [](const f32x16_t& sv) {
-    float t = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    return fmaxf(t, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-  };
 
   // S = K(slot) . Q^T for both halves: K fragments four ahead in a 5-slot ring, the
   // half-1 Q fragments kQL..15 from LDS with them; dma(i) runs after step i
@@ -1190,7 +1201,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
     DG_ATT_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     compute_s(lbase + 3 * kAttStage + k_lane, [](int) {});
-    float m_seen[2] = {kNegInf, kNegInf};
+    // Once every row has its reference, the reference no longer changes, so the overflow
+    // test only needs the chunk's largest score: each lane keeps a running max of its raw
+    // scores (m_lane), and the row max, scale and test run once, after the loop.
+    float m_seen[2] = {kNegInf, kNegInf}, m_lane[2] = {kNegInf, kNegInf};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       l_run[h] = 0.f;
@@ -1217,7 +1231,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax of S(sub), keys 0..15 (elements 0..7). Once every row has its
-      // reference, the row max (for the overflow test) waits until the MFMAs run.
+      // reference, only the lanes' running max is kept, under the MFMAs below.
       uint2 vf[3][2];
       auto vread = [&](auto fc) {  // fragment f = 8 kh + b: d block b, key half kh
         constexpr int f = decltype(fc)::value;
@@ -1230,7 +1244,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       mask(sc[0], key0 + kSub * sub, 0);
       mask(sc[1], key0 + kSub * sub, 1);
       auto row_max = [&](int h) {
-        const float t = half_max(max16(sc[h])) * a.scale_log2;
+        const float t = half_max(att_max16(sc[h], kNegInf)) * a.scale_log2;
         m_seen[h] = fmaxf(m_seen[h], t);
         if (m_ref[h] == kNegInf) m_ref[h] = t;  // on a retry m_ref already covers this sub-tile
         overflow |= t > m_ref[h] + kOverflow;
@@ -1257,7 +1271,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- O^T += V(sub)^T . P(sub)^T: 16 fragments (two V^T reads each, two ahead), each
-      // feeding both halves; P of keys 16..31 during the first eight, the late row max next
+      // feeding both halves; P of keys 16..31 during the first eight, the running max next
       float pv[2][8];
       StaticFor<0, 2 * DB>::run([&](auto fc) {
         constexpr int f = decltype(fc)::value;
@@ -1281,7 +1295,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
                                   pack_bf16(pv[h][4], pv[h][5]), pack_bf16(pv[h][6], pv[h][7]));
         }
         if constexpr (f == 8 || f == 9) {
-          if (late_max) row_max(f - 8);
+          if (late_max) m_lane[f - 8] = att_max16(sc[f - 8], m_lane[f - 8]);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -1291,6 +1305,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
       if (sub + 1 < nsub) {
         compute_s(ka, [](int) {});
       }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float t = half_max(m_lane[h]) * a.scale_log2;
+      m_seen[h] = fmaxf(m_seen[h], t);
+      overflow |= t > m_ref[h] + kOverflow;
     }
     if (__any(overflow) && lane == 0) redo_flag[0] = 1;
     __syncthreads();
