@@ -993,6 +993,333 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256(AttnArgs a) {
   }
 }
 
+// ---- FP8 (E4M3) K/V, head_dim 256: the 128-row LDS-DMA kernel over codes ---------
+//
+// attn_fwd_bf16_d256 with the K/V ring holding E4M3 codes: a stage is half the bytes,
+// the copies and the LDS fragment reads halve, and each fragment is widened to bf16
+// after its read (v_cvt_scalef32_pk_bf16_fp8 at scale 1: every E4M3 value is a bf16
+// value, so the widening is exact), feeding the same bf16 MFMAs. k_scale is folded
+// into the score scale and v_scale into the output normalisation.
+//
+// LDS layout: one copy instruction writes 1 KB = 4 key rows of 256 codes, 16-byte chunk
+// c of row r at slot 4c + r; blocks of 4 rows are 1088 B (K) and 1056 B (V) apart.
+// - K operand: one ds_read_b128 per lane and pair of k-steps (16 codes of its key). So
+//   that it feeds both steps, the contraction runs over the head dims in a permuted
+//   order: k-step 2j + u takes dims 32j + 16h + 8u .. +7 in the lane half h (Q's
+//   fragments are loaded in the same order). 8 lanes of a read hit 8 distinct 16-byte
+//   bank groups.
+// - V^T operand: one ds_read_b64_tr_b8 per fragment. In each 16-lane group the read
+//   returns to lane j byte j % 8 of the 8 bytes that lane 2r + j / 8 addressed, as byte
+//   r (r = 0..7). A lane of group g (half h = g / 2) addresses 8 codes of key
+//   (4h + r', then 8 + 4h + r' - 4) at dims 32b + 16 (g % 2) + 8 (lane % 2), which gives
+//   lane (row, h) the codes of its P^T keys in order, at dim 32b + row. The two blocks a
+//   group touches are 2 apart, 64 bytes apart in the banks: no conflicts.
+
+constexpr int kF8KPitch = 1088;                     // bytes between K blocks of 4 rows
+constexpr int kF8VPitch = 1056;                     // bytes between V blocks
+constexpr int kF8KRegion = (kSub / 4) * kF8KPitch;  // 8704
+constexpr int kF8VRegion = (kSub / 4) * kF8VPitch;  // 8448
+constexpr int kF8Stage = kF8KRegion + kF8VRegion;   // 17152; 4 stages = 67 KB
+
+template <int kOff>
+__device__ __forceinline__ uint2 att_tr8(uint32_t addr) {
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff) : "memory");
+  return r;
+}
+// 8 E4M3 codes (bytes of lo, then hi) -> 8 bf16, in order
+__device__ __forceinline__ uint4 widen_e4m3(uint32_t lo, uint32_t hi) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)));
+}
+
+template <bool kPaged>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_d256(AttnArgs a) {
+  constexpr int D = 256, KS = 16, DB = 8;
+  __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kF8Stage];
+  __shared__ int redo_flag[1];
+
+  const int w = a.work_offset + xcd_order(blockIdx.x, gridDim.x);
+  const int s_ = find_seq(a, w, false);
+  const AttnSeqPlan sp = a.seqs[s_];
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
+  const int local = w - sp.work_begin;
+  const int qt = sp.mode == DG_CAUSAL ? nqt - 1 - local % nqt : local % nqt;
+  const int rest = local / nqt;
+  const int g = rest % a.hkv;
+  const int chunk = rest / a.hkv;
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
+  const int nkeys = sp.prefix_len + sp.num_q;
+  int lo_first, hi_first, lo_last, hi_last;
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0 + nq - 1, lo_last, hi_last);
+  const int kt_lo = lo_first / kKT, kt_hi = hi_last / kKT;
+  const int t_begin = kt_lo + chunk * sp.chunk_tiles;
+  const int t_end = min(kt_hi + 1, t_begin + sp.chunk_tiles);
+  if (t_begin > kt_hi) return;  // empty chunk (uniform across the work group)
+  const int key0 = t_begin * kKT;
+  const int kend = min(t_end * kKT, hi_last + 1);
+  const int nsub = (kend - key0 + kSub - 1) / kSub;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int row = wave * 32 + l32;
+  const int tok = i0 + row / a.group;
+  const int head = g * a.group + row % a.group;
+  const bool valid = tok < sp.num_q;
+  int lo = 0, hi = -1;
+  if (valid) key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, tok, lo, hi);
+
+  // Q^T fragments in the permuted dim order of the K reads
+  uint4 qf[KS];
+  {
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + (32 * (ks >> 1) + 16 * hh + 8 * (ks & 1)) * 2)
+                     : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- DMA: wave w fills blocks 2w, 2w+1 of the K and V regions; lane i loads chunk
+  // i/4 of key row 4*block + i%4
+  const int rs = a.hkv * D;  // bytes between consecutive keys
+  const int64_t head_off = (int64_t)g * D;
+  const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
+  uint32_t vo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) vo[u] = (4 * (2 * wave + u) + (lane & 3)) * rs + (lane >> 2) * 16;
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* lds0 = (lds_char*)lds;
+  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase) {
+    const char* src = base + key_row<kPaged>(a, sp, kbase) * rs;
+    const int last = nkeys - 1 - kbase;  // rows past the request's last key repeat it (masked)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t off =
+          kbase + kSub <= nkeys ? vo[u] : (uint32_t)min(4 * (2 * wave + u) + (lane & 3), last) * rs + (lane >> 2) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                       (__attribute__((address_space(3))) void*)(dst + (2 * wave + u) * pitch), 16, 0, 0);
+    }
+  };
+  // stage j: K of sub-tile j+1 and V of j (past the chunk's last sub-tile: repeats)
+  auto issue = [&](int j) {
+    lds_char* st = lds0 + (j & 3) * kF8Stage;
+    dma_rows(kb, st, kF8KPitch, key0 + kSub * min(j + 1, nsub - 1));
+    dma_rows(vb, st + kF8KRegion, kF8VPitch, key0 + kSub * min(j, nsub - 1));
+  };
+
+  // ---- LDS read addresses: per-lane base + immediates
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
+  const uint32_t k_lane = (l32 >> 2) * kF8KPitch + 16 * (l32 & 3) + 64 * hh;  // + 128 j
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int kr = (s16 >> 1) < 4 ? 4 * (grp >> 1) + (s16 >> 1) : 8 + 4 * (grp >> 1) + (s16 >> 1) - 4;  // key 0..15
+  const uint32_t v_lane =
+      kF8KRegion + (kr >> 2) * kF8VPitch + 16 * (kr & 3) + 64 * (grp & 1) + 8 * (s16 & 1);  // + 128 b + 4 kh V blocks
+
+  auto mask = [&](f32x16_t& sv, int kbase) {
+    if (!(lo_last <= kbase && kbase + kSub - 1 <= hi_first)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (key < lo || key > hi) sv[e] = kNegInf;
+      }
+    }
+  };
+  auto front = [&](f32x16_t& sv, int kbase) {
+    mask(sv, kbase);
+    float t = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    t = fmaxf(t, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    return half_max(t) * a.scale_log2;
+  };
+  // bf16 operand of k-step ks from the K read of its pair
+  auto kop = [](const uint4& k, int u) { return u == 0 ? widen_e4m3(k.x, k.y) : widen_e4m3(k.z, k.w); };
+
+  f32x16_t o[DB];
+  float l_run;
+  float m_ref = kNegInf;
+  for (;;) {
+    if (tid == 0) redo_flag[0] = 0;
+    // ---- prologue: K(0) into the K region of slot 3, stages 0..2, then S(0)
+    dma_rows(kb, lds0 + 3 * kF8Stage, kF8KPitch, key0);
+    issue(0);
+    issue(1);
+    issue(2);
+    DG_ATT_WAIT_VM(12);  // K(0) landed
+    DG_ATT_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    f32x16_t scur;
+    {
+      const uint32_t ka = lbase + 3 * kF8Stage + k_lane;
+      uint4 k8[KS / 2];
+      StaticFor<0, KS / 2>::run([&](auto j) { k8[j] = att_b128<128 * decltype(j)::value>(ka); });
+      DG_ATT_WAIT_LGKM0();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) scur[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        scur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop(k8[ks >> 1], ks & 1)),
+                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), scur, 0, 0, 0);
+    }
+    float m_seen = front(scur, key0);
+    if (m_ref == kNegInf) m_ref = m_seen;  // on a retry m_ref already covers this sub-tile
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+    l_run = 0.f;
+
+    bool overflow = false;
+    for (int sub = 0; sub < nsub; ++sub) {
+      // one stage of copies per iteration (and per prologue stage): two stages are
+      // younger than stage sub here
+      DG_ATT_WAIT_VM(8);
+      __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t ka = lbase + (sub & 3) * kF8Stage + k_lane;
+      const uint32_t va = lbase + (sub & 3) * kF8Stage + v_lane;
+      const float mu = m_ref == kNegInf ? 0.f : m_ref;
+      const bool has_next = sub + 1 < nsub;  // uniform
+      // refill of stage sub+3 into the slot of sub-1, addressed once here
+      const int kkb = key0 + kSub * min(sub + 4, nsub - 1), vkb = key0 + kSub * min(sub + 3, nsub - 1);
+      const char* rk = kb + key_row<kPaged>(a, sp, kkb) * rs;
+      const char* rv = vb + key_row<kPaged>(a, sp, vkb) * rs;
+      lds_char* rst = lds0 + ((sub + 3) & 3) * kF8Stage;
+      uint32_t ko[2], vv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) ko[u] = vv[u] = vo[u];
+      if (kkb + kSub > nkeys || vkb + kSub > nkeys) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 4 * (2 * wave + u) + (lane & 3);
+          ko[u] = (uint32_t)min(r, nkeys - 1 - kkb) * rs + (lane >> 2) * 16;
+          vv[u] = (uint32_t)min(r, nkeys - 1 - vkb) * rs + (lane >> 2) * 16;
+        }
+      }
+
+      uint4 k8[KS / 2];
+      uint2 v0[DB], v1[DB];
+      StaticFor<0, 4>::run([&](auto j) { k8[j] = att_b128<128 * decltype(j)::value>(ka); });
+      DG_ATT_WAIT_LGKM0();
+
+      // S(sub+1) k-steps 0..7 with K reads of pairs 4..7, the V^T reads of keys 0..15
+      // and P(sub) of keys 0..15
+      f32x16_t snxt;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) snxt[e] = 0.f;
+      float p[16];
+      StaticFor<0, 8>::run([&](auto ic) {
+        constexpr int ks = decltype(ic)::value;
+        snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kop(k8[ks >> 1], ks & 1)),
+                                                       __builtin_bit_cast(bf16x8_t, qf[ks]), snxt, 0, 0, 0);
+        if constexpr ((ks & 1) == 0) k8[4 + (ks >> 1)] = att_b128<128 * (4 + (ks >> 1))>(ka);
+        v0[ks] = att_tr8<128 * ks>(va);
+        p[ks] = fast_exp2(fmaf(scur[ks], a.scale_log2, -mu));
+        l_run += p[ks];
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      uint4 pf[2];
+      pf[0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      DG_ATT_ANCHOR(l_run);
+      DG_ATT_WAIT_LGKM0();
+
+      // O^T += V^T(keys 0..15) . P^T and S(sub+1) k-steps 8..15, with the V^T reads of
+      // keys 16..31, P(sub) of keys 16..31, and the refill of the ring slot of sub-1
+      StaticFor<0, DB>::run([&](auto ic) {
+        constexpr int b = decltype(ic)::value;
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, widen_e4m3(v0[b].x, v0[b].y)),
+                                                       __builtin_bit_cast(bf16x8_t, pf[0]), o[b], 0, 0, 0);
+        snxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, kop(k8[4 + (b >> 1)], b & 1)), __builtin_bit_cast(bf16x8_t, qf[8 + b]), snxt,
+            0, 0, 0);
+        v1[b] = att_tr8<128 * b + 4 * kF8VPitch>(va);
+        if constexpr (b < 2)
+          __builtin_amdgcn_global_load_lds((const void*)(rk + ko[b]),
+                                           (__attribute__((address_space(3))) void*)(rst + (2 * wave + b) * kF8KPitch),
+                                           16, 0, 0);
+        else if constexpr (b < 4)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(rv + vv[b - 2]),
+              (__attribute__((address_space(3))) void*)(rst + kF8KRegion + (2 * wave + b - 2) * kF8VPitch), 16, 0, 0);
+        p[8 + b] = fast_exp2(fmaf(scur[8 + b], a.scale_log2, -mu));
+        l_run += p[8 + b];
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      pf[1] = make_uint4(pack_bf16(p[8], p[9]), pack_bf16(p[10], p[11]), pack_bf16(p[12], p[13]),
+                         pack_bf16(p[14], p[15]));
+      DG_ATT_ANCHOR4(pf[1]);
+      DG_ATT_ANCHOR(l_run);
+      DG_ATT_WAIT_LGKM0();
+
+      // O^T += V^T(keys 16..31) . P^T, with the next sub-tile's mask, row max and
+      // reference between the MFMAs
+      if (has_next) mask(snxt, key0 + kSub * (sub + 1));
+      float t4[4], tmax = kNegInf;
+      StaticFor<0, DB>::run([&](auto ic) {
+        constexpr int b = decltype(ic)::value;
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, widen_e4m3(v1[b].x, v1[b].y)),
+                                                       __builtin_bit_cast(bf16x8_t, pf[1]), o[b], 0, 0, 0);
+        if constexpr (b < 4) t4[b] = fmaxf(fmaxf(snxt[4 * b], snxt[4 * b + 1]), fmaxf(snxt[4 * b + 2], snxt[4 * b + 3]));
+        if (b == 4) tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        if (b == 5) tmax = half_max(tmax) * a.scale_log2;
+        if (b == 6 && has_next) {
+          m_seen = fmaxf(m_seen, tmax);
+          if (m_ref == kNegInf) m_ref = tmax;
+          overflow |= tmax > m_ref + kOverflow;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      scur = snxt;
+    }
+    DG_ATT_WAIT_VM(0);
+    if (__any(overflow) && lane == 0) redo_flag[0] = 1;
+    __syncthreads();
+    const int redo = redo_flag[0];
+    if (!redo) break;
+    __syncthreads();  // every wave has read the flag before it is cleared
+    m_ref = fmaxf(m_ref, m_seen);
+  }
+
+  // ---- epilogue (as attn_fwd_bf16_d256, with v_scale in the normalisation)
+  constexpr int kOPitch = 528;
+  char* ost = lds + wave * 32 * kOPitch;
+  const float l_tot = half_sum(l_run);
+  {
+    const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * a.v_scale;
+    char* orow = ost + l32 * kOPitch;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<uint2*>(orow + (32 * b + 8 * e4 + 4 * hh) * 2) =
+            make_uint2(pack_bf16(o[b][4 * e4] * inv, o[b][4 * e4 + 1] * inv),
+                       pack_bf16(o[b][4 * e4 + 2] * inv, o[b][4 * e4 + 3] * inv));
+  }
+  const int64_t prow0 = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kRows;
+  if (valid && hh == 0) {
+    if (sp.num_chunks > 1)
+      *reinterpret_cast<float2*>(a.part_ml + (prow0 + row) * 2) = make_float2(m_ref, l_tot);
+    else if (a.lse)
+      a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+  DG_ATT_WAIT_LGKM0();
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const int lr = 2 * r + hh;
+    const int srow = wave * 32 + lr, stok = i0 + srow / a.group, shead = g * a.group + srow % a.group;
+    const uint4 x = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + l32 * 16);
+    if (stok >= sp.num_q) continue;
+    char* dst = sp.num_chunks == 1
+                    ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + stok) * a.hq + shead) * D * 2
+                    : reinterpret_cast<char*>(a.part_o) + (prow0 + srow) * D * 2;
+    *reinterpret_cast<uint4*>(dst + l32 * 16) = x;
+  }
+}
+
 // ---- bf16, head_dim 256, 64 query rows per wave ---------------------------------
 //
 // The ring, LDS layout and copies of attn_fwd_bf16_d256, with each wave owning 64
@@ -1390,12 +1717,20 @@ int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-// FP8 K/V: the register-staged kernel at bf16, then the merge of bf16 partials
+// FP8 K/V: work [0, num_dma) on the LDS-DMA kernel over codes (head_dim 256), the rest
+// on the register-staged kernel at bf16, then the merge of bf16 partials
 template <int D, bool kPaged>
 int launch_fp8(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
-  if (plan.num_work > 0) {
-    args.work_offset = 0;
-    hipLaunchKernelGGL((attn_fwd<true, D, kPaged, true>), dim3(plan.num_work), dim3(kThreads), 0, s, args);
+  if constexpr (D == 256) {
+    if (plan.num_dma > 0) {
+      args.work_offset = 0;
+      hipLaunchKernelGGL(attn_fwd_fp8_d256<kPaged>, dim3(plan.num_dma), dim3(kThreads), 0, s, args);
+    }
+  }
+  if (plan.num_work > plan.num_dma) {
+    args.work_offset = plan.num_dma;
+    hipLaunchKernelGGL((attn_fwd<true, D, kPaged, true>), dim3(plan.num_work - plan.num_dma), dim3(kThreads), 0, s,
+                       args);
   }
   if (plan.num_merge > 0) hipLaunchKernelGGL((attn_merge<true, D>), dim3(plan.num_merge), dim3(kThreads), 0, s, args);
   return (int)hipGetLastError();

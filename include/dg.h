@@ -389,9 +389,9 @@ int dg_abi_version(void);                  /* DG_ABI_VERSION */
 
 /* Test hook, not for production use. With on != 0, every later dg_attn_mixed call (from
  * any thread) plans all its requests on the register-staged attention kernel, the one
- * that otherwise serves head_dim 64/128, fp32, FP8 K/V and contiguous bf16 head_dim-256
- * requests whose K/V span passes 2^31 - 1 bytes; results stay within the same bars, not
- * bit-equal to the LDS-DMA kernels. on = 0 restores the normal per-request choice.
+ * that otherwise serves head_dim 64/128, fp32, FP8 K/V at head_dim 64/128, and contiguous
+ * head_dim-256 requests whose K/V span passes 2^31 - 1 bytes; results stay within the
+ * same bars, not bit-equal to the LDS-DMA kernels. on = 0 restores the normal per-request choice.
  * Returns the previous setting (0 or 1). */
 int dg_test_force_register_staged(int on);
 

@@ -3,9 +3,11 @@ kv_fp8 = 1 and dg_kv_write into FP8 pools.
 
 Bar:
 - every E4M3 code widens exactly: attention over one key returns v_scale times the
-  decoded V row, bit for bit (a power-of-two v_scale keeps the product exact);
+  decoded V row, bit for bit (a power-of-two v_scale keeps the product exact), on the
+  register-staged kernel (head_dim 64) and on the LDS-DMA kernel over codes (256);
 - with unit scales, FP8 attention equals bf16 attention on the decoded values bit for
-  bit (the same kernel after the tile is staged);
+  bit at head_dim 64/128 (the same register-staged kernel after the tile is staged; at
+  256 the codes run on their own kernel, whose contraction order differs);
 - against the oracle on the dequantized inputs: max-relative error per row <= 2e-2
   and lse within 1e-3, the bf16 path's bar (contiguous and paged, head_dim 64/128/256,
   grouped heads, windows, both modes, split-KV chunks);
@@ -43,14 +45,16 @@ def _fp8_kv(seed, shape, scale):
     return _CODES[key]
 
 
-def test_every_code_widens_exactly():
-    # V rows hold all 254 non-NaN codes (the two NaN codes replaced by +-1)
+@pytest.mark.parametrize("D", [64, 256])
+def test_every_code_widens_exactly(D):
+    # V rows hold all 254 non-NaN codes (the two NaN codes replaced by +-1); at head_dim
+    # 256 (the LDS-DMA kernel over codes) each of the 4 rows is the code list rotated by
+    # 64, so every code passes through 4 different dims (lanes and fragments)
     codes = np.arange(256, dtype=np.uint8)
     codes[0x7F], codes[0xFF] = 0x38, 0xB8
-    D = 64
-    v = codes.reshape(4, 1, D)
+    v = codes.reshape(4, 1, D) if D == 64 else np.stack([np.roll(codes, 64 * r) for r in range(4)]).reshape(4, 1, D)
     k = np.full_like(v, 0x38)
-    q = normal(401, (4, 1, D), bf16=True)
+    q = normal(401 + D, (4, 1, D), bf16=True)
     seqs = [Seq(i, 1, i, 0, BIDIR) for i in range(4)]
     for vs in (1.0, 0.125):
         out = torch.empty(4, 1, D, device=DEV, dtype=torch.bfloat16)
@@ -98,6 +102,12 @@ CASES = [
      8, 8, 128, 0, 0.5, 0.25),
     ("d64 edges: empty, one-token, global", [(50, 0, BIDIR), (0, 1, BIDIR), (0, 1, CAUSAL), (129, 65, BIDIR)], -1,
      2, 1, 64, 64, 0.07, 0.09),
+    # head_dim 256 on the LDS-DMA kernel over codes: chunks of 1 to 7 sub-tiles with ragged
+    # last sub-tiles (the ring's repeated rows), one-token and empty requests, a window
+    ("d256 short chunks, ragged tails", [(37, 29, CAUSAL), (100, 61, BIDIR), (0, 33, BIDIR), (200, 1, BIDIR),
+                                         (10, 0, CAUSAL)], -1, 8, 2, 256, 64, 0.02, 0.03),
+    ("d256 W=40 chunks of 192 keys", [(300, 70, CAUSAL), (5, 130, BIDIR)], 40, 16, 8, 256, 192, 0.011, 0.017),
+    ("d256 G=8 one q tile, long prefix", [(3000, 16, BIDIR)], -1, 16, 2, 256, 0, 1 / 64, 1 / 64),
 ]
 
 
