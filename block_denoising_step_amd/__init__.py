@@ -155,8 +155,9 @@ def load() -> ctypes.CDLL:
 
 
 class wide_min_sub:
-    """Test hook as a context manager: inside it, a bf16 head_dim-256 request runs on the
-    64-rows-per-wave attention kernel from `n` sub-tiles per work group (dg_test_wide_min_sub)."""
+    """Test hook as a context manager: inside it, a head_dim-256 request (bf16 or FP8 K/V)
+    runs on a 64-rows-per-wave attention kernel from `n` sub-tiles per work group
+    (dg_test_wide_min_sub)."""
 
     def __init__(self, n: int):
         self._n = n

@@ -1695,6 +1695,360 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_d256_w64(AttnArgs a) {
   }
 }
 
+// ---- FP8 (E4M3) K/V, head_dim 256, 64 query rows per wave -------------------------
+//
+// attn_fwd_bf16_d256_w64 over the code ring of attn_fwd_fp8_d256 (same layout, copies
+// and fragment reads, same permuted contraction order). The smaller ring leaves room in
+// LDS for k-steps kF8QL..15 of the second half's Q^T fragments. S's K operands are
+// widened one k-step ahead, so that no vector write of an asm MFMA's operand comes right
+// before it. The epilogue stages O one 32-row half at a time (the ring is smaller than
+// the 64 rows per wave).
+
+constexpr int kF8QL = 8;  // second-half Q^T k-steps kept in VGPRs; the rest in LDS
+
+// lgkmcnt of k-step ks in the S phase below. Reads are issued in this order: K pairs 0, 1
+// and 2 before step 0; after step i, the second half's Q fragment of step i + 4 when it
+// comes from LDS (i + 4 >= kF8QL), and after odd i, K pair (i + 5) / 2. Step ks waits for
+// its Q fragment (from LDS) and for the K pair of step ks + 2, which is widened after its
+// MFMAs.
+constexpr int f8w_wait(int ks) {
+  int pos_k[8] = {}, pos_q[16] = {}, before[16] = {};
+  int n = 0;
+  pos_k[0] = n++;
+  pos_k[1] = n++;
+  pos_k[2] = n++;
+  for (int i = 0; i < 16; ++i) {
+    before[i] = n;
+    if (i + 4 < 16 && i + 4 >= kF8QL) pos_q[i + 4] = n++;
+    if ((i & 1) && (i + 5) / 2 <= 7) pos_k[(i + 5) / 2] = n++;
+  }
+  int need = -1;
+  if (ks >= kF8QL) need = pos_q[ks];
+  if (ks + 2 < 16 && pos_k[(ks + 2) / 2] > need) need = pos_k[(ks + 2) / 2];
+  return before[ks] - 1 - need;
+}
+static_assert(f8w_wait(0) == 1 && f8w_wait(6) == 3 && f8w_wait(7) == 4 && f8w_wait(15) == 0, "read schedule");
+
+template <bool kPaged>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_d256_w64(AttnArgs a) {
+  constexpr int D = 256, KS = 16, DB = 8, kTile = 256;
+  __shared__ __attribute__((aligned(1024))) char lds[kAttStages * kF8Stage];
+  __shared__ int redo_flag[1];
+  __shared__ __attribute__((aligned(16))) char qlds[4 * (KS - kF8QL) * 1024];
+
+  const int w = a.work_offset + xcd_order(blockIdx.x, gridDim.x);
+  const int s_ = find_seq(a, w, false);
+  const AttnSeqPlan sp = a.seqs[s_];
+  const int nqt = (sp.num_q + sp.tokens_per_tile - 1) / sp.tokens_per_tile;
+  const int local = w - sp.work_begin;
+  const int qt = sp.mode == DG_CAUSAL ? nqt - 1 - local % nqt : local % nqt;
+  const int rest = local / nqt;
+  const int g = rest % a.hkv;
+  const int chunk = rest / a.hkv;
+  const int i0 = qt * sp.tokens_per_tile;
+  const int nq = min(sp.tokens_per_tile, sp.num_q - i0);
+  const int nkeys = sp.prefix_len + sp.num_q;
+  int lo_first, hi_first, lo_last, hi_last;
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0, lo_first, hi_first);
+  key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, i0 + nq - 1, lo_last, hi_last);
+  const int kt_lo = lo_first / kKT, kt_hi = hi_last / kKT;
+  const int t_begin = kt_lo + chunk * sp.chunk_tiles;
+  const int t_end = min(kt_hi + 1, t_begin + sp.chunk_tiles);
+  if (t_begin > kt_hi) return;
+  const int key0 = t_begin * kKT;
+  const int kend = min(t_end * kKT, hi_last + 1);
+  const int nsub = (kend - key0 + kSub - 1) / kSub;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  auto row_of = [&](int h) { return wave * 64 + 32 * h + l32; };
+  int lo[2], hi[2];
+  uint4 qf0[KS], qf1[kF8QL];  // Q^T fragments in the permuted dim order of the K reads
+  const uint32_t q_lds =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)qlds + wave * (KS - kF8QL) * 1024 + lane * 16;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tok = i0 + row_of(h) / a.group, head = g * a.group + row_of(h) % a.group;
+    lo[h] = 0;
+    hi[h] = -1;
+    if (tok < sp.num_q) key_bounds(sp.mode, sp.prefix_len, sp.num_q, a.window, tok, lo[h], hi[h]);
+    // rows past the request read its last token (their outputs are never stored)
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)(sp.q_start + min(tok, sp.num_q - 1)) * a.hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow + (32 * (ks >> 1) + 16 * hh + 8 * (ks & 1)) * 2);
+      if (h == 0) {
+        qf0[ks] = x;
+      } else if (ks < kF8QL) {
+        qf1[ks] = x;
+      } else {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t xv = {x.x, x.y, x.z, x.w};
+        asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(q_lds), "v"(xv), "i"((ks - kF8QL) * 1024) : "memory");
+      }
+    }
+  }
+
+  const int rs = a.hkv * D;  // bytes between consecutive keys
+  const int64_t head_off = (int64_t)g * D;
+  const char* kb = reinterpret_cast<const char*>(a.k) + head_off;
+  const char* vb = reinterpret_cast<const char*>(a.v) + head_off;
+  auto vo = [&](int u) { return (uint32_t)((4 * (2 * wave + u) + (lane & 3)) * rs + (lane >> 2) * 16); };
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* lds0 = (lds_char*)lds;
+  // rows kbase .. kbase+31 from pool row `row` on (row < 0: look it up); rows past the
+  // request's last key repeat it (masked)
+  auto dma_rows = [&](const char* base, lds_char* dst, int pitch, int kbase, int64_t row) {
+    const char* src = base + (row < 0 ? key_row<kPaged>(a, sp, kbase) : row) * rs;
+    const int last = nkeys - 1 - kbase;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t off =
+          kbase + kSub <= nkeys ? vo(u) : (uint32_t)min(4 * (2 * wave + u) + (lane & 3), last) * rs + (lane >> 2) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                       (__attribute__((address_space(3))) void*)(dst + (2 * wave + u) * pitch), 16, 0, 0);
+    }
+  };
+  auto issue = [&](int j, int64_t krow = -1, int64_t vrow = -1) {
+    lds_char* st = lds0 + (j & 3) * kF8Stage;
+    dma_rows(kb, st, kF8KPitch, key0 + kSub * min(j + 1, nsub - 1), krow);
+    dma_rows(vb, st + kF8KRegion, kF8VPitch, key0 + kSub * j, vrow);
+  };
+  auto stage_rows = [&](int j, int64_t& krow, int64_t& vrow) {
+    krow = key_row<kPaged>(a, sp, key0 + kSub * min(j + 1, nsub - 1));
+    vrow = key_row<kPaged>(a, sp, key0 + kSub * min(j, nsub - 1));
+  };
+
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds0;
+  const uint32_t k_lane = (l32 >> 2) * kF8KPitch + 16 * (l32 & 3) + 64 * hh;  // + 128 j
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int kr = (s16 >> 1) < 4 ? 4 * (grp >> 1) + (s16 >> 1) : 8 + 4 * (grp >> 1) + (s16 >> 1) - 4;
+  const uint32_t v_lane = kF8KRegion + (kr >> 2) * kF8VPitch + 16 * (kr & 3) + 64 * (grp & 1) + 8 * (s16 & 1);
+
+  auto mask = [&](f32x16_t& sv, int kbase, int h) {
+    if (!(lo_last <= kbase && kbase + kSub - 1 <= hi_first)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (key < lo[h] || key > hi[h]) sv[e] = kNegInf;
+      }
+    }
+  };
+
+  // S = K(slot) . Q^T for both halves. K pairs (16 codes, two k-steps) are read three
+  // pairs ahead into a 4-slot ring, the second half's Q fragments kF8QL..15 four steps
+  // ahead into a 5-slot ring. The K operand of step ks + 2 is widened after step ks's
+  // MFMAs (a 3-slot ring), so its conversions sit two MFMA steps before the asm MFMA
+  // that reads it.
+  f32x16_t sc[2];
+  auto compute_s = [&](uint32_t ka) {
+    uint4 k8[4], ql[5], kw[3];
+    auto kpair = [&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      k8[p % 4] = att_b128<128 * p>(ka);
+    };
+    auto qread = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      ql[i % 5] = att_b128<1024 * (i - kF8QL)>(q_lds);
+    };
+    auto widen_k = [&](int u, const uint4& k) { return u == 0 ? widen_e4m3(k.x, k.y) : widen_e4m3(k.z, k.w); };
+    static_assert(kF8QL >= 4, "the first four steps take Q from VGPRs");
+    kpair(std::integral_constant<int, 0>{});
+    kpair(std::integral_constant<int, 1>{});
+    kpair(std::integral_constant<int, 2>{});
+    DG_ATT_WAIT_LGKM(2);  // K pair 0
+    kw[0] = widen_k(0, k8[0]);
+    kw[1] = widen_k(1, k8[0]);
+    StaticFor<0, KS>::run([&](auto ic) {
+      constexpr int ks = decltype(ic)::value;
+      DG_ATT_WAIT_LGKM(f8w_wait(ks));
+      const uint4& qb1 = ks < kF8QL ? qf1[ks < kF8QL ? ks : 0] : ql[ks % 5];
+      if constexpr (ks < KS - 1) {
+        mfma_v(sc[0], kw[ks % 3], qf0[ks], ks == 0);
+        mfma_v(sc[1], kw[ks % 3], qb1, ks == 0);
+      } else {
+        mfma_v_last2(sc[0], sc[1], kw[ks % 3], qf0[ks], qb1);
+      }
+      if constexpr (ks + 4 < KS && ks + 4 >= kF8QL) qread(std::integral_constant<int, ks + 4>{});
+      if constexpr ((ks & 1) && (ks + 5) / 2 <= 7) kpair(std::integral_constant<int, (ks + 5) / 2>{});
+      if constexpr (ks + 2 < KS) kw[(ks + 2) % 3] = widen_k((ks + 2) & 1, k8[((ks + 2) >> 1) % 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  f32x16_t o[2][DB];
+  float l_run[2];
+  float m_ref[2] = {kNegInf, kNegInf};
+  for (;;) {
+    if (tid == 0) redo_flag[0] = 0;
+    dma_rows(kb, lds0 + 3 * kF8Stage, kF8KPitch, key0, -1);
+    issue(0);
+    if (nsub > 1) issue(1);
+    if (nsub > 2) issue(2);
+    if (nsub > 2) DG_ATT_WAIT_VM(12);
+    else if (nsub > 1) DG_ATT_WAIT_VM(8);
+    else DG_ATT_WAIT_VM(4);
+    DG_ATT_WAIT_LGKM0();  // also the Q writes into LDS
+    __builtin_amdgcn_s_barrier();
+    compute_s(lbase + 3 * kF8Stage + k_lane);
+    // as in attn_fwd_bf16_d256_w64: once every row has its reference, a running max per
+    // lane, and the overflow test once, after the loop
+    float m_seen[2] = {kNegInf, kNegInf}, m_lane[2] = {kNegInf, kNegInf};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      l_run[h] = 0.f;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[h][b][e] = 0.f;
+    }
+
+    bool overflow = false;
+    int64_t krow, vrow;
+    stage_rows(3, krow, vrow);
+    for (int sub = 0; sub < nsub; ++sub) {
+      const int left = nsub - 1 - sub;
+      if (left >= 2) DG_ATT_WAIT_VM(8);
+      else if (left == 1) DG_ATT_WAIT_VM(4);
+      else DG_ATT_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();  // stage sub landed for every wave; slot of sub-1 is free
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t ka = lbase + (sub & 3) * kF8Stage + k_lane;
+      const uint32_t va = lbase + (sub & 3) * kF8Stage + v_lane;
+      if (sub + 3 < nsub) issue(sub + 3, krow, vrow);  // into the slot of sub-1, free since the barrier
+      stage_rows(sub + 4, krow, vrow);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- softmax of S(sub), keys 0..15 (elements 0..7)
+      uint2 vf[3];
+      auto vread = [&](auto fc) {  // fragment f = 8 kh + b: d block b, key half kh
+        constexpr int f = decltype(fc)::value;
+        vf[f % 3] = att_tr8<128 * (f & 7) + 4 * kF8VPitch * (f >> 3)>(va);
+      };
+      vread(std::integral_constant<int, 0>{});
+      vread(std::integral_constant<int, 1>{});
+      mask(sc[0], key0 + kSub * sub, 0);
+      mask(sc[1], key0 + kSub * sub, 1);
+      auto row_max = [&](int h) {
+        const float t = half_max(att_max16(sc[h], kNegInf)) * a.scale_log2;
+        m_seen[h] = fmaxf(m_seen[h], t);
+        if (m_ref[h] == kNegInf) m_ref[h] = t;  // on a retry m_ref already covers this sub-tile
+        overflow |= t > m_ref[h] + kOverflow;
+      };
+      const bool late_max = !__any(m_ref[0] == kNegInf || m_ref[1] == kNegInf);  // uniform
+      if (!late_max) {
+        row_max(0);
+        row_max(1);
+      }
+      float mu[2];
+      uint4 pc[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mu[h] = m_ref[h] == kNegInf ? 0.f : m_ref[h];
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(sc[h][e], a.scale_log2, -mu[h]));
+          l_run[h] += p[e];
+        }
+        asm volatile("" : "+v"(l_run[h]));  // keep the sums here
+        pc[h][0] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- O^T += V(sub)^T . P(sub)^T: 16 fragments (one transposing read each, two
+      // ahead, widened at their step), each feeding both halves
+      float pv[2][8];
+      StaticFor<0, 2 * DB>::run([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        constexpr int b = f & 7, kh = f >> 3;
+        DG_ATT_WAIT_LGKM(f < 2 * DB - 1 ? 1 : 0);
+        const bf16x8_t va8 = __builtin_bit_cast(bf16x8_t, widen_e4m3(vf[f % 3].x, vf[f % 3].y));
+        o[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va8, __builtin_bit_cast(bf16x8_t, pc[0][kh]), o[0][b], 0, 0, 0);
+        o[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va8, __builtin_bit_cast(bf16x8_t, pc[1][kh]), o[1][b], 0, 0, 0);
+        if constexpr (f + 2 < 2 * DB) vread(std::integral_constant<int, f + 2>{});
+        if constexpr (f < 8) {
+          constexpr int h = f >> 2, e0 = 8 + 2 * (f & 3);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            pv[h][e0 - 8 + i] = fast_exp2(fmaf(sc[h][e0 + i], a.scale_log2, -mu[h]));
+            l_run[h] += pv[h][e0 - 8 + i];
+          }
+          asm volatile("" : "+v"(l_run[h]));
+          if constexpr ((f & 3) == 3)
+            pc[h][1] = make_uint4(pack_bf16(pv[h][0], pv[h][1]), pack_bf16(pv[h][2], pv[h][3]),
+                                  pack_bf16(pv[h][4], pv[h][5]), pack_bf16(pv[h][6], pv[h][7]));
+        }
+        if constexpr (f == 8 || f == 9) {
+          if (late_max) m_lane[f - 8] = att_max16(sc[f - 8], m_lane[f - 8]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+
+      // ---- S(sub+1) = K(sub+1) . Q^T
+      if (sub + 1 < nsub) compute_s(ka);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float t = half_max(m_lane[h]) * a.scale_log2;
+      m_seen[h] = fmaxf(m_seen[h], t);
+      overflow |= t > m_ref[h] + kOverflow;
+    }
+    if (__any(overflow) && lane == 0) redo_flag[0] = 1;
+    __syncthreads();
+    const int redo = redo_flag[0];
+    if (!redo) break;
+    __syncthreads();
+    m_ref[0] = fmaxf(m_ref[0], m_seen[0]);
+    m_ref[1] = fmaxf(m_ref[1], m_seen[1]);
+  }
+
+  // ---- epilogue: as attn_fwd_bf16_d256_w64, with v_scale in the normalisation and O
+  // staged one 32-row half at a time (each wave reads back only its own rows)
+  constexpr int kOPitch = 528;
+  char* ost = lds + wave * 32 * kOPitch;
+  float ltot[2];
+  const int64_t prow0 = sp.part_begin + ((int64_t)(g * nqt + qt) * sp.num_chunks + chunk) * kTile;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ltot[h] = half_sum(l_run[h]);
+    const float inv = (ltot[h] > 0.f ? 1.f / ltot[h] : 0.f) * a.v_scale;
+    char* orow = ost + l32 * kOPitch;
+    DG_ATT_WAIT_LGKM0();  // the previous half's rows have been read back
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<uint2*>(orow + (32 * b + 8 * e4 + 4 * hh) * 2) =
+            make_uint2(pack_bf16(o[h][b][4 * e4] * inv, o[h][b][4 * e4 + 1] * inv),
+                       pack_bf16(o[h][b][4 * e4 + 2] * inv, o[h][b][4 * e4 + 3] * inv));
+    if (hh == 0) {
+      const int row = row_of(h), tok = i0 + row / a.group, head = g * a.group + row % a.group;
+      if (tok < sp.num_q) {
+        if (sp.num_chunks > 1)
+          *reinterpret_cast<float2*>(a.part_ml + (prow0 + row) * 2) = make_float2(m_ref[h], ltot[h]);
+        else if (a.lse)
+          a.lse[(int64_t)(sp.q_start + tok) * a.hq + head] = (m_ref[h] + __builtin_amdgcn_logf(ltot[h])) * kLn2;
+      }
+    }
+    DG_ATT_WAIT_LGKM0();  // this half's rows are in LDS
+    // store r covers local rows 2r, 2r+1 of the half: lane i takes 16 bytes i%32 of row 2r + i/32
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const int lr = 2 * r + (lane >> 5);  // row 0..31 of the half
+      const int row = wave * 64 + 32 * h + lr, tok = i0 + row / a.group, head = g * a.group + row % a.group;
+      const uint4 x = *reinterpret_cast<const uint4*>(ost + lr * kOPitch + l32 * 16);
+      if (tok >= sp.num_q) continue;
+      char* dst = sp.num_chunks == 1
+                      ? reinterpret_cast<char*>(a.out) + ((int64_t)(sp.q_start + tok) * a.hq + head) * D * 2
+                      : reinterpret_cast<char*>(a.part_o) + (prow0 + row) * D * 2;
+      *reinterpret_cast<uint4*>(dst + l32 * 16) = x;
+    }
+  }
+}
+
 template <bool kBf16, int D, bool kPaged>
 int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   // work [0, num_wide): 64-rows-per-wave kernel; [num_wide, num_dma): 128-row LDS-DMA
@@ -1717,14 +2071,19 @@ int launch_typed(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-// FP8 K/V: work [0, num_dma) on the LDS-DMA kernel over codes (head_dim 256), the rest
-// on the register-staged kernel at bf16, then the merge of bf16 partials
+// FP8 K/V: work [0, num_wide) on the 64-rows-per-wave kernel over codes, [num_wide,
+// num_dma) on the 128-row one (head_dim 256), the rest on the register-staged kernel at
+// bf16, then the merge of bf16 partials
 template <int D, bool kPaged>
 int launch_fp8(AttnArgs args, const AttnPlan& plan, hipStream_t s) {
   if constexpr (D == 256) {
-    if (plan.num_dma > 0) {
+    if (plan.num_wide > 0) {
       args.work_offset = 0;
-      hipLaunchKernelGGL(attn_fwd_fp8_d256<kPaged>, dim3(plan.num_dma), dim3(kThreads), 0, s, args);
+      hipLaunchKernelGGL(attn_fwd_fp8_d256_w64<kPaged>, dim3(plan.num_wide), dim3(kThreads), 0, s, args);
+    }
+    if (plan.num_dma > plan.num_wide) {
+      args.work_offset = plan.num_wide;
+      hipLaunchKernelGGL(attn_fwd_fp8_d256<kPaged>, dim3(plan.num_dma - plan.num_wide), dim3(kThreads), 0, s, args);
     }
   }
   if (plan.num_work > plan.num_dma) {

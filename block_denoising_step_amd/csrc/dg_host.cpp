@@ -133,7 +133,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   // tiles and chunks; the split of a request, and the kernel that runs it, depend on
   // that request alone, so its result is the same whatever else is in the batch.
   // The LDS-DMA kernels (bf16 queries, head_dim 256; K/V in bf16 or, with kv_fp8, E4M3
-  // codes on the 128-row kernel only) take 32-bit byte offsets within a request's K/V,
+  // codes) take 32-bit byte offsets within a request's K/V,
   // so a contiguous request whose K/V span passes 2^31 - 1 bytes runs on the
   // register-staged kernel; paged requests are addressed per sub-tile and have no limit.
   const bool dma_ok = a->dtype == DG_BF16 && a->head_dim == 256 &&
@@ -184,7 +184,7 @@ dg_status attn_plan(const dg_attn_args* a, AttnPlan* plan, const char** msg) {
   for (int s = 0; s < a->num_seqs; ++s) {
     const dg_seq& q = a->seqs[s];
     wide[s] = false;
-    if (dma[s] && !a->kv_fp8 && q.num_q > 0) {
+    if (dma[s] && q.num_q > 0) {
       const Split w = split(q, kAttnWideTileRows);
       const int64_t groups = w.ntiles_q * w.nch * a->num_kv_heads;
       wide[s] = groups > 0 && w.sub_tiles >= wide_min_sub * groups;

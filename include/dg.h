@@ -395,9 +395,9 @@ int dg_abi_version(void);                  /* DG_ABI_VERSION */
  * Returns the previous setting (0 or 1). */
 int dg_test_force_register_staged(int on);
 
-/* Test hook, not for production use. A bf16 head_dim-256 request runs on the
+/* Test hook, not for production use. A head_dim-256 request (bf16 or FP8 K/V) runs on a
  * 64-rows-per-wave attention kernel when its work groups would average at least this many
- * 32-key sub-tiles (default 64), else on the 128-row kernel; this sets the number for
+ * 32-key sub-tiles (default 64), else on a 128-row kernel; this sets the number for
  * every later dg_attn_mixed call (from any thread), so that tests reach the first kernel
  * at small shapes. n < 1 restores the default. Results stay within the same bars; each
  * request's kernel still depends on that request alone. Returns the previous number. */

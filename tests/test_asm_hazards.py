@@ -1,5 +1,6 @@
-"""The attention kernel's S^T MFMAs are inline asm in their VGPR form (the compiler
-would put their accumulators in the AGPRs, which O fills), so the compiler does not
+"""The 64-rows-per-wave attention kernels' S^T MFMAs (bf16 and FP8 K/V) are inline asm in
+their VGPR form (the compiler would put their accumulators in the AGPRs, which O fills),
+so the compiler does not
 insert their wait states. This test compiles attn.hip for gfx950 and checks, in the
 generated code, the two hazards the asm relies on being absent:
 - no vector instruction writes an asm MFMA's A/B/C operands in the 3 instructions
@@ -16,9 +17,11 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "..", "block_denoising_step_amd", "csrc", "attn.hip")
-# both instantiations: contiguous (false) and paged (true) K/V
+# both instantiations (contiguous and paged K/V) of the bf16 and the FP8 kernels
 KERNELS = ["_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ILb0EEEvNS0_8AttnArgsE",
-           "_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ILb1EEEvNS0_8AttnArgsE"]
+           "_ZN2dg12_GLOBAL__N_122attn_fwd_bf16_d256_w64ILb1EEEvNS0_8AttnArgsE",
+           "_ZN2dg12_GLOBAL__N_121attn_fwd_fp8_d256_w64ILb0EEEvNS0_8AttnArgsE",
+           "_ZN2dg12_GLOBAL__N_121attn_fwd_fp8_d256_w64ILb1EEEvNS0_8AttnArgsE"]
 
 
 def _regs(op):

@@ -137,6 +137,69 @@ def test_fp8_attention_against_oracle(case):
     assert err <= 2e-2 and lerr <= 1e-3
 
 
+# The 64-rows-per-wave kernel over codes at small shapes: with the planner's threshold
+# lowered to 16 sub-tiles per work group (test hook) these requests run on it.
+WIDE_CASES = [
+    # label, spec, window, hq, hkv, kv_chunk, k_scale, v_scale
+    ("wide bidir G=2", [(2048, 200, BIDIR)], -1, 4, 2, 1024, 1 / 64, 1 / 64),
+    ("wide causal W=300 G=2", [(2048, 200, CAUSAL)], 300, 4, 2, 1024, 0.013, 0.021),
+    ("wide G=8 ragged, two requests", [(2048, 100, BIDIR), (1500, 77, CAUSAL)], -1, 16, 2, 1024, 1 / 64, 1 / 32),
+    ("wide G=16 W=600 causal", [(2048, 37, CAUSAL)], 600, 32, 2, 1024, 0.02, 0.03),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_fp8_wide_kernel_against_oracle(case):
+    label, spec, window, hq, hkv, chunk, ks, vs = case
+    say(f"[fp8 wide] {label}")
+    D = 256
+    seqs = pack_seqs(spec)
+    T = sum(n for _, n, _ in spec)
+    S = sum(p + n for p, n, _ in spec)
+    q = normal(431, (T, hq, D), bf16=True)
+    kc, vc = _fp8_kv(432, (S, hkv, D), ks), _fp8_kv(433, (S, hkv, D), vs)
+    out = torch.full((T, hq, D), float("nan"), device=DEV, dtype=torch.bfloat16)
+    lse = torch.full((T, hq), float("nan"), device=DEV)
+    with dg.wide_min_sub(16):
+        dg.dg_attn_mixed(dev(q, True), codes_dev(kc), codes_dev(vc), out, seqs, window, hq, hkv, lse=lse,
+                         kv_chunk=chunk, k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+    want, wlse = attn_mixed_fp8(seqs, window, q, kc, vc, ks, vs, hq, hkv)
+    err = max_rel_rows(host(out), want)
+    lerr = float(np.abs(host(lse) - wlse).max())
+    say(f"  max-rel {err:.3e}  lse abs {lerr:.3e}")
+    assert err <= 2e-2 and lerr <= 1e-3
+
+
+@pytest.mark.parametrize("wide", [False, True])
+def test_fp8_score_jump_recomputes(wide):
+    """Keys after the first 32 score far above the first ones (about 2^92 in log2 units):
+    both head_dim-256 kernels over codes fix each row's reference from its first scores,
+    have to recompute the chunk, and still match the oracle."""
+    P, N, H, D, ks, vs = 2048, 64, 2, 256, 1 / 64, 1 / 64
+    rng = np.random.default_rng(93)
+    q = 0.5 + 0.05 * rng.standard_normal((N, H, D))
+    k = 0.25 + 0.05 * rng.standard_normal((P + N, H, D))
+    k[:32] *= -1.0
+    v = rng.standard_normal((P + N, H, D))
+    q = q.astype(np.float32)
+    kc, vc = quantize(k, ks), quantize(v, vs)
+    seqs = pack_seqs([(P, N, BIDIR)])
+    qd = dev(q, True)
+    want, wlse = attn_mixed_fp8(seqs, -1, host(qd).astype(np.float64), kc, vc, ks, vs, H, H, scale=1.0)
+    for chunk in (4096, 1024):
+        out = torch.full((N, H, D), float("nan"), device=DEV, dtype=torch.bfloat16)
+        lse = torch.full((N, H), float("nan"), device=DEV)
+        with dg.wide_min_sub(16 if wide else 1 << 30):
+            dg.dg_attn_mixed(qd, codes_dev(kc), codes_dev(vc), out, seqs, -1, H, H, lse=lse, scale=1.0,
+                             kv_chunk=chunk, k_scale=ks, v_scale=vs)
+            torch.cuda.synchronize()
+        err = max_rel_rows(host(out), want)
+        lerr = float(np.abs(host(lse) - wlse).max())
+        say(f"[fp8 score jump] wide={wide} chunk={chunk}: max-rel {err:.3e}  lse abs {lerr:.3e}")
+        assert err <= 2e-2 and lerr <= 1e-3
+
+
 @pytest.mark.parametrize("window", [-1, 512])
 def test_fp8_mixed_four_request_batch_sampled(window):
     """The four-request mixed batch at its full size (a 2048-token causal prefill, a causal
