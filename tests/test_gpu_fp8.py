@@ -256,6 +256,38 @@ def test_fp8_paged_attention_against_oracle():
         assert err <= 2e-2 and lerr <= 1e-3
 
 
+def test_fp8_paged_wide_kernel_against_oracle():
+    """Paged FP8 pools on the 64-rows-per-wave kernel over codes (threshold hook, chunks of
+    1024 keys): shuffled 64-row blocks, a bidirectional and a causal request, global and
+    windowed."""
+    B, hq, hkv, D, ks, vs = 64, 8, 2, 256, 0.02, 0.03
+    spec = [(2048, 64, BIDIR), (1500, 70, CAUSAL)]
+    seqs = pack_seqs(spec)
+    T = sum(n for _, n, _ in spec)
+    nbs = [-(-(p + n) // B) for p, n, _ in spec]
+    nblk = sum(nbs) + 5
+    table = np.random.default_rng(435).permutation(nblk)[:sum(nbs)].astype(np.int32)
+    pseqs, start = [], 0
+    for s, nb in zip(seqs, nbs):
+        pseqs.append(Seq(s.q_start, s.num_q, start, s.prefix_len, s.mode))
+        start += nb
+    kc, vc = _fp8_kv(436, (nblk * B, hkv, D), ks), _fp8_kv(437, (nblk * B, hkv, D), vs)
+    q = normal(438, (T, hq, D), bf16=True)
+    tt = torch.from_numpy(table).to(DEV)
+    for window in (-1, 300):
+        out = torch.empty(T, hq, D, device=DEV, dtype=torch.bfloat16)
+        lse = torch.empty(T, hq, device=DEV)
+        with dg.wide_min_sub(16):
+            dg.dg_attn_mixed(dev(q, True), codes_dev(kc), codes_dev(vc), out, pseqs, window, hq, hkv, lse=lse,
+                             kv_chunk=1024, block_table=tt, block_size=B, k_scale=ks, v_scale=vs)
+            torch.cuda.synchronize()
+        want, wlse = attn_mixed_paged_fp8(pseqs, window, q, kc, vc, ks, vs, table, B, hq, hkv)
+        err = max_rel_rows(host(out), want)
+        lerr = float(np.abs(host(lse) - wlse).max())
+        say(f"[fp8 paged wide] W={window}: max-rel {err:.3e}  lse abs {lerr:.3e}")
+        assert err <= 2e-2 and lerr <= 1e-3
+
+
 def _special_values():
     """Ties between neighbouring E4M3 values, saturation, the subnormal range, signed zeros."""
     pos = e4m3_decode(np.arange(127, dtype=np.uint8))
