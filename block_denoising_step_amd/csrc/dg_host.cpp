@@ -337,8 +337,12 @@ dg_status selfcond_plan(const dg_selfcond_args* a, SelfcondPlan* plan, const cha
   // a 64K-value tile, so that the few K steps of each still fill the GPU.
   const bool narrow = plan->dma && !scaled && a->M <= 256 && a->V <= 16384 && a->d % 128 == 0;
   const bool wide = plan->dma && !narrow && a->d % 512 == 0;
-  plan->tile_m = wide ? 128 : 256;
-  plan->tile_n = wide ? 512 : narrow ? 128 : 256;
+  // An fp32 product with fewer than 16 tiles of 256 x 256 takes 64 x 128 tiles: at one
+  // K step per slice, 256 x 256 tiles would leave half the CUs idle (a slice must hold a
+  // whole step) and write a 256 KB partial per step.
+  const bool small_f32 = !plan->dma && a->dtype == DG_F32 && ceil_div(a->M, 256) * ceil_div(a->d, 256) < 16;
+  plan->tile_m = wide ? 128 : small_f32 ? 64 : 256;
+  plan->tile_n = wide ? 512 : narrow || small_f32 ? 128 : 256;
   plan->tile_k = plan->dma ? 32 : (a->dtype == DG_BF16 ? 64 : 32);
   plan->m_tiles = (int)ceil_div(a->M, plan->tile_m);
   plan->n_tiles = (int)ceil_div(a->d, plan->tile_n);

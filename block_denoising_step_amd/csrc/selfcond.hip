@@ -162,26 +162,34 @@ __device__ __forceinline__ TileIdx tile_index(const GemmArgs& g) {
   return t;
 }
 
-template <bool kBf16, bool kFused>
+// BM x BN tile: 256 x 256, or 64 x 128 for small fp32 products (a 256 x 256 tile leaves
+// them half the CUs idle, each work group a one-step slice with a 256 KB partial); 4 waves
+// of (BM/2) x (BN/2). A staging: BM rows x 8 chunks of 16 bytes per K step, BM/32 chunks
+// per thread; B staging (fp32): (BN/4) column blocks x 8 k blocks, BN/128 blocks per thread.
+template <bool kBf16, bool kFused, int BM = 256, int BN = 256>
 __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
   using T = Tr<kBf16>;
   constexpr int BK = T::bk, ESZ = T::esz, EPV = T::epv;
-  __shared__ __attribute__((aligned(16))) char lds_a[2][kBM * kRow];
-  __shared__ __attribute__((aligned(16))) char lds_b[2][kBN * kRow];
+  constexpr int NI = BM / 64, NJ = BN / 64;     // 32 x 32 blocks per wave along rows, columns
+  constexpr int kAC = BM * 8 / kThreads;        // A chunks per thread
+  constexpr int kBB = BN / 128;                 // fp32 B blocks per thread
+  static_assert((BM == 256 && BN == 256) || (BM == 64 && BN == 128 && !kBf16), "tile shapes");
+  __shared__ __attribute__((aligned(16))) char lds_a[2][BM * kRow];
+  __shared__ __attribute__((aligned(16))) char lds_b[2][BN * kRow];
 
-  const TileIdx ti = tile_index<kBM, kBN>(g);
+  const TileIdx ti = tile_index<BM, BN>(g);
   const int m0 = ti.m0, n0 = ti.n0, k_lo = ti.k_lo, k_hi = ti.k_hi;
   const int nsteps = (k_hi - k_lo + BK - 1) / BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
 
-  // A staging: chunk q = i*256 + tid (i < 8) -> row q >> 3, 16-byte chunk q & 7
+  // A staging: chunk q = i*256 + tid (i < kAC) -> row q >> 3, 16-byte chunk q & 7
   const char* pbase = reinterpret_cast<const char*>(g.p);
-  float crow[8];
+  float crow[kAC];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kAC; ++i) {
     const int r = m0 + ((i * kThreads + tid) >> 3);
     crow[i] = 0.f;
     if (kFused && r < g.M) crow[i] = -g.row_max[r] * kLog2e - __builtin_amdgcn_logf(g.row_sum[r]);
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
   auto load_step = [&](int s, uint4 (&a)[8], uint4 (&b)[8]) {
     const int k0 = k_lo + s * BK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kAC; ++i) {
       const int q = i * kThreads + tid;
       const int r = m0 + (q >> 3), kc = k0 + (q & 7) * EPV;
       if (r < g.M && kc + EPV <= k_hi) {
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
             }
       }
     }
-    if (kBf16) {
+    if constexpr (kBf16) {
       const int nb = tid & 31, kb = tid >> 5;  // 32 column blocks x 8 k blocks
       const int col = n0 + nb * 8;
 #pragma unroll
@@ -225,9 +233,9 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
       }
     } else {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < kBB; ++blk) {
         const int id = blk * kThreads + tid;
-        const int nb = id & 63, kb = id >> 6;  // 64 column blocks x 8 k blocks
+        const int nb = id % (BN / 4), kb = id / (BN / 4);  // BN/4 column blocks x 8 k blocks
         const int col = n0 + nb * 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -244,13 +252,13 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     char* A = lds_a[buf];
     char* B = lds_b[buf];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kAC; ++i) {
       const int q = i * kThreads + tid;
       const int row = q >> 3;
       const uint4 v = kFused ? to_prob<kBf16>(a[i], crow[i]) : a[i];
       *reinterpret_cast<uint4*>(A + row * kRow + swz_a(row, q & 7) * 16) = v;
     }
-    if (kBf16) {
+    if constexpr (kBf16) {
       const int nb = tid & 31, kb = tid >> 5;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {  // column nb*8 + c gets k = kb*8 .. kb*8+7
@@ -266,9 +274,9 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
       }
     } else {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < kBB; ++blk) {
         const int id = blk * kThreads + tid;
-        const int nb = id & 63, kb = id >> 6;
+        const int nb = id % (BN / 4), kb = id / (BN / 4);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int n = nb * 4 + c;
@@ -280,18 +288,18 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   auto compute_step = [&](int buf) {
     const char* A = lds_a[buf];
     const char* B = lds_b[buf];
-    if (kBf16) {
+    if constexpr (kBf16) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {  // 16 k per MFMA, lane half h holds chunk 2ks + h
         const int kc = 2 * ks + h;
@@ -317,25 +325,25 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     } else {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {  // 16 k per step: lane half h holds chunks 4ks+2h, 4ks+2h+1
-        float4 fa[4][2], fb[4][2];
+        float4 fa[NI][2], fb[NJ][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i) {
           const int row = wm + 32 * i + l32;
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             fa[i][c] = *reinterpret_cast<const float4*>(A + row * kRow + swz_a(row, 4 * ks + 2 * h + c) * 16);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int n = wn + 32 * j + l32;
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             fb[j][c] = *reinterpret_cast<const float4*>(B + n * kRow + swz_b(n, 4 * ks + 2 * h + c) * 16);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][c].x, fb[j][c].x, acc[i][j], 0, 0, 0);
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void selfcond_gemm_reg(GemmArgs g) {
     }
   }
 
-  store_blocks<kBM, kBN, 4, 4>(g, acc, ti.split, k_lo, ti.mt, ti.nt, (wave >> 1) * 4, (wave & 1) * 4, lane, kBf16);
+  store_blocks<BM, BN, NI, NJ>(g, acc, ti.split, k_lo, ti.mt, ti.nt, wm >> 5, wn >> 5, lane, kBf16);
 }
 
 
@@ -814,8 +822,13 @@ int launch_selfcond(const dg_selfcond_args* a, const SelfcondPlan& plan, void* s
     if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<true, true>), grid, dim3(kThreads), 0, s, g);
     else hipLaunchKernelGGL((selfcond_gemm_reg<true, false>), grid, dim3(kThreads), 0, s, g);
   } else {
-    if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<false, true>), grid, dim3(kThreads), 0, s, g);
-    else hipLaunchKernelGGL((selfcond_gemm_reg<false, false>), grid, dim3(kThreads), 0, s, g);
+    if (plan.tile_m == 64) {
+      if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<false, true, 64, 128>), grid, dim3(kThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_reg<false, false, 64, 128>), grid, dim3(kThreads), 0, s, g);
+    } else {
+      if (fused) hipLaunchKernelGGL((selfcond_gemm_reg<false, true>), grid, dim3(kThreads), 0, s, g);
+      else hipLaunchKernelGGL((selfcond_gemm_reg<false, false>), grid, dim3(kThreads), 0, s, g);
+    }
   }
   if (plan.splits > 1 && epi && epi->mode != kReducePlain) {
     const int64_t n4 = (int64_t)plan.m_tiles * (epi->mode == kReduceGeglu ? epi->half_tiles : plan.n_tiles) *

@@ -86,7 +86,8 @@ def test_one_hot_bit_exact(bf16, V, d):
 
 
 @pytest.mark.parametrize("bf16,M,V,d", [(True, 130, 1000, 256), (False, 5, 77, 128), (True, 1, 262144, 128),
-                                        (True, 300, 4104, 384), (True, 300, 4096, 512), (True, 129, 8192, 1536)])
+                                        (True, 300, 4104, 384), (True, 300, 4096, 512), (True, 129, 8192, 1536),
+                                        (False, 100, 5000, 384)])
 def test_ragged_shapes(bf16, M, V, d):
     """M not a multiple of the tile, V ending mid-step and mid-vector, small d."""
     rng = np.random.default_rng(M + V)
